@@ -1,0 +1,238 @@
+"""Seeded synthetic workloads for the encoder and verification attention path.
+
+This module generates inputs only. It holds none of the attention arithmetic
+(no projection, score, softmax or merge), so both the fp64 oracle and the HIP
+path can be fed from it without sharing any of the method's code.
+
+Workloads (shapes follow the pages; values are synthetic because the pages'
+audio, transcripts and trained weights are not available):
+
+* "audio.cpp PR #1223, Add Edda ASR" (PR description and the encoder commit
+  message): a Whisper-large-v3 encoder, one 30 s window = 1500 frames; the
+  verification block is an anchor plus up to 15 drafted tokens; beam search
+  uses 5 beams sharing one token-tree KV cache whose mask rows admit only a
+  beam's ancestors.
+* "higgs-audio-v3-stt-GGUF" model card, architecture note: 4 s chunks encoded
+  independently with within-chunk attention (4 s = 200 encoder positions at
+  50 positions per second).
+* "BuzzASR/danish discussion #1": the encoder is fully bidirectional and has
+  32 layers ("layer 8 ... layers 9-32"); 1000 mel frames = 500 positions.
+
+Random-number convention: every tensor is drawn from
+``numpy.random.default_rng([seed, cfg, layer, tensor_id, trial])`` (PCG64) as
+float64 ``standard_normal`` times sigma, then rounded to float16 (round to
+nearest even). ``N(0, s)`` in the workload descriptions is read as variance s.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# Whisper-large-v3 encoder attention geometry.
+D_MODEL = 1280
+N_HEADS = 20
+HEAD_DIM = 64
+QKV_COLS = 3 * D_MODEL
+
+# Tensor ids of the RNG key.
+T_X, T_WQKV, T_BQ, T_BV, T_WO, T_VALID, T_Q, T_KSELF, T_VSELF, T_KCROSS, T_VCROSS, T_L, T_TREE = range(13)
+
+W_VAR = 1.0 / D_MODEL   # W_qkv and W_o entries: N(0, 1/1280)
+B_VAR = 0.02            # q and v biases: N(0, 0.02); no k bias
+
+FRAMES_PER_WINDOW = 1500   # one 30 s window
+POSITIONS_PER_SECOND = 50  # 3000 mel frames -> 1500 positions over 30 s
+CHUNK_SECONDS = 4
+CHUNK_LEN = CHUNK_SECONDS * POSITIONS_PER_SECOND  # 200
+ENCODER_LAYERS = 32
+VERIFY_BLOCK = 16  # anchor + 15 drafted tokens
+BEAMS = 5
+
+
+def rng_for(seed: int, cfg: int, layer: int, tensor_id: int, trial: int = 0) -> np.random.Generator:
+    return np.random.default_rng([int(seed), int(cfg), int(layer), int(tensor_id), int(trial)])
+
+
+def normal_f16(rng: np.random.Generator, shape, var: float) -> np.ndarray:
+    """float64 N(0, var) draw rounded to float16 (numpy's cast is round-to-nearest-even)."""
+    return (rng.standard_normal(shape) * math.sqrt(var)).astype(np.float16)
+
+
+@dataclass
+class EncoderLayerWeights:
+    w_qkv: np.ndarray          # fp16 [1280, 3840]; column blocks Q | K | V, head h at 64h..64h+63
+    b_qkv: np.ndarray          # fp16 [3840]; the K third is zero
+    w_o: np.ndarray            # fp16 [1280, 1280]
+    b_o: np.ndarray | None = None
+
+
+def encoder_layer_weights(cfg: int, layer: int, seed: int = 0) -> EncoderLayerWeights:
+    w_qkv = normal_f16(rng_for(seed, cfg, layer, T_WQKV), (D_MODEL, QKV_COLS), W_VAR)
+    b_qkv = np.zeros(QKV_COLS, dtype=np.float16)
+    b_qkv[:D_MODEL] = normal_f16(rng_for(seed, cfg, layer, T_BQ), (D_MODEL,), B_VAR)
+    b_qkv[2 * D_MODEL:] = normal_f16(rng_for(seed, cfg, layer, T_BV), (D_MODEL,), B_VAR)
+    w_o = normal_f16(rng_for(seed, cfg, layer, T_WO), (D_MODEL, D_MODEL), W_VAR)
+    return EncoderLayerWeights(w_qkv=w_qkv, b_qkv=b_qkv, w_o=w_o)
+
+
+@dataclass
+class EncoderWorkload:
+    cfg: int
+    name: str
+    batch: int
+    seq_len: int
+    chunk_len: int          # 0 = full bidirectional window
+    valid_len: np.ndarray   # int32 [batch]; keys at positions >= valid_len are masked
+    layers: int
+    seed: int = 0
+    x: np.ndarray | None = field(default=None, repr=False)  # fp16 [batch*seq_len, 1280]
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.seq_len
+
+    def weights(self, layer: int) -> EncoderLayerWeights:
+        return encoder_layer_weights(self.cfg, layer, self.seed)
+
+
+ENCODER_CONFIGS = {
+    0: dict(name="one 4 s chunk, 1 sublayer", batch=1, seq_len=CHUNK_LEN, chunk_len=0, layers=1),
+    1: dict(name="one 30 s window, 32 sublayers", batch=1, seq_len=FRAMES_PER_WINDOW, chunk_len=0,
+            layers=ENCODER_LAYERS),
+    2: dict(name="45 s of audio in 4 s chunks, 32 sublayers", batch=1, seq_len=12 * CHUNK_LEN,
+            chunk_len=CHUNK_LEN, layers=ENCODER_LAYERS),
+    3: dict(name="16 batched 30 s windows with padded key tails, 32 sublayers", batch=16,
+            seq_len=FRAMES_PER_WINDOW, chunk_len=0, layers=ENCODER_LAYERS),
+}
+
+
+def encoder_workload(cfg: int, seed: int = 0, layers: int | None = None, batch: int | None = None,
+                     seq_len: int | None = None, chunk_len: int | None = None,
+                     valid_len=None) -> EncoderWorkload:
+    """Build encoder workload `cfg` (0..3). Keyword overrides shrink a workload for tests
+    while keeping its structure (same RNG streams, same distributions)."""
+    c = dict(ENCODER_CONFIGS[cfg])
+    if layers is not None:
+        c["layers"] = layers
+    if batch is not None:
+        c["batch"] = batch
+    if seq_len is not None:
+        c["seq_len"] = seq_len
+    if chunk_len is not None:
+        c["chunk_len"] = chunk_len
+    b, s = c["batch"], c["seq_len"]
+    if valid_len is not None:
+        v = np.asarray(valid_len, dtype=np.int32).reshape(b)
+    elif cfg == 2:
+        # 45 s = 2250 positions: 11 full chunks and 50 valid positions of the 12th.
+        v = np.full(b, min(s, 45 * POSITIONS_PER_SECOND), dtype=np.int32)
+    elif cfg == 3:
+        lo = min(300, s)
+        v = rng_for(seed, cfg, 0, T_VALID).integers(lo, s + 1, size=b).astype(np.int32)
+    else:
+        v = np.full(b, s, dtype=np.int32)
+    x = normal_f16(rng_for(seed, cfg, 0, T_X), (b * s, D_MODEL), 1.0)
+    return EncoderWorkload(cfg=cfg, name=c["name"], batch=b, seq_len=s, chunk_len=c["chunk_len"],
+                           valid_len=v, layers=c["layers"], seed=seed, x=x)
+
+
+# --------------------------------------------------------------------------------------
+# Speculative block verification (decoder self-attention over a KV cache indexed by
+# position, plus cross-attention over the 1500 encoder frames).
+# --------------------------------------------------------------------------------------
+
+@dataclass
+class VerifyCase:
+    q: np.ndarray            # fp16 [n_q, 20, 64]
+    k: np.ndarray            # fp16 [n_kv, 20, 64]; row = cache slot = position
+    v: np.ndarray            # fp16 [n_kv, 20, 64]
+    mask: np.ndarray | None  # bool [n_q, n_kv]; True = key admitted; None = every key admitted
+    kind: str                # "causal" | "cross" | "tree"
+    parents: np.ndarray | None = None  # int32 [n_kv] for "tree": parent slot, -1 at the root
+    query_slots: np.ndarray | None = None  # int32 [n_q] for "tree"
+
+    @property
+    def n_q(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def n_kv(self) -> int:
+        return self.k.shape[0]
+
+
+def verify_cache_lengths(trials: int = 8, seed: int = 0) -> np.ndarray:
+    """Self-attention cache length L per trial, uniform on [32, 448]."""
+    return np.array([cache_length(t, seed) for t in range(trials)], dtype=np.int32)
+
+
+def cache_length(trial: int, seed: int = 0) -> int:
+    return int(rng_for(seed, 4, 0, T_L, trial).integers(32, 449))
+
+
+def causal_block_mask(n_q: int, n_kv: int) -> np.ndarray:
+    """Mask rows of a block of n_q new tokens that occupy the last n_q cache slots:
+    query t sits at position n_kv - n_q + t and admits every slot up to and including it."""
+    t = np.arange(n_q)[:, None]
+    j = np.arange(n_kv)[None, :]
+    return j <= (n_kv - n_q + t)
+
+
+def beam_tree(n_kv: int, rng: np.random.Generator, beams: int = BEAMS):
+    """Token tree of n_kv slots shared by `beams` beams (never copied or reordered).
+
+    A shared prefix chain of P = n_kv - beams*S slots (S = (n_kv - 4) // beams steps)
+    is followed by S steps; at every step each beam's newest token takes a fresh slot
+    whose parent is the previous step's slot of a beam drawn uniformly (pruned branches
+    stay behind as dead slots). Returns (parents, query_slots, mask) where the mask
+    row of a query admits exactly its ancestors and itself.
+    """
+    steps = (n_kv - 4) // beams
+    prefix = n_kv - beams * steps
+    if steps < 1 or prefix < 1:
+        raise ValueError("tree needs n_kv >= 4 + beams")
+    parents = np.full(n_kv, -1, dtype=np.int32)
+    parents[1:prefix] = np.arange(prefix - 1)
+    prev = np.full(beams, prefix - 1, dtype=np.int32)
+    for s in range(steps):
+        slots = prefix + beams * s + np.arange(beams, dtype=np.int32)
+        src = rng.integers(0, beams, size=beams) if s > 0 else np.zeros(beams, dtype=np.int64)
+        parents[slots] = prev[src]
+        prev = slots
+    query_slots = prev.copy()
+    mask = np.zeros((beams, n_kv), dtype=bool)
+    for b, slot in enumerate(query_slots):
+        node = int(slot)
+        while node >= 0:
+            mask[b, node] = True
+            node = int(parents[node])
+    return parents, query_slots, mask
+
+
+def verify_self_case(trial: int, layer: int, seed: int = 0, n_kv: int | None = None,
+                     n_q: int = VERIFY_BLOCK) -> VerifyCase:
+    L = cache_length(trial, seed) if n_kv is None else int(n_kv)
+    q = normal_f16(rng_for(seed, 4, layer, T_Q, trial), (n_q, N_HEADS, HEAD_DIM), 1.0)
+    k = normal_f16(rng_for(seed, 4, layer, T_KSELF, trial), (L, N_HEADS, HEAD_DIM), 1.0)
+    v = normal_f16(rng_for(seed, 4, layer, T_VSELF, trial), (L, N_HEADS, HEAD_DIM), 1.0)
+    return VerifyCase(q=q, k=k, v=v, mask=causal_block_mask(n_q, L), kind="causal")
+
+
+def verify_cross_case(trial: int, layer: int, seed: int = 0, n_kv: int = FRAMES_PER_WINDOW,
+                      n_q: int = VERIFY_BLOCK) -> VerifyCase:
+    q = normal_f16(rng_for(seed, 4, layer, T_Q, trial), (n_q, N_HEADS, HEAD_DIM), 1.0)
+    k = normal_f16(rng_for(seed, 4, layer, T_KCROSS, trial), (n_kv, N_HEADS, HEAD_DIM), 1.0)
+    v = normal_f16(rng_for(seed, 4, layer, T_VCROSS, trial), (n_kv, N_HEADS, HEAD_DIM), 1.0)
+    return VerifyCase(q=q, k=k, v=v, mask=None, kind="cross")
+
+
+def verify_tree_case(trial: int, layer: int, seed: int = 0, n_kv: int | None = None) -> VerifyCase:
+    L = cache_length(trial, seed) if n_kv is None else int(n_kv)
+    parents, query_slots, mask = beam_tree(L, rng_for(seed, 4, 0, T_TREE, trial))
+    k = normal_f16(rng_for(seed, 4, layer, T_KSELF, trial), (L, N_HEADS, HEAD_DIM), 1.0)
+    v = normal_f16(rng_for(seed, 4, layer, T_VSELF, trial), (L, N_HEADS, HEAD_DIM), 1.0)
+    # A query's projection is a row of its own slot's input; draw queries independently.
+    q = normal_f16(rng_for(seed, 4, layer, T_Q, trial), (BEAMS, N_HEADS, HEAD_DIM), 1.0)
+    return VerifyCase(q=q, k=k, v=v, mask=mask, kind="tree", parents=parents, query_slots=query_slots)
+
