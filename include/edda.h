@@ -1,0 +1,165 @@
+/*
+ * edda.h — C ABI of libedda.so: Whisper-large-v3 encoder self-attention and
+ * speculative block-verification attention on AMD MI355X (gfx950).
+ *
+ * What the library computes (the pages it follows):
+ *  - "audio.cpp PR #1223, Add Edda ASR", PR description and encoder commit
+ *    message: the encoder packs Q, K and V into one projection and runs flash
+ *    attention over fp16 K/V instead of materializing fp32 scores for all 1500
+ *    frames of a 30 s window.
+ *  - "higgs-audio-v3-stt-GGUF" model card, architecture note: 4 s chunks are
+ *    encoded independently with within-chunk attention, and valid frames must
+ *    not attend to padding.
+ *  - "BuzzASR/danish discussion #1", first reply: the encoder is bidirectional.
+ *  - "audio.cpp PR #1223", commit messages: the decoder verifies an anchor plus
+ *    up to 15 drafted tokens in one pass over KV slots indexed by position;
+ *    beams share one token-tree KV cache whose mask row admits only a beam's
+ *    ancestors.
+ *  - llama.cpp DSpark diff, src/models/dflash.cpp ("cache-aware, non-causal
+ *    attention"): one attention call takes Q, K, V, the output projection and
+ *    the score scale together.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers to IEEE binary16 (fp16) unless noted,
+ *    row-major, 16-byte aligned. Geometry is fixed: d_model 1280, 20 heads of 64.
+ *  - The caller owns every buffer (inputs, outputs, workspaces). The library
+ *    never allocates, frees or synchronizes; it keeps no state between calls
+ *    except the calling thread's last error text. Calls only enqueue work on
+ *    `stream` (a hipStream_t passed as void*; NULL = the null stream) and return.
+ *  - Arguments are validated on the host before anything is enqueued; an
+ *    invalid call returns a non-zero status, enqueues nothing and sets the text
+ *    returned by edda_last_error(). Nothing falls back silently.
+ *  - Arithmetic: fp16 operands, fp32 accumulation and fp32 softmax, fp16
+ *    results rounded to nearest even. The score scale is 1/sqrt(64) = 1/8.
+ *  - Calls on different streams may run concurrently when their output and
+ *    workspace buffers do not overlap.
+ */
+#ifndef EDDA_H
+#define EDDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EDDA_D_MODEL 1280
+#define EDDA_N_HEADS 20
+#define EDDA_HEAD_DIM 64
+#define EDDA_QKV_COLS (3 * EDDA_D_MODEL)
+#define EDDA_MAX_VERIFY_QUERIES 16
+
+typedef enum {
+  EDDA_OK = 0,
+  EDDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, size out of range            */
+  EDDA_ERR_UNSUPPORTED = 2,      /* valid request this build does not handle  */
+  EDDA_ERR_MISALIGNED = 3,       /* a pointer is not 16-byte aligned           */
+  EDDA_ERR_WORKSPACE = 4,        /* workspace missing or too small             */
+  EDDA_ERR_HIP = 5               /* the HIP runtime reported a launch error    */
+} edda_status;
+
+/*
+ * Packed QKV projection: qkv = x * W_qkv + b_qkv.
+ * (audio.cpp PR #1223: the encoder "packs QKV" — one projection instead of three.)
+ *
+ *  x      [rows, 1280]   fp16, row-major.
+ *  w_qkv  [3840, 1280]   fp16, row-major, output-feature major ("Linear" layout:
+ *                        row n holds the 1280 input weights of output column n).
+ *                        Rows 0..1279 are Q, 1280..2559 K, 2560..3839 V; inside
+ *                        each third, head h owns rows 64h..64h+63. This is the
+ *                        stacked q/k/v projection weight of a Whisper layer;
+ *                        mathematically W_qkv = w_qkv^T, a [1280, 3840] matrix.
+ *  b_qkv  [3840] fp16, or NULL for no bias (Whisper has no K bias: pass zeros).
+ *  qkv    [rows, 3840]   fp16 output, row-major, columns Q | K | V.
+ *  rows   >= 1.
+ * Errors: NULL x/w_qkv/qkv or rows < 1 -> EDDA_ERR_INVALID_ARGUMENT; a pointer
+ * not 16-byte aligned -> EDDA_ERR_MISALIGNED; launch failure -> EDDA_ERR_HIP.
+ */
+edda_status edda_qkv_pack(const void* x, int64_t rows, const void* w_qkv, const void* b_qkv,
+                          void* qkv, void* stream);
+
+/*
+ * Encoder self-attention followed by the output projection, for `batch`
+ * windows of `seq_len` rows each (flash attention: the score matrix is never
+ * stored; "audio.cpp PR #1223" encoder commit message).
+ *
+ *  qkv        [batch*seq_len, 3840] fp16 from edda_qkv_pack (window b occupies
+ *             rows b*seq_len .. b*seq_len+seq_len-1).
+ *  chunk_len  0: full bidirectional attention inside each window.
+ *             c in [1, seq_len]: block-diagonal — query row i of a window admits
+ *             only keys of its own chunk [c*floor(i/c), c*floor(i/c)+c)
+ *             ("higgs-audio-v3-stt-GGUF", chunked encoder note).
+ *  valid_len  HOST int32[batch], or NULL (= seq_len for every window). Keys at
+ *             positions >= valid_len[b] are masked in window b; every query
+ *             row, padded or not, is still computed. Each value in [1, seq_len].
+ *             A query row whose admitted key set is empty gets O = 0.
+ *  w_o        [1280, 1280] fp16, output-feature major (Linear layout; W_o = w_o^T).
+ *  b_o        [1280] fp16 or NULL.
+ *  y          [batch*seq_len, 1280] fp16 output: y = O * W_o + b_o, where O
+ *             holds head h's attention output in columns 64h..64h+63.
+ *  workspace  device scratch of at least edda_encoder_workspace_bytes(batch,
+ *             seq_len) bytes (holds O); contents on entry are ignored.
+ * Errors: EDDA_ERR_INVALID_ARGUMENT for NULL required pointers, batch < 1,
+ * seq_len < 1, chunk_len outside {0} U [1, seq_len], valid_len[b] outside
+ * [1, seq_len]; EDDA_ERR_MISALIGNED; EDDA_ERR_WORKSPACE; EDDA_ERR_HIP.
+ */
+edda_status edda_encoder_attn(const void* qkv, int32_t batch, int32_t seq_len, int32_t chunk_len,
+                              const int32_t* valid_len, const void* w_o, const void* b_o, void* y,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The attention core of edda_encoder_attn without the output projection:
+ * o = concat_h softmax(Q_h K_h^T / 8, masked) V_h, flash-style (scores never
+ * stored). Arguments as for edda_encoder_attn; o is [batch*seq_len, 1280] fp16
+ * with head h in columns 64h..64h+63.
+ * Errors as for edda_encoder_attn (no workspace is needed).
+ */
+edda_status edda_flash_attn(const void* qkv, int32_t batch, int32_t seq_len, int32_t chunk_len,
+                            const int32_t* valid_len, void* o, void* stream);
+
+/* Bytes of workspace edda_encoder_attn needs (0 if the shape is invalid). */
+size_t edda_encoder_workspace_bytes(int32_t batch, int32_t seq_len);
+
+/*
+ * Block-verification attention: n_q query tokens (the anchor plus up to 15
+ * drafted tokens, or one token per beam) attend to a KV cache whose slot j
+ * holds position j ("audio.cpp PR #1223": KV slots indexed by position; beams
+ * share a token-tree cache whose mask rows admit only ancestors). Also serves
+ * cross-attention over the encoder output (mask_rows = NULL).
+ *
+ *  q          [n_q, 20, 64] fp16 query projections (unscaled).
+ *  n_q        in [1, 16].
+ *  k, v       [n_kv, 20, 64] fp16, row j = cache slot j.
+ *  n_kv       >= 1.
+ *  mask_rows  DEVICE uint32 [n_q][ceil(n_kv/32)]; bit (j % 32) of word j / 32
+ *             of row t set = query t admits slot j. NULL = every slot admitted.
+ *             Causal verification of a block in the last n_q slots sets bits
+ *             0 .. n_kv-n_q+t of row t. Contents are not validated; a row with
+ *             no admitted slot gets O = 0. Bits at j >= n_kv are ignored.
+ *  o          [n_q, 20, 64] fp16 output: o[t,h] = softmax_j(q[t,h].k[j,h]/8) v[j,h]
+ *             over the admitted slots j.
+ *  workspace  device scratch of at least edda_verify_workspace_bytes(n_q, n_kv)
+ *             bytes (split-KV partial results; may be 0 bytes when that returns 0).
+ * Errors: EDDA_ERR_INVALID_ARGUMENT (NULL q/k/v/o, n_q outside [1,16], n_kv < 1),
+ * EDDA_ERR_MISALIGNED (q/k/v/o not 16-byte aligned, mask_rows not 4-byte
+ * aligned), EDDA_ERR_WORKSPACE, EDDA_ERR_HIP.
+ */
+edda_status edda_verify_attn(const void* q, int32_t n_q, const void* k, const void* v, int32_t n_kv,
+                             const uint32_t* mask_rows, void* o, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace edda_verify_attn needs (0 when one split suffices or the shape is invalid). */
+size_t edda_verify_workspace_bytes(int32_t n_q, int32_t n_kv);
+
+/* Text of the calling thread's most recent error ("" after a successful call). */
+const char* edda_last_error(void);
+
+/* Library version string. */
+const char* edda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EDDA_H */

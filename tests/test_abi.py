@@ -1,0 +1,131 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects every invalid argument with its
+documented status before any HIP call (fake, never-dereferenced addresses are
+passed; validation must fail first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from whisper_asr_encoder_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "edda.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, HIP = range(6)
+A = 1 << 20           # a 16-byte aligned fake device address (never dereferenced here)
+B = A + 0x10000
+ODD = A + 2           # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libedda.so not built")
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(edda_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_error_text(lib):
+    assert b"gfx950" in lib.edda_version()
+    assert lib.edda_qkv_pack(None, 10, None, None, None, None) == INVALID
+    assert b"non-null" in lib.edda_last_error()
+
+
+def test_workspace_sizes(lib):
+    assert lib.edda_encoder_workspace_bytes(1, 1500) == 1500 * 1280 * 2
+    assert lib.edda_encoder_workspace_bytes(16, 1500) == 16 * 1500 * 1280 * 2
+    assert lib.edda_encoder_workspace_bytes(0, 1500) == 0
+    assert lib.edda_encoder_workspace_bytes(1, -3) == 0
+    assert lib.edda_verify_workspace_bytes(16, 100) == 0      # one split: no workspace
+    assert lib.edda_verify_workspace_bytes(16, 1500) > 0
+    assert lib.edda_verify_workspace_bytes(17, 1500) == 0      # invalid n_q
+    assert lib.edda_verify_workspace_bytes(1, 0) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 10, A, None, B, None), INVALID),
+    ((A, 0, A, None, B, None), INVALID),
+    ((A, -1, A, None, B, None), INVALID),
+    ((A, 1 << 40, A, None, B, None), INVALID),
+    ((ODD, 10, A, None, B, None), MISALIGNED),
+    ((A, 10, A, ODD, B, None), MISALIGNED),
+    ((A, 10, A, None, ODD, None), MISALIGNED),
+])
+def test_qkv_pack_rejects(lib, args, status):
+    assert lib.edda_qkv_pack(*args) == status
+
+
+def enc(lib, qkv=A, batch=1, seq=200, chunk=0, valid=None, w_o=A, b_o=None, y=B, ws=B + (1 << 24),
+        ws_bytes=1 << 30):
+    vl = None
+    if valid is not None:
+        arr = (ctypes.c_int32 * len(valid))(*valid)
+        vl = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    return lib.edda_encoder_attn(qkv, batch, seq, chunk, vl, w_o, b_o, y, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qkv=None), INVALID), (dict(w_o=None), INVALID), (dict(y=None), INVALID),
+    (dict(batch=0), INVALID), (dict(seq=0), INVALID), (dict(chunk=-1), INVALID),
+    (dict(chunk=201), INVALID), (dict(batch=2, valid=[200, 0]), INVALID),
+    (dict(batch=2, valid=[201, 5]), INVALID), (dict(valid=[-4]), INVALID),
+    (dict(batch=1 << 20, seq=1500), INVALID),
+    (dict(qkv=ODD), MISALIGNED), (dict(b_o=ODD), MISALIGNED), (dict(ws=ODD), MISALIGNED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=200 * 1280 * 2 - 1), WORKSPACE),
+])
+def test_encoder_attn_rejects(lib, kw, status):
+    assert enc(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qkv=None), INVALID), (dict(o=None), INVALID), (dict(batch=0), INVALID), (dict(seq=-1), INVALID),
+    (dict(chunk=300), INVALID), (dict(valid=[0]), INVALID), (dict(qkv=ODD), MISALIGNED), (dict(o=ODD), MISALIGNED),
+])
+def test_flash_attn_rejects(lib, kw, status):
+    args = dict(qkv=A, batch=1, seq=200, chunk=0, valid=None, o=B)
+    args.update(kw)
+    vl = None
+    if args["valid"] is not None:
+        arr = (ctypes.c_int32 * len(args["valid"]))(*args["valid"])
+        vl = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    assert lib.edda_flash_attn(args["qkv"], args["batch"], args["seq"], args["chunk"], vl, args["o"], None) == status
+
+
+def ver(lib, q=A, n_q=16, k=A, v=A, n_kv=448, mask=None, o=B, ws=B + (1 << 24), ws_bytes=1 << 30):
+    return lib.edda_verify_attn(q, n_q, k, v, n_kv, mask, o, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(o=None), INVALID),
+    (dict(n_q=0), INVALID), (dict(n_q=17), INVALID), (dict(n_kv=0), INVALID), (dict(n_kv=-5), INVALID),
+    (dict(q=ODD), MISALIGNED), (dict(o=ODD), MISALIGNED), (dict(mask=A + 2), MISALIGNED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+])
+def test_verify_attn_rejects(lib, kw, status):
+    assert ver(lib, **kw) == status
+
+
+def test_mask_packing_bit_order():
+    import numpy as np
+    m = np.zeros((2, 40), dtype=bool)
+    m[0, [0, 5, 31, 32, 39]] = True
+    m[1, :] = True
+    w = _lib.pack_mask_rows(m)
+    assert w.shape == (2, 2) and w.dtype == np.uint32
+    assert w[0, 0] == (1 | (1 << 5) | (1 << 31)) and w[0, 1] == (1 | (1 << 7))
+    assert w[1, 0] == 0xFFFFFFFF and w[1, 1] == 0xFF

@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs. Bar: max |delta| <= 3e-3 and relative Frobenius error
+<= 1e-3 on every compared output, all outputs finite.
+
+Small cases compare every element; full-size workloads (the launch
+configuration the benchmark times) compare whole layers or sampled windows and
+rows that the oracle computes one by one.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from whisper_asr_encoder_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 3e-3
+REL_FRO = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def check(got, ref, what, atol=ATOL, rel_fro=REL_FRO):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    diff = np.abs(got - ref)
+    mx = float(diff.max()) if diff.size else 0.0
+    nrm = float(np.linalg.norm(ref))
+    fro = float(np.linalg.norm(got - ref) / nrm) if nrm > 0 else float(np.linalg.norm(got - ref))
+    say(f"  {what}: max|d| = {mx:.3e}, rel_fro = {fro:.3e}")
+    assert mx <= atol, f"{what}: max |delta| {mx:.3e} > {atol}"
+    assert fro <= rel_fro, f"{what}: relative Frobenius {fro:.3e} > {rel_fro}"
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch
+    from whisper_asr_encoder_amd import _lib
+    _lib.load()
+    return torch
+
+
+def dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy()
+
+
+def run_encoder(torch, x, weights, batch, seq_len, chunk_len, valid_len, poison=True, keep=None):
+    """Run every sublayer through the C ABI; return host copies of y (and qkv) for the
+    layers in `keep` (default all). Every layer's output is checked finite on the device."""
+    from whisper_asr_encoder_amd.encoder import EncoderAttention
+    enc = EncoderAttention(weights, batch, seq_len, chunk_len, valid_len)
+    keep = set(range(len(weights))) if keep is None else set(keep)
+    xd = dev(torch, x)
+    y = torch.empty((batch * seq_len, I.D_MODEL), dtype=torch.float16, device="cuda")
+    ys, qkvs = {}, {}
+    for layer in range(len(weights)):
+        y.fill_(float("nan") if poison else 0.0)
+        enc.qkv.fill_(float("nan"))
+        enc.workspace.fill_(255)
+        enc.sublayer(xd, layer, y)
+        assert bool(torch.isfinite(y).all()), f"layer {layer}: non-finite output"
+        if layer in keep:
+            ys[layer] = host(y)
+            qkvs[layer] = host(enc.qkv)
+    torch.cuda.synchronize()
+    return ys, qkvs
+
+
+def oracle_layer(x, w, batch, seq_len, chunk_len, valid_len, rows=None):
+    return oracle.encoder_attention(x, w.w_qkv, w.b_qkv, w.w_o, w.b_o, batch, seq_len, chunk_len,
+                                    valid_len, I.N_HEADS, rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# Encoder: small cases, every element.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("batch,seq_len,chunk_len,valid", [
+    (1, 200, 0, None),          # one 4 s chunk (the small workload)
+    (1, 1, 0, None),            # a single frame
+    (1, 37, 0, None),           # ragged: shorter than every tile
+    (1, 300, 0, [129]),         # key tail cut mid-tile
+    (2, 150, 0, [1, 150]),      # one key only / full
+    (1, 450, 200, None),        # chunks 200, 200, 50
+    (1, 450, 200, [260]),       # last chunk fully padded -> zero rows
+    (1, 130, 1, None),          # chunk of one frame: O = V row
+    (1, 200, 65, [199]),        # chunk just above a key tile
+    (3, 96, 32, [96, 40, 33]),  # several windows, chunked and padded
+])
+def test_encoder_small(torch, batch, seq_len, chunk_len, valid):
+    say(f"encoder small batch={batch} seq={seq_len} chunk={chunk_len} valid={valid}")
+    wl = I.encoder_workload(0, batch=batch, seq_len=seq_len, chunk_len=chunk_len, layers=1, valid_len=valid)
+    w = wl.weights(0)
+    ys, qkvs = run_encoder(torch, wl.x, [w], batch, seq_len, chunk_len, wl.valid_len)
+    ref = oracle_layer(wl.x, w, batch, seq_len, chunk_len, wl.valid_len)
+    check(qkvs[0], ref["qkv"], "qkv")
+    check(ys[0], ref["y"], "y")
+
+
+def test_encoder_bias_variants(torch):
+    say("encoder with output bias and without QKV bias")
+    wl = I.encoder_workload(0, seq_len=77, layers=1)
+    w = wl.weights(0)
+    r = np.random.default_rng(7)
+    w.b_o = (r.standard_normal(I.D_MODEL) * 0.1).astype(np.float16)
+    ys, _ = run_encoder(torch, wl.x, [w], 1, 77, 0, None)
+    check(ys[0], oracle_layer(wl.x, w, 1, 77, 0, [77])["y"], "y with b_o")
+    w.b_qkv = None
+    w.b_o = None
+    ys, qkvs = run_encoder(torch, wl.x, [w], 1, 77, 0, None)
+    ref = oracle_layer(wl.x, w, 1, 77, 0, [77])
+    check(qkvs[0], ref["qkv"], "qkv without bias")
+    check(ys[0], ref["y"], "y without bias")
+
+
+def test_encoder_deterministic(torch):
+    say("encoder determinism")
+    wl = I.encoder_workload(1, layers=1)
+    w = wl.weights(0)
+    a, _ = run_encoder(torch, wl.x, [w], 1, 1500, 0, None)
+    b, _ = run_encoder(torch, wl.x, [w], 1, 1500, 0, None, poison=False)
+    assert np.array_equal(a[0], b[0])
+
+
+# ---------------------------------------------------------------------------
+# Encoder: the full-size workloads (32 sublayers, as timed).
+# ---------------------------------------------------------------------------
+
+def test_config_small_chunk(torch):
+    say("workload: one 4 s chunk, one sublayer")
+    wl = I.encoder_workload(0)
+    w = wl.weights(0)
+    ys, qkvs = run_encoder(torch, wl.x, [w], 1, 200, 0, None)
+    ref = oracle_layer(wl.x, w, 1, 200, 0, [200])
+    check(qkvs[0], ref["qkv"], "qkv")
+    check(ys[0], ref["y"], "y")
+
+
+def test_config_30s_window(torch):
+    say("workload: 30 s window, 32 sublayers (layers 0, 13, 31 compared in full)")
+    wl = I.encoder_workload(1)
+    weights = [wl.weights(l) for l in range(wl.layers)]
+    ys, qkvs = run_encoder(torch, wl.x, weights, 1, 1500, 0, None, keep=(0, 13, 31))
+    for l in (0, 13, 31):
+        ref = oracle_layer(wl.x, weights[l], 1, 1500, 0, [1500])
+        check(qkvs[l], ref["qkv"], f"layer {l} qkv")
+        check(ys[l], ref["y"], f"layer {l} y")
+
+
+def test_config_chunked_45s(torch):
+    say("workload: 45 s in 4 s chunks, 32 sublayers (layers 0, 31 in full)")
+    wl = I.encoder_workload(2)
+    weights = [wl.weights(l) for l in range(wl.layers)]
+    ys, _ = run_encoder(torch, wl.x, weights, 1, wl.seq_len, wl.chunk_len, wl.valid_len, keep=(0, 31))
+    for l in (0, 31):
+        ref = oracle_layer(wl.x, weights[l], 1, wl.seq_len, wl.chunk_len, wl.valid_len)
+        check(ys[l], ref["y"], f"layer {l} y")
+
+
+def test_config_batched_windows(torch):
+    say("workload: 16 windows with padded key tails, 32 sublayers (sampled)")
+    wl = I.encoder_workload(3)
+    weights = [wl.weights(l) for l in range(wl.layers)]
+    ys, _ = run_encoder(torch, wl.x, weights, wl.batch, wl.seq_len, 0, wl.valid_len, keep=(0, 17, 31))
+    order = np.argsort(wl.valid_len)
+    picks = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
+    rng = np.random.default_rng(11)
+    for l, wins in ((0, picks), (31, picks[:1]), (17, picks[1:2])):
+        for b in wins:
+            rows = b * wl.seq_len + np.sort(rng.choice(wl.seq_len, size=96, replace=False))
+            rows = np.unique(np.concatenate([rows, [b * wl.seq_len, b * wl.seq_len + wl.seq_len - 1,
+                                                    b * wl.seq_len + int(wl.valid_len[b]) - 1]]))
+            ref = oracle_layer(wl.x, weights[l], wl.batch, wl.seq_len, 0, wl.valid_len, rows=rows)
+            check(ys[l][rows], ref["y"], f"layer {l} window {b} (valid {wl.valid_len[b]}) y")
+
+
+# ---------------------------------------------------------------------------
+# Verification attention.
+# ---------------------------------------------------------------------------
+
+def run_verify(torch, case, mask=None, use_mask=True):
+    from whisper_asr_encoder_amd.encoder import VerifyAttention
+    va = VerifyAttention(max(case.n_kv, 1))
+    m = case.mask if use_mask else None
+    if mask is not None:
+        m = mask
+    o = torch.full(case.q.shape, float("nan"), dtype=torch.float16, device="cuda")
+    va.workspace.fill_(255)
+    va(dev(torch, case.q), dev(torch, case.k), dev(torch, case.v), va.mask_rows(m), o)
+    torch.cuda.synchronize()
+    return host(o), m
+
+
+@pytest.mark.parametrize("trial", range(8))
+def test_verify_workload(torch, trial):
+    L = I.cache_length(trial)
+    say(f"verify trial {trial}: causal self-attention over L={L}, cross over 1500, beam tree")
+    for layer in (0, 31):
+        c = I.verify_self_case(trial, layer)
+        got, m = run_verify(torch, c)
+        check(got, oracle.verify_attention(c.q, c.k, c.v, m), f"L{layer} causal")
+        x = I.verify_cross_case(trial, layer)
+        got, _ = run_verify(torch, x)
+        check(got, oracle.verify_attention(x.q, x.k, x.v, None), f"L{layer} cross")
+        t = I.verify_tree_case(trial, layer)
+        got, m = run_verify(torch, t)
+        check(got, oracle.verify_attention(t.q, t.k, t.v, m), f"L{layer} tree")
+
+
+@pytest.mark.parametrize("n_q,n_kv,kind", [
+    (1, 1, "none"), (1, 33, "causal"), (16, 16, "causal"), (16, 31, "causal"), (16, 32, "causal"),
+    (16, 33, "causal"), (16, 127, "random"), (16, 128, "none"), (16, 129, "causal"),
+    (5, 300, "random"), (16, 1500, "none"), (7, 4096, "random"), (16, 200, "empty_rows")])
+def test_verify_edges(torch, n_q, n_kv, kind):
+    say(f"verify edge n_q={n_q} n_kv={n_kv} {kind}")
+    r = np.random.default_rng(n_q * 7919 + n_kv)
+    q = r.standard_normal((n_q, 20, 64)).astype(np.float16)
+    k = (r.standard_normal((n_kv, 20, 64)) * 1.5).astype(np.float16)
+    v = r.standard_normal((n_kv, 20, 64)).astype(np.float16)
+    if kind == "causal":
+        mask = oracle.causal_rows(n_q, n_kv) if n_kv >= n_q else r.random((n_q, n_kv)) < 0.5
+    elif kind == "none":
+        mask = None
+    else:
+        mask = r.random((n_q, n_kv)) < 0.3
+        if kind == "empty_rows":
+            mask[[0, 5, 15]] = False
+    case = I.VerifyCase(q=q, k=k, v=v, mask=mask, kind=kind)
+    got, m = run_verify(torch, case)
+    ref = oracle.verify_attention(q, k, v, m)
+    check(got, ref, "o")
+    if kind == "empty_rows":
+        assert np.all(got[[0, 5, 15]] == 0)

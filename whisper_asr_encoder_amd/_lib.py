@@ -1,0 +1,202 @@
+"""ctypes binding of libedda.so (argument marshalling only).
+
+Every computation runs in the library's HIP kernels; this module turns torch
+tensors into device pointers, passes the current HIP stream, and raises on a
+non-zero status with the library's error text. PyTorch provides device memory
+and streams and nothing else. There is no fallback: if the library is missing
+or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libedda.so")
+
+D_MODEL = 1280
+N_HEADS = 20
+HEAD_DIM = 64
+QKV_COLS = 3 * D_MODEL
+MAX_VERIFY_QUERIES = 16
+
+STATUS = {0: "EDDA_OK", 1: "EDDA_ERR_INVALID_ARGUMENT", 2: "EDDA_ERR_UNSUPPORTED",
+          3: "EDDA_ERR_MISALIGNED", 4: "EDDA_ERR_WORKSPACE", 5: "EDDA_ERR_HIP"}
+
+# Every symbol include/edda.h declares.
+EXPORTS = ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_encoder_workspace_bytes", "edda_verify_attn",
+           "edda_verify_workspace_bytes", "edda_last_error", "edda_version")
+
+
+class EddaError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"{STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libedda.so (once) and declare its prototypes. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() or "
+                           "python -m whisper_asr_encoder_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.edda_qkv_pack.argtypes = [vp, i64, vp, vp, vp, vp]
+    lib.edda_encoder_attn.argtypes = [vp, i32, i32, i32, ctypes.POINTER(i32), vp, vp, vp, vp, sz, vp]
+    lib.edda_flash_attn.argtypes = [vp, i32, i32, i32, ctypes.POINTER(i32), vp, vp]
+    lib.edda_encoder_workspace_bytes.argtypes = [i32, i32]
+    lib.edda_encoder_workspace_bytes.restype = sz
+    lib.edda_verify_attn.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.edda_verify_workspace_bytes.argtypes = [i32, i32]
+    lib.edda_verify_workspace_bytes.restype = sz
+    lib.edda_last_error.restype = ctypes.c_char_p
+    lib.edda_version.restype = ctypes.c_char_p
+    for name in ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_verify_attn"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().edda_last_error().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise EddaError(status, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require(t, name, shape=None, dtype=None):
+    import torch
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return torch
+
+
+# ---------------------------------------------------------------------------
+# Host-side layout helpers (load time, not part of the timed path).
+# ---------------------------------------------------------------------------
+
+def linear_layout(w_in_out: np.ndarray) -> np.ndarray:
+    """Weight packing: a [in, out] matrix W (y = x W) -> its output-feature-major
+    copy [out, in] (the layout the library reads; rows of a stacked q/k/v Linear weight)."""
+    return np.ascontiguousarray(np.asarray(w_in_out, dtype=np.float16).T)
+
+
+def pack_mask_rows(mask: np.ndarray) -> np.ndarray:
+    """bool [n_q, n_kv] -> uint32 [n_q, ceil(n_kv/32)], bit j % 32 of word j // 32 = slot j admitted."""
+    mask = np.asarray(mask, dtype=bool)
+    n_q, n_kv = mask.shape
+    words = (n_kv + 31) // 32
+    padded = np.zeros((n_q, words * 32), dtype=bool)
+    padded[:, :n_kv] = mask
+    packed = np.packbits(padded.reshape(n_q, words, 32), axis=2, bitorder="little")
+    return np.ascontiguousarray(packed).view("<u4").reshape(n_q, words).astype(np.uint32)
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI).
+# ---------------------------------------------------------------------------
+
+def edda_qkv_pack(x, w_qkv, b_qkv, qkv, stream=None):
+    """qkv[rows, 3840] = x[rows, 1280] * w_qkv^T + b_qkv; w_qkv is [3840, 1280] (Linear layout)."""
+    lib = load()
+    torch = _require(x, "x", dtype=None)
+    rows = x.shape[0]
+    _require(x, "x", (rows, D_MODEL), torch.float16)
+    _require(w_qkv, "w_qkv", (QKV_COLS, D_MODEL), torch.float16)
+    if b_qkv is not None:
+        _require(b_qkv, "b_qkv", (QKV_COLS,), torch.float16)
+    _require(qkv, "qkv", (rows, QKV_COLS), torch.float16)
+    _check(lib.edda_qkv_pack(_ptr(x), rows, _ptr(w_qkv), _ptr(b_qkv), _ptr(qkv), _stream(stream)))
+
+
+def encoder_workspace_bytes(batch: int, seq_len: int) -> int:
+    return int(load().edda_encoder_workspace_bytes(batch, seq_len))
+
+
+def edda_encoder_attn(qkv, batch, seq_len, chunk_len, valid_len, w_o, b_o, y, workspace, stream=None):
+    """y = attention(qkv) * w_o^T + b_o over `batch` windows of `seq_len` rows.
+    valid_len: host sequence of ints (or None); workspace: device uint8 tensor."""
+    lib = load()
+    torch = _require(qkv, "qkv", (batch * seq_len, QKV_COLS))
+    _require(w_o, "w_o", (D_MODEL, D_MODEL), torch.float16)
+    if b_o is not None:
+        _require(b_o, "b_o", (D_MODEL,), torch.float16)
+    _require(y, "y", (batch * seq_len, D_MODEL), torch.float16)
+    _require(workspace, "workspace")
+    _require(qkv, "qkv", dtype=torch.float16)
+    keep, vl = _valid_arg(valid_len, batch)
+    _check(lib.edda_encoder_attn(_ptr(qkv), batch, seq_len, chunk_len, vl, _ptr(w_o), _ptr(b_o), _ptr(y),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)))
+    del keep
+
+
+def _valid_arg(valid_len, batch):
+    if valid_len is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(valid_len, dtype=np.int32).reshape(-1))
+    if arr.size != batch:
+        raise ValueError(f"valid_len must have {batch} entries")
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def edda_flash_attn(qkv, batch, seq_len, chunk_len, valid_len, o, stream=None):
+    """o[rows, 1280] = per-head masked softmax attention of qkv (no output projection)."""
+    lib = load()
+    torch = _require(qkv, "qkv", (batch * seq_len, QKV_COLS))
+    _require(qkv, "qkv", dtype=torch.float16)
+    _require(o, "o", (batch * seq_len, D_MODEL), torch.float16)
+    keep, vl = _valid_arg(valid_len, batch)
+    _check(lib.edda_flash_attn(_ptr(qkv), batch, seq_len, chunk_len, vl, _ptr(o), _stream(stream)))
+    del keep
+
+
+def verify_workspace_bytes(n_q: int, n_kv: int) -> int:
+    return int(load().edda_verify_workspace_bytes(n_q, n_kv))
+
+
+def edda_verify_attn(q, k, v, mask_rows, o, workspace=None, stream=None):
+    """o[n_q,20,64] = softmax over admitted slots of (q.k/8) times v. mask_rows: device uint32
+    tensor [n_q, ceil(n_kv/32)] (see pack_mask_rows) or None for every slot admitted."""
+    lib = load()
+    torch = _require(q, "q")
+    n_q, n_kv = q.shape[0], k.shape[0]
+    _require(q, "q", (n_q, N_HEADS, HEAD_DIM), torch.float16)
+    _require(k, "k", (n_kv, N_HEADS, HEAD_DIM), torch.float16)
+    _require(v, "v", (n_kv, N_HEADS, HEAD_DIM), torch.float16)
+    _require(o, "o", (n_q, N_HEADS, HEAD_DIM), torch.float16)
+    if mask_rows is not None:
+        _require(mask_rows, "mask_rows", (n_q, (n_kv + 31) // 32))
+        if mask_rows.dtype not in (torch.int32, torch.uint32):
+            raise ValueError("mask_rows must hold 32-bit words")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.edda_verify_attn(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, _ptr(mask_rows), _ptr(o),
+                                _ptr(workspace), ws_bytes, _stream(stream)))
