@@ -1,24 +1,34 @@
-// Kernel 2: flash attention for the encoder (fp16 Q/K/V, fp32 online softmax and
-// accumulation); the score matrix never leaves registers.
+// Kernel 2: flash attention for the encoder (fp16 Q/K/V, fp32 softmax statistics
+// and accumulation); scores never leave registers.
 //
-// Work unit: one workgroup per (window, chunk segment, 32*NW query rows, head).
-// With chunk_len = c > 0 every chunk of a window is an independent segment
-// whose rows admit keys [seg0, min(seg0 + c, valid)); with c = 0 the segment is
-// the whole window and the key interval is [0, valid).  Masking therefore
-// reduces to one key interval per workgroup: the key loop visits only that
-// interval, and only its last, partial 64-key tile masks elements.
+// Work unit.  One workgroup per (window, chunk segment, 128 query rows, head).
+// With chunk_len = c > 0 each chunk of a window is an independent segment whose
+// rows admit keys [seg0, min(seg0 + c, valid)); with c = 0 the segment is the
+// whole window and its key interval is [0, valid).  Masking is therefore one key
+// interval per workgroup: only the tail of that interval is masked elementwise.
 //
-// Per wave (32 query rows) and 64-key tile, on 32x32x16 MFMAs:
-//   S^T = K Q^T  : K fragments from LDS, Q^T fragments resident in registers.
-//                  Lane l then holds 32 scores of ONE query (l % 32), so row
-//                  max / sum need only per-lane work plus one exchange with
-//                  lane l ^ 32.
-//   P   = 2^(S*log2e/8 - m)   (fp32, v_exp_f32), packed to fp16 with RNE.
-//   O^T += V^T P^T : the fp16 P values are already laid out as the B operand
-//                  (the MFMA's k index is permuted consistently on both
-//                  operands); V^T fragments come from a transposed LDS copy.
-// K/V tiles are double-buffered in LDS: the global loads of tile t+1 are in
-// flight while tile t is computed.
+// Workgroup = 8 waves = 2 query groups (64 rows each) x 4 key quarters.  Keys are
+// consumed in iterations of 128: quarter j takes keys [32 j, 32 j + 32) of each
+// iteration, so each wave sees a quarter of the keys and the four partial results
+// of a query group are merged through LDS at the end.  Two waves share every K/V
+// tile (one per query group), and each wave runs two 32-row query blocks against
+// each K/V fragment, halving LDS reads per MFMA.
+//
+// Per wave and 32-key tile, on 32x32x16 MFMAs:
+//   S^T = K Q^T   K fragments from LDS, Q^T fragments resident in registers; lane l
+//                 holds 16 scores of query l % 32 (per query block), so row
+//                 statistics need per-lane work plus one exchange with lane l ^ 32.
+//   P = 2^(S log2(e)/8 - m)  with m a per-row reference: the row maximum of the
+//                 wave's first tile.  Later tiles reuse it; when a tile's sum of P
+//                 reaches 2^14 (a P value might approach the fp16 range) the tile
+//                 is recomputed against the new maximum and the running sums are
+//                 rescaled, so the result is exact softmax either way.
+//   l += sum P    with v_dot2_f32_f16 over the packed fp16 P that the PV MFMA uses.
+//   O^T += V^T P^T  fp16 P is already laid out as the B operand (the MFMA's k index
+//                 is permuted identically on both operands); V^T fragments are read
+//                 with ds_read_b64_tr_b16 from the row-major V tile.
+// K and V tiles reach LDS by direct-to-LDS DMA (natural row layout, 16-byte chunks
+// XOR-swizzled per row) through a 4-stage ring with one barrier per iteration.
 #include <math.h>
 
 #include "device.hpp"
@@ -27,225 +37,348 @@
 namespace edda {
 namespace {
 
-constexpr int kKeyTile = 64;
-constexpr int kKld = kHeadDim + 8;   // K tile row stride (halves): 144 B, 16-byte aligned
-constexpr int kVld = kKeyTile + 4;   // V^T tile row stride (halves): 136 B, 8-byte aligned
+constexpr int kKT = 32;                 // keys per tile (one quarter of an iteration)
+constexpr int kQuarters = 4;
+constexpr int kQGroups = 2;
+constexpr int kQW = 64;                 // query rows per wave
+constexpr int kBMq = kQGroups * kQW;    // 128 query rows per workgroup
+constexpr int kIterKeys = kQuarters * kKT;
+constexpr int kWaves = kQGroups * kQuarters;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kStages = 4;
+constexpr int kRowB = kHeadDim * 2;     // 128 bytes per K/V row
+constexpr int kTileB = kKT * kRowB;     // 4 KB
+constexpr int kStageB = kQuarters * 2 * kTileB;  // K and V tiles of every quarter: 32 KB
+constexpr int kXcds = 8;
 constexpr int kMaxBatchPerLaunch = 256;
+constexpr float kRedoSum = 16384.0f;    // per-tile sum of P that triggers a re-reference
 
 struct ValidLens {
   int32_t v[kMaxBatchPerLaunch];
 };
 
-template <int NW>
-__global__ __launch_bounds__(NW * kWave) void flash_attn_kernel(const f16* __restrict__ qkv,
-                                                                f16* __restrict__ O, int seq_len,
-                                                                int seg_len_max, int n_segs,
-                                                                int tiles_per_seg, int window0,
-                                                                ValidLens valid) {
-  constexpr int NT = NW * kWave;
-  constexpr int BM = 32 * NW;
-  constexpr int KC = kKeyTile * 8 / NT;   // K 16-byte chunks per thread per tile
-  constexpr int VP = kKeyTile / 2 * 8 / NT;  // V key-pair chunks per thread per tile
-  static_assert(KC >= 1 && VP >= 1, "tile too small for the workgroup");
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-  __shared__ __attribute__((aligned(16))) f16 Ks[2][kKeyTile * kKld];
-  __shared__ __attribute__((aligned(16))) f16 Vts[2][kHeadDim * kVld];
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(g), "s"(lds_addr) : "memory", "m0");
+}
+template <int n>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(n) : "memory");
+}
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+// Byte offset of element (row, col) in a swizzled 128-byte-row tile.
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * kRowB + ((((col >> 3) ^ swz(row)) << 4) | ((col & 7) << 1));
+}
+
+// Transposed LDS read: with lane 4r+c of each 16-lane group addressing 4 consecutive
+// fp16 of row r, lane i of the group receives column i of those 4 rows.
+__device__ __forceinline__ f16x4 read_tr(const char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_void*)p);
+  return __builtin_bit_cast(f16x4, v);
+}
+
+__global__ __launch_bounds__(kThreads) void flash_attn_kernel(
+    const f16* __restrict__ qkv, f16* __restrict__ O, int seq_len, int seg_len_max, int n_segs,
+    int tiles_per_seg, int window0, ValidLens valid) {
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qg = wave / kQuarters, quarter = wave % kQuarters;
   const int l32 = lane & 31, g = lane >> 5;
-  const int head = blockIdx.y;
 
-  int t = blockIdx.x;
+  // XCD-aware decode: consecutive logical tiles (the query tiles of one head) share an XCD.
+  const int nwg = gridDim.x, wid = blockIdx.x;
+  const int xcd = wid % kXcds, per = nwg / kXcds, rem = nwg % kXcds;
+  int t = xcd * per + min(xcd, rem) + wid / kXcds;
   const int qt = t % tiles_per_seg;
   t /= tiles_per_seg;
+  const int head = t % kHeads;
+  t /= kHeads;
   const int seg = t % n_segs;
   const int wloc = t / n_segs;
   const int window = window0 + wloc;
 
   const int seg0 = seg * seg_len_max;
-  const int seg_len = min(seg_len_max, seq_len - seg0);
-  const int q_begin = seg0 + qt * BM;
-  if (q_begin >= seg0 + seg_len) return;  // whole workgroup beyond this segment's rows
+  const int seg_end = min(seg0 + seg_len_max, seq_len);
+  const int q_begin = seg0 + qt * kBMq;
+  if (q_begin >= seg_end) return;  // uniform for the workgroup
   const int k_lo = seg0;
   const int k_hi = max(k_lo, min(seg0 + seg_len_max, (int)valid.v[wloc]));
 
   const size_t win_row0 = (size_t)window * seq_len;
-  const int q_row = q_begin + 32 * wave + l32;  // this lane's query (window-local)
-  const bool row_ok = q_row < seg0 + seg_len;
   const f16* qkv_w = qkv + win_row0 * kQkvCols;
-  f16* out_row = O + (win_row0 + q_row) * kDModel + head * kHeadDim;
+  const int wq0 = q_begin + qg * kQW;  // this wave's first query row
+  const bool wave_rows = wq0 < seg_end;
 
-  if (k_hi <= k_lo) {  // no admitted key: O = 0 for every row of the segment
-    if (row_ok) {
-      const f16x8 z = {};
+  if (k_hi <= k_lo) {  // no admitted key: zero rows
+    if (wave_rows) {
 #pragma unroll
-      for (int c = 0; c < kHeadDim / 8; c += 2) store16(out_row + 8 * (c + g), z);
+      for (int qb = 0; qb < 2; ++qb) {
+        const int q = wq0 + 32 * qb + l32;
+        if (q < seg_end) {
+          f16* orow = O + (win_row0 + q) * kDModel + head * kHeadDim;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) store16(orow + 8 * (2 * c + g), (f16x8){});
+        }
+      }
     }
     return;
   }
 
-  // Q^T fragments (B operand): lane holds Q[q_row][16 s + 8 g .. +7] for s = 0..3.
-  f16x8 qf[4];
-  {
-    const f16x8 z = {};
-    const f16* qp = qkv_w + (size_t)q_row * kQkvCols + head * kHeadDim + 8 * g;
+  // Q^T fragments: lane holds Q[wq0 + 32 qb + l32][16 s + 8 g .. +7].
+  f16x8 qf[2][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qf[s] = row_ok ? load16(qp + 16 * s) : z;
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q = wq0 + 32 * qb + l32;
+    const f16* qp = qkv_w + (size_t)q * kQkvCols + head * kHeadDim + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[qb][s] = q < seg_end ? load16(qp + 16 * s) : (f16x8){};
   }
 
-  const f16* kbase = qkv_w + kDModel + head * kHeadDim;
-  const f16* vbase = qkv_w + 2 * kDModel + head * kHeadDim;
-  f16x8 rk[KC], rv0[VP], rv1[VP];
-  const f16x8 z8 = {};
-
-  auto gload = [&](int kt) {
+  // DMA duties: wave (qg, quarter) loads quarter's K (qg 0) or V (qg 1) tile: 4 x 8 rows.
+  const int n_iter = (k_hi - k_lo + kIterKeys - 1) / kIterKeys;
+  const uint32_t smem_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
+  const f16* dma_base = qkv_w + (qg == 0 ? kDModel : 2 * kDModel) + head * kHeadDim;
+  const int drow = lane >> 3;  // row within an 8-row DMA group
+  auto issue = [&](int it) {
+    const uint32_t st = smem_addr + (it % kStages) * kStageB + quarter * 2 * kTileB + qg * kTileB;
+    const int key0 = k_lo + it * kIterKeys + quarter * kKT;
 #pragma unroll
-    for (int r = 0; r < KC; ++r) {
-      const int idx = tid + NT * r;
-      const int key = kt + (idx >> 3), c = idx & 7;
-      rk[r] = key < k_hi ? load16(kbase + (size_t)key * kQkvCols + 8 * c) : z8;
-    }
-#pragma unroll
-    for (int r = 0; r < VP; ++r) {
-      const int idx = tid + NT * r;
-      const int key = kt + 2 * (idx >> 3), c = idx & 7;
-      rv0[r] = key < k_hi ? load16(vbase + (size_t)key * kQkvCols + 8 * c) : z8;
-      rv1[r] = key + 1 < k_hi ? load16(vbase + (size_t)(key + 1) * kQkvCols + 8 * c) : z8;
+    for (int j = 0; j < kKT / 8; ++j) {
+      const int row = 8 * j + drow;
+      const int key = min(key0 + row, k_hi - 1);  // rows past the interval: any valid row (masked)
+      const int lc = (lane & 7) ^ swz(row);
+      dma16(dma_base + (size_t)key * kQkvCols + 8 * lc, st + j * 1024);
     }
   };
-  auto sstore = [&](int buf) {
+  constexpr int IPW = kKT / 8;
+
+  // Per-lane LDS offsets.
+  int kfrag_off[4];
 #pragma unroll
-    for (int r = 0; r < KC; ++r) {
-      const int idx = tid + NT * r;
-      store16(&Ks[buf][(idx >> 3) * kKld + 8 * (idx & 7)], rk[r]);
+  for (int s = 0; s < 4; ++s) kfrag_off[s] = tile_off(l32, 16 * s + 8 * g);
+  int vtr_off[2][2][2];  // [db][sigma][half]
+  {
+    const int i = lane & 15, r = i >> 2, c = i & 3;
+    const int d0 = 16 * ((lane >> 4) & 1) + 4 * c;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) vtr_off[db][sg][h] = tile_off(16 * sg + 8 * h + 4 * g + r, 32 * db + d0);
+  }
+
+  const float c_scale = kLog2e / 8.0f;
+  float mref[2] = {-INFINITY, -INFINITY};  // raw-score reference per query block
+  float mref_c[2] = {0.0f, 0.0f};
+  float l_run[2] = {0.0f, 0.0f};
+  f32x16 oacc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) oacc[a][b] = (f32x16){};
+  bool have_ref = false;
+
+#pragma unroll
+  for (int p = 0; p < kStages - 1; ++p)
+    if (p < n_iter) issue(p);
+
+  for (int it = 0; it < n_iter; ++it) {
+    // Tiles issued after iteration it: min(kStages-2, n_iter-1-it).
+    if (it + 2 < n_iter) {
+      wait_vmcnt_barrier<IPW * 2>();
+    } else if (it + 1 < n_iter) {
+      wait_vmcnt_barrier<IPW>();
+    } else {
+      wait_vmcnt_barrier<0>();
     }
+    if (it + kStages - 1 < n_iter) issue(it + kStages - 1);
+
+    const int kt0 = k_lo + it * kIterKeys + quarter * kKT;
+    if (!wave_rows || kt0 >= k_hi) continue;  // wave-uniform: nothing for this wave here
+    const char* ks = smem + (it % kStages) * kStageB + quarter * 2 * kTileB;
+    const char* vs = ks + kTileB;
+    const bool partial = kt0 + kKT > k_hi;
+
+    f16x8 kf[4];
 #pragma unroll
-    for (int r = 0; r < VP; ++r) {
-      const int idx = tid + NT * r;
-      const int kp = idx >> 3, c = idx & 7;
-      // V^T[d][key]: the two keys of a pair share one 32-bit LDS word.
+    for (int s = 0; s < 4; ++s) kf[s] = *reinterpret_cast<const f16x8*>(ks + kfrag_off[s]);
+    f32x16 sacc[2];
+    auto scores = [&]() {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const f16x2 pr = {rv0[r][e], rv1[r][e]};
-        *reinterpret_cast<f16x2*>(&Vts[buf][(8 * c + e) * kVld + 2 * kp]) = pr;
+      for (int qb = 0; qb < 2; ++qb) {
+        sacc[qb] = (f32x16){};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sacc[qb] = mfma_32x32x16(kf[s], qf[qb][s], sacc[qb]);
+      }
+      if (partial) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (kt0 + 8 * (e >> 2) + 4 * g + (e & 3) >= k_hi) sacc[qb][e] = -INFINITY;
+      }
+    };
+    // Row maximum of this tile per query block (both lane halves agree).
+    auto tile_max = [&](int qb) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, sacc[qb][e]);
+      return fmaxf(m, __shfl_xor(m, 32));
+    };
+    f16x8 pf[2][2];
+    float lt[2];
+    auto probabilities = [&]() {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float p[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) p[e] = exp2_fast(fmaf(sacc[qb][e], c_scale, -mref_c[qb]));
+        float acc = 0.0f;
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+          const f16x2 a = pack_rne(p[8 * sg + 0], p[8 * sg + 1]), b = pack_rne(p[8 * sg + 2], p[8 * sg + 3]);
+          const f16x2 c = pack_rne(p[8 * sg + 4], p[8 * sg + 5]), d = pack_rne(p[8 * sg + 6], p[8 * sg + 7]);
+          const f16x2 one = {(f16)1.0f, (f16)1.0f};
+          acc = __builtin_amdgcn_fdot2(a, one, acc, false);
+          acc = __builtin_amdgcn_fdot2(b, one, acc, false);
+          acc = __builtin_amdgcn_fdot2(c, one, acc, false);
+          acc = __builtin_amdgcn_fdot2(d, one, acc, false);
+          pf[qb][sg] = (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+        }
+        lt[qb] = acc;
+      }
+    };
+
+    scores();
+    if (!have_ref) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        mref[qb] = tile_max(qb);  // finite: key kt0 < k_hi is admitted for every row
+        mref_c[qb] = mref[qb] * c_scale;
+      }
+      have_ref = true;
+    }
+    probabilities();
+    // A tile sum this large means scores rose well above the reference: re-reference.
+    if (__builtin_amdgcn_ballot_w64(lt[0] >= kRedoSum || lt[1] >= kRedoSum) != 0) {
+      scores();
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float m_new = fmaxf(mref[qb], tile_max(qb));
+        const float alpha = exp2_fast((mref[qb] - m_new) * c_scale);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[qb][db][e] *= alpha;
+        mref[qb] = m_new;
+        mref_c[qb] = m_new * c_scale;
+      }
+      probabilities();
+    }
+    l_run[0] += lt[0];
+    l_run[1] += lt[1];
+
+    // O^T += V^T P^T over two 16-key steps.
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const f16x4 lo = read_tr(vs + vtr_off[db][sg][0]);
+        const f16x4 hi = read_tr(vs + vtr_off[db][sg][1]);
+        const f16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) oacc[qb][db] = mfma_32x32x16(vf, pf[qb][sg], oacc[qb][db]);
       }
     }
-  };
+  }
 
-  const float c_scale = kLog2e / 8.0f;  // log2(e) / sqrt(64)
-  float m_run = -INFINITY;              // running max of raw scores for this lane's query
-  float l_run = 0.0f;                   // this lane's partial sum (half of the keys)
-  f32x16 oacc[2] = {(f32x16){}, (f32x16){}};
-  const bool wave_active = __builtin_amdgcn_readfirstlane(
-      (int)(q_begin + 32 * wave < seg0 + seg_len));
-
-  gload(k_lo);
-  sstore(0);
+  // Merge the four key quarters of each query group through LDS (the ring is free:
+  // every DMA completed before the last iteration's barrier).
   __syncthreads();
-  const int n_tiles = (k_hi - k_lo + kKeyTile - 1) / kKeyTile;
-  for (int it = 0; it < n_tiles; ++it) {
-    const int buf = it & 1;
-    const int kt = k_lo + it * kKeyTile;
-    if (it + 1 < n_tiles) gload(kt + kKeyTile);
-
-    if (wave_active) {
-      // S^T for keys kt + 32 kb + (8 i + 4 g + j), query l32.
-      f32x16 sacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = (f32x16){};
+  for (int qb = 0; qb < 2; ++qb) l_run[qb] += __shfl_xor(l_run[qb], 32);
+  constexpr int kSlotB = (2 * 2 * 16 + 2 * 2) * 256;  // O (2 qb x 2 db x 16) + m, l (2 qb x 2), per lane
+  auto slot = [&](int q_group, int s) { return reinterpret_cast<float*>(smem + (q_group * 2 + s) * kSlotB); };
+  auto put = [&](float* sl) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const f16x8 kf = load16(&Ks[buf][(32 * kb + l32) * kKld + 16 * s + 8 * g]);
-          sacc[kb] = mfma_32x32x16(kf, qf[s], sacc[kb]);
-        }
-      }
-      if (kt + kKeyTile > k_hi) {  // partial last tile: mask keys >= k_hi
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = kt + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-            if (key >= k_hi) sacc[kb][e] = -INFINITY;
-          }
-      }
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[kb][e]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = (m_run == -INFINITY) ? 0.0f : exp2_fast((m_run - m_new) * c_scale);
-      const float mc = (m_new == -INFINITY) ? 0.0f : m_new * c_scale;
-      m_run = m_new;
-      float lsum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = exp2_fast(fmaf(sacc[kb][e], c_scale, -mc));
-          sacc[kb][e] = p;
-          lsum += p;
-        }
-      l_run = l_run * alpha + lsum;
+    for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+        for (int e = 0; e < 16; ++e) sl[((qb * 2 + db) * 16 + e) * 64 + lane] = oacc[qb][db][e];
+      sl[(64 + qb * 2) * 64 + lane] = have_ref ? mref[qb] : -INFINITY;
+      sl[(64 + qb * 2 + 1) * 64 + lane] = l_run[qb];
+    }
+  };
+  auto take = [&](const float* sl) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mo = sl[(64 + qb * 2) * 64 + lane], lo = sl[(64 + qb * 2 + 1) * 64 + lane];
+      const float mm = have_ref ? mref[qb] : -INFINITY;
+      const float M = fmaxf(mm, mo);
+      if (M == -INFINITY) continue;  // neither side saw a key
+      const float wa = have_ref ? exp2_fast((mm - M) * c_scale) : 0.0f;
+      const float wb = mo == -INFINITY ? 0.0f : exp2_fast((mo - M) * c_scale);
+      l_run[qb] = l_run[qb] * wa + lo * wb;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          oacc[qb][db][e] = oacc[qb][db][e] * wa + sl[((qb * 2 + db) * 16 + e) * 64 + lane] * wb;
+      mref[qb] = M;
+    }
+    have_ref = true;
+  };
+  if (quarter >= 2) put(slot(qg, quarter - 2));
+  __syncthreads();
+  if (quarter < 2) take(slot(qg, quarter));
+  __syncthreads();
+  if (quarter == 1) put(slot(qg, 0));
+  __syncthreads();
+  if (quarter != 0 || !wave_rows) return;
+  take(slot(qg, 0));
 
-      // O^T += V^T P^T over four 16-key steps sigma = (kb, hb).
 #pragma unroll
-      for (int sg = 0; sg < 4; ++sg) {
-        const int kb = sg >> 1, hb = sg & 1;
-        const f16x8 pf = pack8(sacc[kb][8 * hb + 0], sacc[kb][8 * hb + 1], sacc[kb][8 * hb + 2],
-                               sacc[kb][8 * hb + 3], sacc[kb][8 * hb + 4], sacc[kb][8 * hb + 5],
-                               sacc[kb][8 * hb + 6], sacc[kb][8 * hb + 7]);
-        const int base = 32 * kb + 16 * hb + 4 * g;
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q = wq0 + 32 * qb + l32;
+    if (q >= seg_end) continue;
+    const float inv = l_run[qb] > 0.0f ? 1.0f / l_run[qb] : 0.0f;
+    f16* orow = O + (win_row0 + q) * kDModel + head * kHeadDim;
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const f16* vrow = &Vts[buf][(32 * db + l32) * kVld];
-          const f16x4 v_lo = *reinterpret_cast<const f16x4*>(vrow + base);
-          const f16x4 v_hi = *reinterpret_cast<const f16x4*>(vrow + base + 8);
-          const f16x8 vf = {v_lo[0], v_lo[1], v_lo[2], v_lo[3], v_hi[0], v_hi[1], v_hi[2], v_hi[3]};
-          oacc[db] = mfma_32x32x16(vf, pf, oacc[db]);
-        }
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f16x2 lo = pack_rne(oacc[qb][db][4 * i + 0] * inv, oacc[qb][db][4 * i + 1] * inv);
+        const f16x2 hi = pack_rne(oacc[qb][db][4 * i + 2] * inv, oacc[qb][db][4 * i + 3] * inv);
+        *reinterpret_cast<f16x4*>(orow + 32 * db + 8 * i + 4 * g) = (f16x4){lo[0], lo[1], hi[0], hi[1]};
       }
-    }
-    if (it + 1 < n_tiles) sstore(buf ^ 1);
-    __syncthreads();
   }
-
-  if (!row_ok) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f16x2 lo = pack_rne(oacc[db][4 * i + 0] * inv, oacc[db][4 * i + 1] * inv);
-      const f16x2 hi = pack_rne(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
-      *reinterpret_cast<f16x4*>(out_row + 32 * db + 8 * i + 4 * g) = (f16x4){lo[0], lo[1], hi[0], hi[1]};
-    }
 }
 
 }  // namespace
 
 hipError_t launch_flash_attn(const void* qkv, void* O, int batch, int seq_len, int chunk_len,
                              const int32_t* valid_host, hipStream_t stream) {
-  constexpr int NW = 4;
-  constexpr int BM = 32 * NW;
   const int seg_len_max = chunk_len > 0 ? chunk_len : seq_len;
   const int n_segs = (seq_len + seg_len_max - 1) / seg_len_max;
-  const int tiles_per_seg = (seg_len_max + BM - 1) / BM;
+  const int tiles_per_seg = (seg_len_max + kBMq - 1) / kBMq;
   for (int w0 = 0; w0 < batch; w0 += kMaxBatchPerLaunch) {
     const int nb = min(kMaxBatchPerLaunch, batch - w0);
     ValidLens vl;
     for (int b = 0; b < nb; ++b) vl.v[b] = valid_host ? valid_host[w0 + b] : seq_len;
     for (int b = nb; b < kMaxBatchPerLaunch; ++b) vl.v[b] = 0;
-    dim3 grid(nb * n_segs * tiles_per_seg, kHeads);
-    hipLaunchKernelGGL((flash_attn_kernel<NW>), grid, dim3(NW * kWave), 0, stream,
+    dim3 grid(nb * n_segs * tiles_per_seg * kHeads);
+    hipLaunchKernelGGL(flash_attn_kernel, grid, dim3(kThreads), 0, stream,
                        static_cast<const f16*>(qkv), static_cast<f16*>(O), seq_len, seg_len_max,
                        n_segs, tiles_per_seg, w0, vl);
     hipError_t e = hipGetLastError();

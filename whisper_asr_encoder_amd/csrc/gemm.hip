@@ -2,28 +2,70 @@
 // projection (N = 3840) and the attention output projection (N = 1280).
 //
 // C[M, N] = A[M, K] * Bt[N, K]^T + bias[N].  A (activations) and Bt (weights in
-// output-feature-major "Linear" layout) are both K-contiguous, so a 16-byte
-// LDS read yields one MFMA operand fragment with no transpose.  The MFMA
-// computes C^T tiles (weights as the A operand): each lane then owns four
-// consecutive output columns of one row, stored as one 8-byte write with the
-// bias added in fp32 and a single round-to-nearest-even to fp16.
+// output-feature-major "Linear" layout) are both K-contiguous, so a 16-byte LDS
+// read yields one MFMA operand fragment with no transpose.  The MFMA computes
+// C^T tiles (weights as the A operand); fp32 accumulation, bias added in fp32,
+// one round-to-nearest-even to fp16.
 //
-// Tiling: BM x BN workgroup tile, BK = 64, 256 threads = WM x WN waves, each
-// wave a (BM/WM) x (BN/WN) tile of 32x32x16 MFMAs.  Global->register prefetch
-// of tile k+1 overlaps the MFMAs of tile k; LDS is double-buffered with one
-// barrier per K step.  Rows are padded by 16 bytes (stride 144 B) so the
-// 32-row fragment reads spread over all banks.
+// Data movement (one workgroup of 4 waves per BM x BN tile, K step BK = 64):
+//  * global -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4) into a ring of
+//    STAGES tiles; STAGES tiles are in flight before the first MFMA and the stage
+//    of tile k is refilled with tile k+STAGES as soon as every wave has read it.
+//    A DMA instruction writes 1 KB = 8 rows of 128 bytes contiguously, so rows are
+//    not padded; instead the eight 16-byte chunks of row r are XOR-permuted with
+//    (r >> 1) & 7, which keeps the 16 rows of a fragment read on distinct banks.
+//    The DMA is issued from inline asm and waited for with explicit vmcnt counts,
+//    so the compiler's own LDS wait tracking stays exact.
+//  * LDS -> registers: the fragments of k16 step s+1 are read while the MFMAs of
+//    step s run (one read slotted after each MFMA), double-buffered in VGPRs.
+//  * epilogue: accumulators (+ bias, fp16) are staged through LDS and written back
+//    as full rows with 16-byte stores, instead of 8-byte pieces of 32 rows.
+// Workgroups are mapped to tiles XCD-aware: workgroup w runs on XCD w % 8, and each
+// XCD gets a contiguous range of tiles ordered N-tile-major, so an XCD's L2 serves
+// its weight slices to all M tiles.  Rows of A beyond M are fetched from row M-1
+// (valid memory) and never stored.
+#include <type_traits>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace edda {
 namespace {
 
-constexpr int kBK = 64;
-constexpr int kLdk = kBK + 8;  // halves per padded LDS row
+constexpr int kBK = 64;             // K elements per tile
+constexpr int kRowBytes = kBK * 2;  // 128 bytes per tile row
+constexpr int kKSteps = kBK / 16;   // 16-deep MFMA steps per tile
 constexpr int kGemmThreads = 256;
+constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 
-template <int BM, int BN, int WM, int WN>
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct-to-LDS DMA of 16 bytes per lane: lane i's bytes land at LDS byte address
+// lds_addr + 16 i (lds_addr wave-uniform, passed in M0).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(g), "s"(lds_addr) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
+// Wait until at most n DMA instructions of this wave are outstanding, then join the
+// workgroup barrier.  One asm statement with a memory clobber, so no LDS access
+// moves across it.  No memory fence: a fence would drain every in-flight DMA.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(n) : "memory");
+}
+
+// Compiler-visible wait for every outstanding LDS read of this wave.
+__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+template <int BM, int BN, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __restrict__ A,
                                                                  const f16* __restrict__ Bt,
                                                                  const f16* __restrict__ bias,
@@ -33,53 +75,60 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32-aligned");
-  constexpr int kChunksPerRow = kBK / 8;
-  constexpr int AC = BM * kChunksPerRow / kGemmThreads;
-  constexpr int BC = BN * kChunksPerRow / kGemmThreads;
-  static_assert(AC * kGemmThreads == BM * kChunksPerRow && BC * kGemmThreads == BN * kChunksPerRow,
-                "tile must split evenly over the threads");
+  constexpr int kWaves = kGemmThreads / kWave;
+  static_assert((BM / 8) % kWaves == 0 && (BN / 8) % kWaves == 0, "DMA groups must split evenly");
+  constexpr int AGW = BM / 8 / kWaves, BGW = BN / 8 / kWaves;
+  constexpr int IPW = AGW + BGW;  // DMA instructions per wave per tile
+  constexpr int kStageBytes = (BM + BN) * kRowBytes;
+  constexpr int kCld = BN + 8;    // epilogue tile row stride (halves)
+  static_assert(BM * kCld * 2 <= STAGES * kStageBytes, "epilogue tile must fit in the ring");
+  static_assert(STAGES >= 2, "need at least two stages");
 
-  __shared__ __attribute__((aligned(16))) f16 As[2][BM * kLdk];
-  __shared__ __attribute__((aligned(16))) f16 Bs[2][BN * kLdk];
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, g = lane >> 5;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
 
-  f16x8 ra[AC], rb[BC];
-  const f16x8 zero8 = {};
+  const int mt = (M + BM - 1) / BM;
+  const int nwg = gridDim.x, wid = blockIdx.x;
+  const int xcd = wid % kXcds, per = nwg / kXcds, rem = nwg % kXcds;
+  const int tile = xcd * per + min(xcd, rem) + wid / kXcds;
+  const int m0 = (tile % mt) * BM;
+  const int n0 = (tile / mt) * BN;
+  const int nk = K / kBK;
 
-  auto gload = [&](int k0) {
+  // DMA sources: lane i of an 8-row group fetches row group*8 + i/8, physical chunk i%8,
+  // i.e. logical chunk (i%8) ^ swz(row).
+  const int dr = lane >> 3, dpc = lane & 7;
+  const f16* a_src[AGW];
+  const f16* b_src[BGW];
 #pragma unroll
-    for (int c = 0; c < AC; ++c) {
-      const int idx = tid + kGemmThreads * c;
-      const int row = idx / kChunksPerRow, kc = idx % kChunksPerRow;
-      const int gm = m0 + row;
-      ra[c] = gm < M ? load16(A + (size_t)gm * K + k0 + kc * 8) : zero8;
-    }
+  for (int j = 0; j < AGW; ++j) {
+    const int row = (wave * AGW + j) * 8 + dr;
+    a_src[j] = A + (size_t)min(m0 + row, M - 1) * K + (dpc ^ swz(row)) * 8;
+  }
 #pragma unroll
-    for (int c = 0; c < BC; ++c) {
-      const int idx = tid + kGemmThreads * c;
-      const int row = idx / kChunksPerRow, kc = idx % kChunksPerRow;
-      rb[c] = load16(Bt + (size_t)(n0 + row) * K + k0 + kc * 8);
-    }
+  for (int j = 0; j < BGW; ++j) {
+    const int row = (wave * BGW + j) * 8 + dr;
+    b_src[j] = Bt + (size_t)(n0 + row) * K + (dpc ^ swz(row)) * 8;
+  }
+  const uint32_t smem_addr = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  auto issue = [&](int kt) {
+    const uint32_t st = smem_addr + (kt % STAGES) * kStageBytes;
+    const int k0 = kt * kBK;
+#pragma unroll
+    for (int j = 0; j < AGW; ++j) dma16(a_src[j] + k0, st + (wave * AGW + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < BGW; ++j) dma16(b_src[j] + k0, st + BM * kRowBytes + (wave * BGW + j) * 1024);
   };
-  auto sstore = [&](int buf) {
+
+  // Fragment byte offsets inside a stage: row l32 (+ multiples of 32), chunk (2s+g) ^ swz(row).
+  int frag_off[kKSteps];
 #pragma unroll
-    for (int c = 0; c < AC; ++c) {
-      const int idx = tid + kGemmThreads * c;
-      store16(&As[buf][(idx / kChunksPerRow) * kLdk + (idx % kChunksPerRow) * 8], ra[c]);
-    }
-#pragma unroll
-    for (int c = 0; c < BC; ++c) {
-      const int idx = tid + kGemmThreads * c;
-      store16(&Bs[buf][(idx / kChunksPerRow) * kLdk + (idx % kChunksPerRow) * 8], rb[c]);
-    }
-  };
+  for (int s = 0; s < kKSteps; ++s) frag_off[s] = l32 * kRowBytes + (((2 * s + g) ^ swz(l32)) << 4);
 
   f32x16 acc[FN][FM];
 #pragma unroll
@@ -87,62 +136,123 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = (f32x16){};
 
-  const int nk = K / kBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
+  f16x8 fa[2][FM], fb[2][FN];
+  auto read_frags = [&](int kt, int s, auto set_c) {
+    constexpr int set = decltype(set_c)::value;
+    const char* sa = smem + (kt % STAGES) * kStageBytes + wm * WTM * kRowBytes;
+    const char* sb = smem + (kt % STAGES) * kStageBytes + BM * kRowBytes + wn * WTN * kRowBytes;
 #pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      f16x8 af[FM], bf[FN];
+    for (int fm = 0; fm < FM; ++fm)
+      fa[set][fm] = *reinterpret_cast<const f16x8*>(sa + fm * 32 * kRowBytes + frag_off[s]);
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        af[fm] = load16(&As[buf][(wm * WTM + 32 * fm + l32) * kLdk + 16 * s + 8 * g]);
+    for (int fn = 0; fn < FN; ++fn)
+      fb[set][fn] = *reinterpret_cast<const f16x8*>(sb + fn * 32 * kRowBytes + frag_off[s]);
+  };
+  auto mfmas = [&](auto set_c) {
+    constexpr int set = decltype(set_c)::value;
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        bf[fn] = load16(&Bs[buf][(wn * WTN + 32 * fn + l32) * kLdk + 16 * s + 8 * g]);
+    for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
+      for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma_32x32x16(fb[set][fn], fa[set][fm], acc[fn][fm]);
+  };
+  // Slot one LDS read after each MFMA (then the remaining MFMAs).
+  auto interleave = [&]() {
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma_32x32x16(bf[fn], af[fm], acc[fn][fm]);
+    for (int i = 0; i < FM + FN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
-  }
+#pragma unroll
+    for (int i = FM + FN; i < FM * FN; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  static_assert(kKSteps == 4, "the step schedule below assumes four k16 steps per tile");
 
-  // Epilogue: lane owns row m and columns n .. n+3 of each 32x32 block (C^T layout).
+  // Steps 0..2 of tile kt: read step s+1 while the MFMAs of step s run.
+  auto first_steps = [&](int kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(kt, 1, S1());
+    mfmas(S0());
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(kt, 2, S0());
+    mfmas(S1());
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(kt, 3, S1());
+    mfmas(S0());
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int m = m0 + wm * WTM + 32 * fm + l32;
-    if (m >= M) continue;
+  for (int p = 0; p < STAGES; ++p)
+    if (p < nk) issue(p);
+  if (nk > STAGES - 1) {
+    wait_vmcnt_barrier<IPW * (STAGES - 1)>();
+  } else {
+    wait_vmcnt_barrier<0>();
+  }
+  read_frags(0, 0, S0());
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    first_steps(kt);
+    // Tile kt is fully read once its last fragments are in registers: publish that,
+    // wait for tile kt+1 (tiles issued after it: min(STAGES-2, nk-2-kt)), refill the
+    // freed stage, and read step 0 of tile kt+1 during the last MFMAs of tile kt.
+    wait_lds_reads();
+    if (kt + STAGES - 1 < nk) {
+      wait_vmcnt_barrier<IPW * (STAGES - 2)>();
+    } else if (STAGES > 3 && kt + 2 < nk) {
+      wait_vmcnt_barrier<IPW>();
+    } else {
+      wait_vmcnt_barrier<0>();
+    }
+    if (kt + STAGES < nk) issue(kt + STAGES);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(kt + 1, 0, S0());
+    mfmas(S1());
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  first_steps(nk - 1);
+  mfmas(S1());
+
+  // Epilogue: bias, fp16, stage the tile in LDS, then coalesced 16-byte row stores.
+  wait_lds_reads();
+  __syncthreads();  // every wave is done reading the ring
+  f16* cs = reinterpret_cast<f16*>(smem);
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
+  for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + wn * WTN + 32 * fn + 8 * i + 4 * g;
-        float v0 = acc[fn][fm][4 * i + 0], v1 = acc[fn][fm][4 * i + 1];
-        float v2 = acc[fn][fm][4 * i + 2], v3 = acc[fn][fm][4 * i + 3];
-        if (bias) {
-          const f16x4 bb = *reinterpret_cast<const f16x4*>(bias + n);
-          v0 += (float)bb[0];
-          v1 += (float)bb[1];
-          v2 += (float)bb[2];
-          v3 += (float)bb[3];
-        }
-        const f16x2 lo = pack_rne(v0, v1), hi = pack_rne(v2, v3);
-        *reinterpret_cast<f16x4*>(C + (size_t)m * N + n) = (f16x4){lo[0], lo[1], hi[0], hi[1]};
+    for (int i = 0; i < 4; ++i) {
+      const int nl = wn * WTN + 32 * fn + 8 * i + 4 * g;  // tile-local column
+      const f16x4 bb = bias ? *reinterpret_cast<const f16x4*>(bias + n0 + nl) : (f16x4){};
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int ml = wm * WTM + 32 * fm + l32;
+        const f16x2 lo = pack_rne(acc[fn][fm][4 * i + 0] + (float)bb[0], acc[fn][fm][4 * i + 1] + (float)bb[1]);
+        const f16x2 hi = pack_rne(acc[fn][fm][4 * i + 2] + (float)bb[2], acc[fn][fm][4 * i + 3] + (float)bb[3]);
+        *reinterpret_cast<f16x4*>(cs + ml * kCld + nl) = (f16x4){lo[0], lo[1], hi[0], hi[1]};
       }
     }
   }
+  __syncthreads();
+  constexpr int kChunksPerRow = BN / 8;
+  constexpr int kChunks = BM * kChunksPerRow;
+#pragma unroll 4
+  for (int c = tid; c < kChunks; c += kGemmThreads) {
+    const int ml = c / kChunksPerRow, cc = c % kChunksPerRow;
+    const int m = m0 + ml;
+    if (m < M) store16(C + (size_t)m * N + n0 + cc * 8, load16(cs + ml * kCld + cc * 8));
+  }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int STAGES>
 hipError_t launch_tile(const void* A, const void* Bt, const void* bias, void* C, int M, int N, int K,
                        hipStream_t stream) {
-  dim3 grid(N / BN, (M + BM - 1) / BM);
-  hipLaunchKernelGGL((gemm_bias_kernel<BM, BN, WM, WN>), grid, dim3(kGemmThreads), 0, stream,
+  dim3 grid((N / BN) * ((M + BM - 1) / BM));
+  hipLaunchKernelGGL((gemm_bias_kernel<BM, BN, WM, WN, STAGES>), grid, dim3(kGemmThreads), 0, stream,
                      static_cast<const f16*>(A), static_cast<const f16*>(Bt),
                      static_cast<const f16*>(bias), static_cast<f16*>(C), M, N, K);
   return hipGetLastError();
@@ -152,10 +262,11 @@ hipError_t launch_tile(const void* A, const void* Bt, const void* bias, void* C,
 
 hipError_t launch_gemm_bias(const void* A, const void* Bt, const void* bias, void* C, int M, int N,
                             int K, hipStream_t stream) {
-  // Pick the tile whose grid best fills 256 compute units.
-  if (N % 128 == 0 && (long)((M + 127) / 128) * (N / 128) >= 200)
-    return launch_tile<128, 128, 2, 2>(A, Bt, bias, C, M, N, K, stream);
-  return launch_tile<64, 64, 2, 2>(A, Bt, bias, C, M, N, K, stream);
+  if (N % 192 == 0 && (long)((M + 127) / 128) * (N / 192) >= 160)
+    return launch_tile<128, 192, 2, 2, 3>(A, Bt, bias, C, M, N, K, stream);
+  if (N % 128 == 0 && (long)((M + 127) / 128) * (N / 128) >= 160)
+    return launch_tile<128, 128, 2, 2, 4>(A, Bt, bias, C, M, N, K, stream);
+  return launch_tile<128, 64, 2, 2, 4>(A, Bt, bias, C, M, N, K, stream);
 }
 
 }  // namespace edda
