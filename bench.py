@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP16_TFLOPS = 2516.6    # MI355X dense fp16 MFMA: 256 CUs x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+COPY_BYTES = 256 << 20       # reference copy: reads and writes this many bytes
 D, H, DH, QKV = 1280, 20, 64, 3840
 
 
@@ -310,6 +311,9 @@ def main():
     ap.add_argument("--workload", default="window", choices=["small", "window", "chunked", "batched", "verify"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 256 MiB device-to-device copy (reference dispatch for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
@@ -321,6 +325,13 @@ def main():
         sys.exit(1)
     from whisper_asr_encoder_amd import _lib
     _lib.load()
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.workload == "verify":
         res = verify_bench(args, torch)
     else:

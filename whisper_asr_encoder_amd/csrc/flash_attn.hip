@@ -45,7 +45,7 @@ constexpr int kBMq = kQGroups * kQW;    // 128 query rows per workgroup
 constexpr int kIterKeys = kQuarters * kKT;
 constexpr int kWaves = kQGroups * kQuarters;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kStages = 4;
+constexpr int kStages = 4;  // tile i is live for four barrier slots (see the schedule below)
 constexpr int kRowB = kHeadDim * 2;     // 128 bytes per K/V row
 constexpr int kTileB = kKT * kRowB;     // 4 KB
 constexpr int kStageB = kQuarters * 2 * kTileB;  // K and V tiles of every quarter: 32 KB
@@ -185,92 +185,91 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) oacc[a][b] = (f32x16){};
-  bool have_ref = false;
+  f32x16 sacc[2];   // scores of the tile between its MFMA and softmax phases
+  f16x8 pf[2][2];   // fp16 P of the tile between its softmax and PV phases
 
-#pragma unroll
-  for (int p = 0; p < kStages - 1; ++p)
-    if (p < n_iter) issue(p);
+  auto k_tile = [&](int it) { return smem + (it % kStages) * kStageB + quarter * 2 * kTileB; };
 
-  for (int it = 0; it < n_iter; ++it) {
-    // Tiles issued after iteration it: min(kStages-2, n_iter-1-it).
-    if (it + 2 < n_iter) {
-      wait_vmcnt_barrier<IPW * 2>();
-    } else if (it + 1 < n_iter) {
-      wait_vmcnt_barrier<IPW>();
-    } else {
-      wait_vmcnt_barrier<0>();
-    }
-    if (it + kStages - 1 < n_iter) issue(it + kStages - 1);
-
-    const int kt0 = k_lo + it * kIterKeys + quarter * kKT;
-    if (!wave_rows || kt0 >= k_hi) continue;  // wave-uniform: nothing for this wave here
-    const char* ks = smem + (it % kStages) * kStageB + quarter * 2 * kTileB;
-    const char* vs = ks + kTileB;
-    const bool partial = kt0 + kKT > k_hi;
-
+  // S^T for tile it.  Only the last tile can extend past k_hi, so only it masks.
+  auto qk = [&](int it, bool last) {
+    const char* ks = k_tile(it);
     f16x8 kf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) kf[s] = *reinterpret_cast<const f16x8*>(ks + kfrag_off[s]);
-    f32x16 sacc[2];
-    auto scores = [&]() {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      sacc[qb] = (f32x16){};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sacc[qb] = mfma_32x32x16(kf[s], qf[qb][s], sacc[qb]);
+    }
+    if (last) {
+      // Admitted keys of this lane's tile rows: key index kt0 + 8(e>>2) + 4g + (e&3) < k_hi.
+      const int lim = k_hi - (k_lo + it * kIterKeys + quarter * kKT) - 4 * g;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (8 * (e >> 2) + (e & 3) >= lim) sacc[qb][e] = -INFINITY;
+    }
+  };
+  // O^T += V^T P^T for tile it.
+  auto pv = [&](int it) {
+    const char* vs = k_tile(it) + kTileB;
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const f16x4 lo = read_tr(vs + vtr_off[db][sg][0]);
+        const f16x4 hi = read_tr(vs + vtr_off[db][sg][1]);
+        const f16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) oacc[qb][db] = mfma_32x32x16(vf, pf[qb][sg], oacc[qb][db]);
+      }
+    }
+  };
+  // Row maximum of the current tile per query block (both lane halves agree).
+  auto tile_max = [&](int qb) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, sacc[qb][e]);
+    return fmaxf(m, __shfl_xor(m, 32));
+  };
+  float lt[2];
+  auto probabilities = [&]() {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(sacc[qb][8 * sg + e], c_scale, -mref_c[qb]));
+        const f16x2 a = pack_rne(p[0], p[1]), b = pack_rne(p[2], p[3]);
+        const f16x2 c = pack_rne(p[4], p[5]), d = pack_rne(p[6], p[7]);
+        const f16x2 one = {(f16)1.0f, (f16)1.0f};
+        acc = __builtin_amdgcn_fdot2(a, one, acc, false);
+        acc = __builtin_amdgcn_fdot2(b, one, acc, false);
+        acc = __builtin_amdgcn_fdot2(c, one, acc, false);
+        acc = __builtin_amdgcn_fdot2(d, one, acc, false);
+        pf[qb][sg] = (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+      }
+      lt[qb] = acc;
+    }
+  };
+  // Softmax of the tile in sacc.  The first tile of a wave sets the reference (a fully
+  // masked first tile leaves it at -inf with P = 0; all later tiles are masked too).
+  // Later tiles keep it unless their P sum shows scores well above it: then the tile is
+  // redone against the new maximum and the running sums are rescaled.
+  auto softmax = [&](bool first) {
+    if (first) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        sacc[qb] = (f32x16){};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) sacc[qb] = mfma_32x32x16(kf[s], qf[qb][s], sacc[qb]);
+        mref[qb] = tile_max(qb);
+        mref_c[qb] = mref[qb] == -INFINITY ? 0.0f : mref[qb] * c_scale;
       }
-      if (partial) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (kt0 + 8 * (e >> 2) + 4 * g + (e & 3) >= k_hi) sacc[qb][e] = -INFINITY;
-      }
-    };
-    // Row maximum of this tile per query block (both lane halves agree).
-    auto tile_max = [&](int qb) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) m = fmaxf(m, sacc[qb][e]);
-      return fmaxf(m, __shfl_xor(m, 32));
-    };
-    f16x8 pf[2][2];
-    float lt[2];
-    auto probabilities = [&]() {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float p[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) p[e] = exp2_fast(fmaf(sacc[qb][e], c_scale, -mref_c[qb]));
-        float acc = 0.0f;
-#pragma unroll
-        for (int sg = 0; sg < 2; ++sg) {
-          const f16x2 a = pack_rne(p[8 * sg + 0], p[8 * sg + 1]), b = pack_rne(p[8 * sg + 2], p[8 * sg + 3]);
-          const f16x2 c = pack_rne(p[8 * sg + 4], p[8 * sg + 5]), d = pack_rne(p[8 * sg + 6], p[8 * sg + 7]);
-          const f16x2 one = {(f16)1.0f, (f16)1.0f};
-          acc = __builtin_amdgcn_fdot2(a, one, acc, false);
-          acc = __builtin_amdgcn_fdot2(b, one, acc, false);
-          acc = __builtin_amdgcn_fdot2(c, one, acc, false);
-          acc = __builtin_amdgcn_fdot2(d, one, acc, false);
-          pf[qb][sg] = (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-        }
-        lt[qb] = acc;
-      }
-    };
-
-    scores();
-    if (!have_ref) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        mref[qb] = tile_max(qb);  // finite: key kt0 < k_hi is admitted for every row
-        mref_c[qb] = mref[qb] * c_scale;
-      }
-      have_ref = true;
     }
     probabilities();
-    // A tile sum this large means scores rose well above the reference: re-reference.
-    if (__builtin_amdgcn_ballot_w64(lt[0] >= kRedoSum || lt[1] >= kRedoSum) != 0) {
-      scores();
+    if (!first && __builtin_amdgcn_ballot_w64(lt[0] >= kRedoSum || lt[1] >= kRedoSum) != 0) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const float m_new = fmaxf(mref[qb], tile_max(qb));
@@ -287,19 +286,76 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
     }
     l_run[0] += lt[0];
     l_run[1] += lt[1];
+  };
 
-    // O^T += V^T P^T over two 16-key steps.
-#pragma unroll
-    for (int sg = 0; sg < 2; ++sg) {
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const f16x4 lo = read_tr(vs + vtr_off[db][sg][0]);
-        const f16x4 hi = read_tr(vs + vtr_off[db][sg][1]);
-        const f16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) oacc[qb][db] = mfma_32x32x16(vf, pf[qb][sg], oacc[qb][db]);
+  // Ping-pong schedule over barrier slots b = 0 .. 2 n_iter + 1 (slot b lies between
+  // barrier b and the next one).  Query group 0 runs the MFMA phase of iteration i
+  // (PV of tile i-1, QK of tile i) in slot 2i and the softmax of tile i in slot 2i+1;
+  // query group 1 runs one slot later, so on every SIMD one wave of each group alternates
+  // MFMA and VALU work against the other.  Both groups pass the same 2 n_iter + 2
+  // barriers.  Tile i's stage is live from slot 2i to slot 2i+3; tile j is issued right
+  // after barrier 2j-4 (two tiles ahead) and waited for before barrier 2j.  The first and
+  // last tiles are peeled so the steady-state body has no conditions.
+  auto even_barrier = [&](int j) {  // barrier 2j
+    if (j < n_iter) {
+      if (j + 1 < n_iter) {
+        wait_vmcnt_barrier<IPW>();
+      } else {
+        wait_vmcnt_barrier<0>();
       }
+      if (j + 2 < n_iter) issue(j + 2);
+    } else {
+      wait_vmcnt_barrier<0>();
     }
+  };
+  auto odd_barrier = [&]() { wait_vmcnt_barrier<0>(); };
+  const int nl = n_iter - 1;  // last tile
+  issue(0);
+  if (n_iter > 1) issue(1);
+  if (qg == 0) {
+    even_barrier(0);
+    qk(0, nl == 0);
+    odd_barrier();
+    softmax(true);
+    for (int i = 1; i < nl; ++i) {
+      even_barrier(i);
+      pv(i - 1);
+      qk(i, false);
+      odd_barrier();
+      softmax(false);
+    }
+    if (nl > 0) {
+      even_barrier(nl);
+      pv(nl - 1);
+      qk(nl, true);
+      odd_barrier();
+      softmax(false);
+    }
+    even_barrier(n_iter);
+    pv(nl);
+    odd_barrier();
+  } else {
+    even_barrier(0);
+    odd_barrier();
+    qk(0, nl == 0);
+    even_barrier(1);
+    softmax(true);
+    for (int i = 1; i < nl; ++i) {
+      odd_barrier();
+      pv(i - 1);
+      qk(i, false);
+      even_barrier(i + 1);
+      softmax(false);
+    }
+    if (nl > 0) {
+      odd_barrier();
+      pv(nl - 1);
+      qk(nl, true);
+      even_barrier(nl + 1);
+      softmax(false);
+    }
+    odd_barrier();
+    pv(nl);
   }
 
   // Merge the four key quarters of each query group through LDS (the ring is free:
@@ -316,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sl[((qb * 2 + db) * 16 + e) * 64 + lane] = oacc[qb][db][e];
-      sl[(64 + qb * 2) * 64 + lane] = have_ref ? mref[qb] : -INFINITY;
+      sl[(64 + qb * 2) * 64 + lane] = mref[qb];
       sl[(64 + qb * 2 + 1) * 64 + lane] = l_run[qb];
     }
   };
@@ -324,10 +380,10 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float mo = sl[(64 + qb * 2) * 64 + lane], lo = sl[(64 + qb * 2 + 1) * 64 + lane];
-      const float mm = have_ref ? mref[qb] : -INFINITY;
+      const float mm = mref[qb];
       const float M = fmaxf(mm, mo);
       if (M == -INFINITY) continue;  // neither side saw a key
-      const float wa = have_ref ? exp2_fast((mm - M) * c_scale) : 0.0f;
+      const float wa = mm == -INFINITY ? 0.0f : exp2_fast((mm - M) * c_scale);
       const float wb = mo == -INFINITY ? 0.0f : exp2_fast((mo - M) * c_scale);
       l_run[qb] = l_run[qb] * wa + lo * wb;
 #pragma unroll
@@ -337,7 +393,6 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
           oacc[qb][db][e] = oacc[qb][db][e] * wa + sl[((qb * 2 + db) * 16 + e) * 64 + lane] * wb;
       mref[qb] = M;
     }
-    have_ref = true;
   };
   if (quarter >= 2) put(slot(qg, quarter - 2));
   __syncthreads();

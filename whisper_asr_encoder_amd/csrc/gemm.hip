@@ -21,8 +21,8 @@
 //  * epilogue: accumulators (+ bias, fp16) are staged through LDS and written back
 //    as full rows with 16-byte stores, instead of 8-byte pieces of 32 rows.
 // Workgroups are mapped to tiles XCD-aware: workgroup w runs on XCD w % 8, and each
-// XCD gets a contiguous range of tiles ordered N-tile-major, so an XCD's L2 serves
-// its weight slices to all M tiles.  Rows of A beyond M are fetched from row M-1
+// XCD gets one rectangular region of the output (the 8 regions chosen to minimise the
+// A and B bytes the eight L2s fetch), so operands are fetched once per region.  Rows of A beyond M are fetched from row M-1
 // (valid memory) and never stored.
 #include <type_traits>
 
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
                                                                  const f16* __restrict__ Bt,
                                                                  const f16* __restrict__ bias,
                                                                  f16* __restrict__ C, int M, int N,
-                                                                 int K) {
+                                                                 int K, int reg_m, int reg_n) {
   static_assert(WM * WN * kWave == kGemmThreads, "wave grid must use 256 threads");
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -92,12 +92,29 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, g = lane >> 5;
 
-  const int mt = (M + BM - 1) / BM;
+  const int mt = (M + BM - 1) / BM, nt = N / BN;
   const int nwg = gridDim.x, wid = blockIdx.x;
   const int xcd = wid % kXcds, per = nwg / kXcds, rem = nwg % kXcds;
-  const int tile = xcd * per + min(xcd, rem) + wid / kXcds;
-  const int m0 = (tile % mt) * BM;
-  const int n0 = (tile / mt) * BN;
+  // Logical tile index t: the workgroups of one XCD take a contiguous range of t.
+  int t = xcd * per + min(xcd, rem) + wid / kXcds;
+  // t enumerates tiles region by region: the output is cut into reg_m x reg_n regions
+  // (reg_m * reg_n = 8), region r = i * reg_n + j covering M-tile band i and N-tile band
+  // j, M-tile fastest inside a region.  An XCD then fetches only its band of A and of B.
+  int mi = 0, ni = 0;
+  for (int r = 0; r < reg_m * reg_n; ++r) {
+    const int i = r / reg_n, j = r % reg_n;
+    const int mlo = mt * i / reg_m, mhi = mt * (i + 1) / reg_m;
+    const int nlo = nt * j / reg_n, nhi = nt * (j + 1) / reg_n;
+    const int cnt = (mhi - mlo) * (nhi - nlo);
+    if (t < cnt) {
+      mi = mlo + t % (mhi - mlo);
+      ni = nlo + t / (mhi - mlo);
+      break;
+    }
+    t -= cnt;
+  }
+  const int m0 = mi * BM;
+  const int n0 = ni * BN;
   const int nk = K / kBK;
 
   // DMA sources: lane i of an 8-row group fetches row group*8 + i/8, physical chunk i%8,
@@ -251,10 +268,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
 template <int BM, int BN, int WM, int WN, int STAGES>
 hipError_t launch_tile(const void* A, const void* Bt, const void* bias, void* C, int M, int N, int K,
                        hipStream_t stream) {
-  dim3 grid((N / BN) * ((M + BM - 1) / BM));
+  const int mt = (M + BM - 1) / BM, nt = N / BN;
+  // XCD regions: reg_m x reg_n = 8 minimising the operand bytes fetched into the eight L2s,
+  // reg_n * |A| + reg_m * |B|  (proportional to reg_n * M + reg_m * N); bands must be non-empty.
+  int reg_m = 1, reg_n = 1;
+  long best = -1;
+  for (int a = 1; a <= kXcds; a *= 2) {
+    const int b = kXcds / a;
+    if (a > mt || b > nt) continue;
+    const long cost = (long)b * M + (long)a * N;
+    if (best < 0 || cost < best) best = cost, reg_m = a, reg_n = b;
+  }
+  dim3 grid(nt * mt);
   hipLaunchKernelGGL((gemm_bias_kernel<BM, BN, WM, WN, STAGES>), grid, dim3(kGemmThreads), 0, stream,
                      static_cast<const f16*>(A), static_cast<const f16*>(Bt),
-                     static_cast<const f16*>(bias), static_cast<f16*>(C), M, N, K);
+                     static_cast<const f16*>(bias), static_cast<f16*>(C), M, N, K, reg_m, reg_n);
   return hipGetLastError();
 }
 
