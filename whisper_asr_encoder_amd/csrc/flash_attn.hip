@@ -18,12 +18,15 @@
 //   S^T = K Q^T   K fragments from LDS, Q^T fragments resident in registers; lane l
 //                 holds 16 scores of query l % 32 (per query block), so row
 //                 statistics need per-lane work plus one exchange with lane l ^ 32.
+//                 Q is held pre-scaled by log2(e)/8 and the MFMA accumulator starts
+//                 at -m, so the MFMA itself yields the exponent S log2(e)/8 - m.
 //   P = 2^(S log2(e)/8 - m)  with m a per-row reference: the row maximum of the
 //                 wave's first tile.  Later tiles reuse it; when a tile's sum of P
 //                 reaches 2^14 (a P value might approach the fp16 range) the tile
 //                 is recomputed against the new maximum and the running sums are
 //                 rescaled, so the result is exact softmax either way.
-//   l += sum P    with v_dot2_f32_f16 over the packed fp16 P that the PV MFMA uses.
+//   l += sum P    in fp32 adds (v_dot2 shares the matrix pipeline, so it would
+//                 serialise against the other query group's MFMAs).
 //   O^T += V^T P^T  fp16 P is already laid out as the B operand (the MFMA's k index
 //                 is permuted identically on both operands); V^T fragments are read
 //                 with ds_read_b64_tr_b16 from the row-major V tile.
@@ -52,6 +55,7 @@ constexpr int kStageB = kQuarters * 2 * kTileB;  // K and V tiles of every quart
 constexpr int kXcds = 8;
 constexpr int kMaxBatchPerLaunch = 256;
 constexpr float kRedoSum = 16384.0f;    // per-tile sum of P that triggers a re-reference
+constexpr float kQScale = 0.18033688011112042f;  // log2(e) / sqrt(64)
 
 struct ValidLens {
   int32_t v[kMaxBatchPerLaunch];
@@ -65,11 +69,29 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                ::"v"(g), "s"(lds_addr) : "memory", "m0");
 }
+// Wait for this wave's DMA down to n outstanding instructions, then the workgroup
+// barrier.  The scheduling barriers keep every instruction (arithmetic included) on its
+// side, so the work of a barrier slot stays in that slot.
 template <int n>
 __device__ __forceinline__ void wait_vmcnt_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(n) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// Workgroup barrier with no memory wait: orders LDS reads against later DMA writes only.
+__device__ __forceinline__ void plain_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// 16-byte chunk swizzle of a 128-byte row: h = (row >> 1) & 7 rotated right by one bit.
+// Rows 2m and 2m+1 fall in opposite bank halves, so K fragment reads (one row per lane)
+// need h bijective over 8 rows; transposed V reads touch rows 4m..4m+3 at once, so rows
+// 4m and 4m+2 must differ above bit 0 of the swizzle, which the rotation gives.
+__device__ __forceinline__ int swz(int row) {
+  const int h = (row >> 1) & 7;
+  return ((h & 1) << 2) | (h >> 1);
+}
 
 // Byte offset of element (row, col) in a swizzled 128-byte-row tile.
 __device__ __forceinline__ int tile_off(int row, int col) {
@@ -132,31 +154,24 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
     return;
   }
 
-  // Q^T fragments: lane holds Q[wq0 + 32 qb + l32][16 s + 8 g .. +7].
-  f16x8 qf[2][4];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q = wq0 + 32 * qb + l32;
-    const f16* qp = qkv_w + (size_t)q * kQkvCols + head * kHeadDim + 8 * g;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qf[qb][s] = q < seg_end ? load16(qp + 16 * s) : (f16x8){};
-  }
+  f16x8 qf[2][4];  // Q^T fragments, filled once the first tiles are in flight
 
   // DMA duties: wave (qg, quarter) loads quarter's K (qg 0) or V (qg 1) tile: 4 x 8 rows.
   const int n_iter = (k_hi - k_lo + kIterKeys - 1) / kIterKeys;
   const uint32_t smem_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
   const f16* dma_base = qkv_w + (qg == 0 ? kDModel : 2 * kDModel) + head * kHeadDim;
   const int drow = lane >> 3;  // row within an 8-row DMA group
-  auto issue = [&](int it) {
+  // One DMA instruction: rows 8j .. 8j+7 of this wave's share of tile it.
+  auto issue_part = [&](int it, int j) {
     const uint32_t st = smem_addr + (it % kStages) * kStageB + quarter * 2 * kTileB + qg * kTileB;
-    const int key0 = k_lo + it * kIterKeys + quarter * kKT;
+    const int row = 8 * j + drow;
+    const int key = min(k_lo + it * kIterKeys + quarter * kKT + row, k_hi - 1);  // past the interval: masked
+    const int lc = (lane & 7) ^ swz(row);
+    dma16(dma_base + (size_t)key * kQkvCols + 8 * lc, st + j * 1024);
+  };
+  auto issue = [&](int it) {
 #pragma unroll
-    for (int j = 0; j < kKT / 8; ++j) {
-      const int row = 8 * j + drow;
-      const int key = min(key0 + row, k_hi - 1);  // rows past the interval: any valid row (masked)
-      const int lc = (lane & 7) ^ swz(row);
-      dma16(dma_base + (size_t)key * kQkvCols + 8 * lc, st + j * 1024);
-    }
+    for (int j = 0; j < kKT / 8; ++j) issue_part(it, j);
   };
   constexpr int IPW = kKT / 8;
 
@@ -176,9 +191,10 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
         for (int h = 0; h < 2; ++h) vtr_off[db][sg][h] = tile_off(16 * sg + 8 * h + 4 * g + r, 32 * db + d0);
   }
 
-  const float c_scale = kLog2e / 8.0f;
-  float mref[2] = {-INFINITY, -INFINITY};  // raw-score reference per query block
-  float mref_c[2] = {0.0f, 0.0f};
+  // Per query block: reference m in scaled units (-inf until a key is seen) and the
+  // MFMA accumulator seed -m (0 while m is -inf).
+  float mref[2] = {-INFINITY, -INFINITY};
+  f32x16 cneg[2] = {(f32x16){}, (f32x16){}};
   float l_run[2] = {0.0f, 0.0f};
   f32x16 oacc[2][2];
 #pragma unroll
@@ -191,16 +207,21 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
   auto k_tile = [&](int it) { return smem + (it % kStages) * kStageB + quarter * 2 * kTileB; };
 
   // S^T for tile it.  Only the last tile can extend past k_hi, so only it masks.
-  auto qk = [&](int it, bool last) {
+  // dma >= 0: also issue the four DMA instructions of tile dma, one per MFMA pair, so
+  // the address unit never sees a burst (used when no PV phase precedes).
+  auto qk = [&](int it, bool last, int dma) {
     const char* ks = k_tile(it);
     f16x8 kf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) kf[s] = *reinterpret_cast<const f16x8*>(ks + kfrag_off[s]);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      sacc[qb] = (f32x16){};
+      sacc[qb] = mfma_32x32x16(kf[0], qf[qb][0], cneg[qb]);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) sacc[qb] = mfma_32x32x16(kf[s], qf[qb][s], sacc[qb]);
+      for (int s = 1; s < 4; ++s) {
+        sacc[qb] = mfma_32x32x16(kf[s], qf[qb][s], sacc[qb]);
+        if (dma >= 0 && (s & 1)) issue_part(dma, 2 * qb + (s >> 1));
+      }
     }
     if (last) {
       // Admitted keys of this lane's tile rows: key index kt0 + 8(e>>2) + 4g + (e&3) < k_hi.
@@ -212,8 +233,8 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
           if (8 * (e >> 2) + (e & 3) >= lim) sacc[qb][e] = -INFINITY;
     }
   };
-  // O^T += V^T P^T for tile it.
-  auto pv = [&](int it) {
+  // O^T += V^T P^T for tile it; dma >= 0: one DMA instruction of tile dma per MFMA pair.
+  auto pv = [&](int it, int dma) {
     const char* vs = k_tile(it) + kTileB;
 #pragma unroll
     for (int sg = 0; sg < 2; ++sg) {
@@ -224,6 +245,7 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
         const f16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) oacc[qb][db] = mfma_32x32x16(vf, pf[qb][sg], oacc[qb][db]);
+        if (dma >= 0) issue_part(dma, 2 * sg + db);
       }
     }
   };
@@ -238,22 +260,22 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
   auto probabilities = [&]() {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float acc = 0.0f;
+      float p[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p[e] = exp2_fast(sacc[qb][e]);
 #pragma unroll
       for (int sg = 0; sg < 2; ++sg) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(sacc[qb][8 * sg + e], c_scale, -mref_c[qb]));
-        const f16x2 a = pack_rne(p[0], p[1]), b = pack_rne(p[2], p[3]);
-        const f16x2 c = pack_rne(p[4], p[5]), d = pack_rne(p[6], p[7]);
-        const f16x2 one = {(f16)1.0f, (f16)1.0f};
-        acc = __builtin_amdgcn_fdot2(a, one, acc, false);
-        acc = __builtin_amdgcn_fdot2(b, one, acc, false);
-        acc = __builtin_amdgcn_fdot2(c, one, acc, false);
-        acc = __builtin_amdgcn_fdot2(d, one, acc, false);
+        const float* q = p + 8 * sg;
+        const f16x2 a = pack_rne(q[0], q[1]), b = pack_rne(q[2], q[3]);
+        const f16x2 c = pack_rne(q[4], q[5]), d = pack_rne(q[6], q[7]);
         pf[qb][sg] = (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
       }
-      lt[qb] = acc;
+      float t[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = p[e] + p[e + 8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] += t[e + 4];
+      lt[qb] = (t[0] + t[2]) + (t[1] + t[3]);
     }
   };
   // Softmax of the tile in sacc.  The first tile of a wave sets the reference (a fully
@@ -265,22 +287,31 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         mref[qb] = tile_max(qb);
-        mref_c[qb] = mref[qb] == -INFINITY ? 0.0f : mref[qb] * c_scale;
+        const float off = mref[qb] == -INFINITY ? 0.0f : mref[qb];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          sacc[qb][e] -= off;
+          cneg[qb][e] = -off;
+        }
       }
     }
     probabilities();
     if (!first && __builtin_amdgcn_ballot_w64(lt[0] >= kRedoSum || lt[1] >= kRedoSum) != 0) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const float m_new = fmaxf(mref[qb], tile_max(qb));
-        const float alpha = exp2_fast((mref[qb] - m_new) * c_scale);
+        const float d = fmaxf(tile_max(qb), 0.0f);  // excess of this tile over the reference
+        const float alpha = exp2_fast(-d);
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
           for (int e = 0; e < 16; ++e) oacc[qb][db][e] *= alpha;
-        mref[qb] = m_new;
-        mref_c[qb] = m_new * c_scale;
+        mref[qb] += d;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          sacc[qb][e] -= d;
+          cneg[qb][e] = -mref[qb];
+        }
       }
       probabilities();
     }
@@ -293,69 +324,102 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
   // (PV of tile i-1, QK of tile i) in slot 2i and the softmax of tile i in slot 2i+1;
   // query group 1 runs one slot later, so on every SIMD one wave of each group alternates
   // MFMA and VALU work against the other.  Both groups pass the same 2 n_iter + 2
-  // barriers.  Tile i's stage is live from slot 2i to slot 2i+3; tile j is issued right
-  // after barrier 2j-4 (two tiles ahead) and waited for before barrier 2j.  The first and
-  // last tiles are peeled so the steady-state body has no conditions.
-  auto even_barrier = [&](int j) {  // barrier 2j
-    if (j < n_iter) {
-      if (j + 1 < n_iter) {
-        wait_vmcnt_barrier<IPW>();
-      } else {
-        wait_vmcnt_barrier<0>();
-      }
-      if (j + 2 < n_iter) issue(j + 2);
+  // barriers.  Tile t's stage is read from slot 2t to slot 2t+3, so tile t+2 may be
+  // loaded from slot 2t on: each wave spreads its share of tile i+2 over its MFMA phase
+  // of iteration i (slot 2i or 2i+1) and waits for tile i before barrier 2i.  The odd
+  // barriers only order LDS reads and wait for no memory.  The first and last tiles are
+  // peeled so the steady-state body has no conditions.
+  auto even_barrier = [&](int j) {  // barrier 2j: tile j has landed in LDS
+    if (j + 1 < n_iter) {
+      wait_vmcnt_barrier<IPW>();
     } else {
       wait_vmcnt_barrier<0>();
     }
   };
-  auto odd_barrier = [&]() { wait_vmcnt_barrier<0>(); };
+  auto odd_barrier = [&]() { plain_barrier(); };
   const int nl = n_iter - 1;  // last tile
   issue(0);
   if (n_iter > 1) issue(1);
+
+  // Q^T fragments: lane holds Q[wq0 + 32 qb + l32][16 s + 8 g .. +7] scaled by log2(e)/8.
+  // Loaded after the first tiles' DMA so both latencies overlap; rows past the segment
+  // load its last row instead (finite values whose outputs are never stored).  The scale
+  // is applied as q c_hi + q c_lo with c_hi = fp16(c), so the product is rounded once.
+  {
+    const f16x8 chi = (f16x8)(f16)kQScale;
+    const f16x8 clo = (f16x8)(f16)(kQScale - (float)(f16)kQScale);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int q = min(wq0 + 32 * qb + l32, seg_end - 1);
+      const f16* qp = qkv_w + (size_t)q * kQkvCols + head * kHeadDim + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 v = load16(qp + 16 * s);
+        qf[qb][s] = __builtin_elementwise_fma(v, chi, v * clo);
+      }
+    }
+  }
+  const int dma0 = n_iter > 2 ? 2 : -1;
   if (qg == 0) {
     even_barrier(0);
-    qk(0, nl == 0);
+    qk(0, nl == 0, dma0);
     odd_barrier();
     softmax(true);
-    for (int i = 1; i < nl; ++i) {
+    int i = 1;
+    for (; i + 2 < n_iter; ++i) {
       even_barrier(i);
-      pv(i - 1);
-      qk(i, false);
+      pv(i - 1, i + 2);
+      qk(i, false, -1);
+      odd_barrier();
+      softmax(false);
+    }
+    if (i < nl) {
+      even_barrier(i);
+      pv(i - 1, -1);
+      qk(i, false, -1);
       odd_barrier();
       softmax(false);
     }
     if (nl > 0) {
       even_barrier(nl);
-      pv(nl - 1);
-      qk(nl, true);
+      pv(nl - 1, -1);
+      qk(nl, true, -1);
       odd_barrier();
       softmax(false);
     }
     even_barrier(n_iter);
-    pv(nl);
+    pv(nl, -1);
     odd_barrier();
   } else {
     even_barrier(0);
     odd_barrier();
-    qk(0, nl == 0);
+    qk(0, nl == 0, dma0);
     even_barrier(1);
     softmax(true);
-    for (int i = 1; i < nl; ++i) {
+    int i = 1;
+    for (; i + 2 < n_iter; ++i) {
       odd_barrier();
-      pv(i - 1);
-      qk(i, false);
+      pv(i - 1, i + 2);
+      qk(i, false, -1);
+      even_barrier(i + 1);
+      softmax(false);
+    }
+    if (i < nl) {
+      odd_barrier();
+      pv(i - 1, -1);
+      qk(i, false, -1);
       even_barrier(i + 1);
       softmax(false);
     }
     if (nl > 0) {
       odd_barrier();
-      pv(nl - 1);
-      qk(nl, true);
+      pv(nl - 1, -1);
+      qk(nl, true, -1);
       even_barrier(nl + 1);
       softmax(false);
     }
     odd_barrier();
-    pv(nl);
+    pv(nl, -1);
   }
 
   // Merge the four key quarters of each query group through LDS (the ring is free:
@@ -383,8 +447,8 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
       const float mm = mref[qb];
       const float M = fmaxf(mm, mo);
       if (M == -INFINITY) continue;  // neither side saw a key
-      const float wa = mm == -INFINITY ? 0.0f : exp2_fast((mm - M) * c_scale);
-      const float wb = mo == -INFINITY ? 0.0f : exp2_fast((mo - M) * c_scale);
+      const float wa = mm == -INFINITY ? 0.0f : exp2_fast(mm - M);
+      const float wb = mo == -INFINITY ? 0.0f : exp2_fast(mo - M);
       l_run[qb] = l_run[qb] * wa + lo * wb;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
