@@ -1,0 +1,136 @@
+"""Summaries of rocprofv3 output for the encoder kernels (host-side text processing).
+
+Reads the CSV files that `rocprofv3 --kernel-trace --stats` and two `rocprofv3 --pmc`
+passes (FETCH_SIZE, then WRITE_SIZE) write, and produces
+
+* per-kernel launch statistics (calls, mean / min / max duration),
+* HBM traffic per launch: the median counter value per dispatch (KiB) scaled by the
+  factor that makes the same counter read the true byte count of a plain device copy
+  of known size in the same run (bench.py --calibrate-copy issues that copy).
+
+    python -m whisper_asr_encoder_amd.profiling TRACE_DIR FETCH_DIR WRITE_DIR OUT_DIR \
+        --command "<the rocprofv3 command lines>"
+
+writes OUT_DIR/<kernel>_window.md for each kernel and OUT_DIR/traffic.json, keyed by the
+names bench.py reports (qkv_gemm, flash_attn, out_gemm), each with the digest of the
+kernel sources the counters were taken on.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
+
+# Kernel symbol fragment -> (report key, source files).  The window workload launches
+# the 128x192 GEMM variant for the QKV projection (N = 3840) and the 128x64 variant for
+# the output projection (N = 1280).
+KERNELS = {
+    "gemm_bias_kernelILi128ELi192E": ("qkv_gemm", ["gemm.hip"]),
+    "flash_attn_kernel": ("flash_attn", ["flash_attn.hip"]),
+    "gemm_bias_kernelILi128ELi64E": ("out_gemm", ["gemm.hip"]),
+}
+COPY_KERNEL = "copyBuffer"
+
+
+def source_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(HERE, "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _one(pattern):
+    files = sorted(glob.glob(pattern))
+    if not files:
+        raise FileNotFoundError(pattern)
+    return files[0]
+
+
+def kernel_stats(trace_dir):
+    out = {}
+    with open(_one(os.path.join(trace_dir, "*kernel_stats.csv"))) as f:
+        for row in csv.DictReader(f):
+            out[row["Name"]] = {"calls": int(row["Calls"]), "avg_ns": float(row["AverageNs"]),
+                                "min_ns": float(row["MinNs"]), "max_ns": float(row["MaxNs"])}
+    return out
+
+
+def counter_values(pmc_dir, counter):
+    vals = {}
+    with open(_one(os.path.join(pmc_dir, "*counter_collection.csv"))) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return vals
+
+
+def _match(values, fragment):
+    hits = [v for k, v in values.items() if fragment in k]
+    return [x for h in hits for x in h]
+
+
+def summarize(trace_dir, fetch_dir, write_dir, out_dir, command):
+    stats = kernel_stats(trace_dir)
+    fetch = counter_values(fetch_dir, "FETCH_SIZE")
+    write = counter_values(write_dir, "WRITE_SIZE")
+    copy_f, copy_w = _match(fetch, COPY_KERNEL), _match(write, COPY_KERNEL)
+    if not copy_f or not copy_w:
+        raise RuntimeError("no calibration copy dispatch in the counter runs (run bench.py --calibrate-copy)")
+    f_scale = COPY_BYTES / (max(copy_f) * 1024.0)
+    w_scale = COPY_BYTES / (max(copy_w) * 1024.0)
+    os.makedirs(out_dir, exist_ok=True)
+    traffic = {"_method": (f"median per-dispatch FETCH_SIZE x {f_scale:.3f} + WRITE_SIZE x {w_scale:.3f} "
+                           f"(KiB -> bytes; factors make a {COPY_BYTES >> 20} MiB device copy read its "
+                           "true size)")}
+    for frag, (key, srcs) in KERNELS.items():
+        st = [v for k, v in stats.items() if frag in k]
+        fv, wv = _match(fetch, frag), _match(write, frag)
+        if not st or not fv or not wv:
+            continue
+        s = st[0]
+        fb = statistics.median(fv) * 1024.0 * f_scale
+        wb = statistics.median(wv) * 1024.0 * w_scale
+        digest = source_digest(srcs)
+        traffic[key] = {"bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                        "source_digest": digest}
+        name = [k for k in stats if frag in k][0]
+        with open(os.path.join(out_dir, f"{key}_window.md"), "w") as f:
+            f.write(f"# {key}: one 30 s window (1500 frames), 32 attention sublayers\n\n")
+            f.write(f"Kernel symbol: `{name}`\n\n")
+            f.write("Commands (run from the repository root on one MI355X):\n\n```\n" + command.strip() + "\n```\n\n")
+            f.write("| figure | value |\n|---|---|\n")
+            f.write(f"| dispatches in the trace run | {s['calls']} |\n")
+            f.write(f"| mean duration | {s['avg_ns'] / 1e3:.2f} us |\n")
+            f.write(f"| min / max duration | {s['min_ns'] / 1e3:.2f} / {s['max_ns'] / 1e3:.2f} us |\n")
+            f.write(f"| FETCH_SIZE median per dispatch | {statistics.median(fv):.0f} KiB (x {f_scale:.3f}) |\n")
+            f.write(f"| WRITE_SIZE median per dispatch | {statistics.median(wv):.0f} KiB (x {w_scale:.3f}) |\n")
+            f.write(f"| HBM bytes per launch (scaled) | {(fb + wb) / 1e6:.2f} MB "
+                    f"(read {fb / 1e6:.2f}, write {wb / 1e6:.2f}) |\n")
+            f.write(f"| kernel sources digest | {digest} |\n")
+    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+        f.write("\n")
+    return traffic
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("trace_dir")
+    ap.add_argument("fetch_dir")
+    ap.add_argument("write_dir")
+    ap.add_argument("out_dir")
+    ap.add_argument("--command", required=True)
+    a = ap.parse_args()
+    print(json.dumps(summarize(a.trace_dir, a.fetch_dir, a.write_dir, a.out_dir, a.command), indent=1))
+
+
+if __name__ == "__main__":
+    main()
