@@ -10,7 +10,9 @@
 // Data movement (one workgroup of 4 waves per BM x BN tile, K step BK = 64):
 //  * global -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4) into a ring of
 //    STAGES tiles; STAGES tiles are in flight before the first MFMA and the stage
-//    of tile k is refilled with tile k+STAGES as soon as every wave has read it.
+//    of tile k is refilled with tile k+STAGES once every wave has read it: each wave
+//    spreads its DMA instructions for that tile over the k16 steps of tile k+1 (a
+//    burst of them right after the barrier would stall on the address unit).
 //    A DMA instruction writes 1 KB = 8 rows of 128 bytes contiguously, so rows are
 //    not padded; instead the eight 16-byte chunks of row r are XOR-permuted with
 //    (r >> 1) & 7, which keeps the 16 rows of a fragment read on distinct banks.
@@ -133,19 +135,42 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
     b_src[j] = Bt + (size_t)(n0 + row) * K + (dpc ^ swz(row)) * 8;
   }
   const uint32_t smem_addr = __builtin_amdgcn_readfirstlane(lds_address(smem));
-  auto issue = [&](int kt) {
+  // DMA instruction j (0 .. IPW-1) of this wave's share of tile kt.
+  auto issue_part = [&](int kt, int j) {
     const uint32_t st = smem_addr + (kt % STAGES) * kStageBytes;
     const int k0 = kt * kBK;
-#pragma unroll
-    for (int j = 0; j < AGW; ++j) dma16(a_src[j] + k0, st + (wave * AGW + j) * 1024);
-#pragma unroll
-    for (int j = 0; j < BGW; ++j) dma16(b_src[j] + k0, st + BM * kRowBytes + (wave * BGW + j) * 1024);
+    if (j < AGW) {
+      dma16(a_src[j] + k0, st + (wave * AGW + j) * 1024);
+    } else {
+      dma16(b_src[j - AGW] + k0, st + BM * kRowBytes + (wave * BGW + j - AGW) * 1024);
+    }
   };
+  auto issue = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) issue_part(kt, j);
+  };
+  // Parts [lo, hi) of tile dma (nothing when dma < 0).
+  auto issue_range = [&](int dma, int lo, int hi) {
+    if (dma >= 0) {
+#pragma unroll
+      for (int j = lo; j < hi; ++j) issue_part(dma, j);
+    }
+  };
+  constexpr int kPart1 = (IPW + 3) / 4, kPart2 = (IPW + 1) / 2, kPart3 = (3 * IPW + 3) / 4;
 
   // Fragment byte offsets inside a stage: row l32 (+ multiples of 32), chunk (2s+g) ^ swz(row).
   int frag_off[kKSteps];
 #pragma unroll
   for (int s = 0; s < kKSteps; ++s) frag_off[s] = l32 * kRowBytes + (((2 * s + g) ^ swz(l32)) << 4);
+
+  // Bias values of this lane's output columns, loaded now so the epilogue does not wait.
+  f16x4 bias_v[FN][4];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      bias_v[fn][i] = bias ? *reinterpret_cast<const f16x4*>(bias + n0 + wn * WTN + 32 * fn + 8 * i + 4 * g)
+                           : (f16x4){};
 
   f32x16 acc[FN][FM];
 #pragma unroll
@@ -186,21 +211,25 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
   using S1 = std::integral_constant<int, 1>;
   static_assert(kKSteps == 4, "the step schedule below assumes four k16 steps per tile");
 
-  // Steps 0..2 of tile kt: read step s+1 while the MFMAs of step s run.
-  auto first_steps = [&](int kt) {
+  // Steps 0..2 of tile kt: read step s+1 while the MFMAs of step s run; the DMA of
+  // tile dma is spread over the steps (the rest follows step 3).
+  auto first_steps = [&](int kt, int dma) {
     __builtin_amdgcn_sched_barrier(0);
     read_frags(kt, 1, S1());
     mfmas(S0());
     interleave();
     __builtin_amdgcn_sched_barrier(0);
+    issue_range(dma, 0, kPart1);
     read_frags(kt, 2, S0());
     mfmas(S1());
     interleave();
     __builtin_amdgcn_sched_barrier(0);
+    issue_range(dma, kPart1, kPart2);
     read_frags(kt, 3, S1());
     mfmas(S0());
     interleave();
     __builtin_amdgcn_sched_barrier(0);
+    issue_range(dma, kPart2, kPart3);
   };
 
 #pragma unroll
@@ -213,7 +242,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
   }
   read_frags(0, 0, S0());
   for (int kt = 0; kt + 1 < nk; ++kt) {
-    first_steps(kt);
+    // Tile kt refills the stage freed before it with tile kt + STAGES - 1.
+    const int dma = kt >= 1 && kt + STAGES - 1 < nk ? kt + STAGES - 1 : -1;
+    first_steps(kt, dma);
+    issue_range(dma, kPart3, IPW);
     // Tile kt is fully read once its last fragments are in registers: publish that,
     // wait for tile kt+1 (tiles issued after it: min(STAGES-2, nk-2-kt)), refill the
     // freed stage, and read step 0 of tile kt+1 during the last MFMAs of tile kt.
@@ -225,14 +257,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
     } else {
       wait_vmcnt_barrier<0>();
     }
-    if (kt + STAGES < nk) issue(kt + STAGES);
     __builtin_amdgcn_sched_barrier(0);
     read_frags(kt + 1, 0, S0());
     mfmas(S1());
     interleave();
     __builtin_amdgcn_sched_barrier(0);
   }
-  first_steps(nk - 1);
+  first_steps(nk - 1, -1);
   mfmas(S1());
 
   // Epilogue: bias, fp16, stage the tile in LDS, then coalesced 16-byte row stores.
@@ -244,7 +275,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int nl = wn * WTN + 32 * fn + 8 * i + 4 * g;  // tile-local column
-      const f16x4 bb = bias ? *reinterpret_cast<const f16x4*>(bias + n0 + nl) : (f16x4){};
+      const f16x4 bb = bias_v[fn][i];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const int ml = wm * WTM + 32 * fm + l32;
