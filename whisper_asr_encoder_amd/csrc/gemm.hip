@@ -67,12 +67,23 @@ __device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0x
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
+// Tile order, computed on the host.  Logical tile t (see the kernel) lies in region r
+// when first[r] <= t < first[r+1]; inside region r, M-tile mlo[r] + u % height[r] and
+// N-tile nlo[r] + u / height[r] with u = t - first[r], the quotient taken as
+// (u * inv[r]) >> 32 with inv[r] = ceil(2^32 / height[r]) (up to 2^32 for height 1;
+// exact for u, height < 2^16).
+struct TileMap {
+  int32_t first[kXcds + 1];
+  int32_t mlo[kXcds], nlo[kXcds], height[kXcds];
+  uint64_t inv[kXcds];
+};
+
 template <int BM, int BN, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __restrict__ A,
                                                                  const f16* __restrict__ Bt,
                                                                  const f16* __restrict__ bias,
                                                                  f16* __restrict__ C, int M, int N,
-                                                                 int K, int reg_m, int reg_n) {
+                                                                 int K, TileMap map) {
   static_assert(WM * WN * kWave == kGemmThreads, "wave grid must use 256 threads");
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -94,27 +105,25 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, g = lane >> 5;
 
-  const int mt = (M + BM - 1) / BM, nt = N / BN;
   const int nwg = gridDim.x, wid = blockIdx.x;
   const int xcd = wid % kXcds, per = nwg / kXcds, rem = nwg % kXcds;
   // Logical tile index t: the workgroups of one XCD take a contiguous range of t.
-  int t = xcd * per + min(xcd, rem) + wid / kXcds;
+  const int t = xcd * per + min(xcd, rem) + wid / kXcds;
   // t enumerates tiles region by region: the output is cut into reg_m x reg_n regions
-  // (reg_m * reg_n = 8), region r = i * reg_n + j covering M-tile band i and N-tile band
-  // j, M-tile fastest inside a region.  An XCD then fetches only its band of A and of B.
-  int mi = 0, ni = 0;
-  for (int r = 0; r < reg_m * reg_n; ++r) {
-    const int i = r / reg_n, j = r % reg_n;
-    const int mlo = mt * i / reg_m, mhi = mt * (i + 1) / reg_m;
-    const int nlo = nt * j / reg_n, nhi = nt * (j + 1) / reg_n;
-    const int cnt = (mhi - mlo) * (nhi - nlo);
-    if (t < cnt) {
-      mi = mlo + t % (mhi - mlo);
-      ni = nlo + t / (mhi - mlo);
-      break;
-    }
-    t -= cnt;
-  }
+  // (reg_m * reg_n = 8) of M-tile bands x N-tile bands, M-tile fastest inside a region,
+  // so an XCD fetches only its band of A and of B.
+  int r = 0;
+#pragma unroll
+  for (int i = 1; i < kXcds; ++i) r += t >= map.first[i];
+  int first = map.first[0], mlo = map.mlo[0], nlo = map.nlo[0], height = map.height[0];
+  uint64_t inv = map.inv[0];
+#pragma unroll
+  for (int i = 1; i < kXcds; ++i)
+    if (r == i) first = map.first[i], mlo = map.mlo[i], nlo = map.nlo[i], height = map.height[i], inv = map.inv[i];
+  const uint32_t u = (uint32_t)(t - first);
+  const int q = (int)(((uint64_t)u * inv) >> 32);  // u < 2^16, inv <= 2^32: no overflow
+  const int mi = mlo + (int)u - q * height;
+  const int ni = nlo + q;
   const int m0 = mi * BM;
   const int n0 = ni * BN;
   const int nk = K / kBK;
@@ -310,10 +319,29 @@ hipError_t launch_tile(const void* A, const void* Bt, const void* bias, void* C,
     const long cost = (long)b * M + (long)a * N;
     if (best < 0 || cost < best) best = cost, reg_m = a, reg_n = b;
   }
+  // Region r = i * reg_n + j covers M-tile band i and N-tile band j.  Regions beyond
+  // reg_m * reg_n (fewer than 8 when a band would be empty) get empty ranges.
+  TileMap map{};
+  int acc = 0;
+  for (int r = 0; r < kXcds; ++r) {
+    map.first[r] = acc;
+    if (r < reg_m * reg_n) {
+      const int i = r / reg_n, j = r % reg_n;
+      const int mlo = mt * i / reg_m, mhi = mt * (i + 1) / reg_m;
+      const int nlo = nt * j / reg_n, nhi = nt * (j + 1) / reg_n;
+      map.mlo[r] = mlo, map.nlo[r] = nlo, map.height[r] = mhi - mlo;
+      map.inv[r] = (((uint64_t)1 << 32) + (mhi - mlo) - 1) / (uint64_t)(mhi - mlo);
+      acc += (mhi - mlo) * (nhi - nlo);
+    } else {
+      map.mlo[r] = map.nlo[r] = 0, map.height[r] = 1, map.inv[r] = (uint64_t)1 << 32;
+    }
+  }
+  map.first[kXcds] = acc;
+  if ((long)mt * nt >= 65536) return hipErrorInvalidValue;  // the quotient trick needs u < 2^16
   dim3 grid(nt * mt);
   hipLaunchKernelGGL((gemm_bias_kernel<BM, BN, WM, WN, STAGES>), grid, dim3(kGemmThreads), 0, stream,
                      static_cast<const f16*>(A), static_cast<const f16*>(Bt),
-                     static_cast<const f16*>(bias), static_cast<f16*>(C), M, N, K, reg_m, reg_n);
+                     static_cast<const f16*>(bias), static_cast<f16*>(C), M, N, K, map);
   return hipGetLastError();
 }
 
