@@ -105,9 +105,18 @@ __device__ __forceinline__ f16x4 read_tr(const char* p) {
   return __builtin_bit_cast(f16x4, v);
 }
 
+// q = u / h, r = u % h for 0 <= u < 2^24, from rcp = 1/h (fp32, host-rounded): u and
+// u * rcp are within one unit of the quotient, which one correction step fixes.
+__device__ __forceinline__ void divmod_rcp(int u, int h, float rcp, int& q, int& r) {
+  q = (int)((float)u * rcp);
+  r = u - q * h;
+  if (r < 0) --q, r += h;
+  if (r >= h) ++q, r -= h;
+}
+
 __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
     const f16* __restrict__ qkv, f16* __restrict__ O, int seq_len, int seg_len_max, int n_segs,
-    int tiles_per_seg, int window0, ValidLens valid) {
+    int tiles_per_seg, float rcp_segs, float rcp_tiles, int window0, ValidLens valid) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageB];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -118,13 +127,11 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
   // XCD-aware decode: consecutive logical tiles (the query tiles of one head) share an XCD.
   const int nwg = gridDim.x, wid = blockIdx.x;
   const int xcd = wid % kXcds, per = nwg / kXcds, rem = nwg % kXcds;
-  int t = xcd * per + min(xcd, rem) + wid / kXcds;
-  const int qt = t % tiles_per_seg;
-  t /= tiles_per_seg;
-  const int head = t % kHeads;
-  t /= kHeads;
-  const int seg = t % n_segs;
-  const int wloc = t / n_segs;
+  const int t = xcd * per + min(xcd, rem) + wid / kXcds;
+  int t1, qt, seg, wloc;
+  divmod_rcp(t, tiles_per_seg, rcp_tiles, t1, qt);
+  const int t2 = t1 / kHeads, head = t1 - t2 * kHeads;
+  divmod_rcp(t2, n_segs, rcp_segs, wloc, seg);
   const int window = window0 + wloc;
 
   const int seg0 = seg * seg_len_max;
@@ -422,65 +429,74 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
     pv(nl, -1);
   }
 
-  // Merge the four key quarters of each query group through LDS (the ring is free:
-  // every DMA completed before the last iteration's barrier).
+  // Merge the four key quarters of each query group in one LDS round (the ring is free:
+  // every DMA completed before the last iteration's barrier).  Wave `quarter` of a group
+  // finalises output block (qb, db) = (quarter / 2, quarter % 2): it receives the other
+  // three waves' partial O^T of that block and their (m, l) of that query block.
   __syncthreads();
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) l_run[qb] += __shfl_xor(l_run[qb], 32);
-  constexpr int kSlotB = (2 * 2 * 16 + 2 * 2) * 256;  // O (2 qb x 2 db x 16) + m, l (2 qb x 2), per lane
-  auto slot = [&](int q_group, int s) { return reinterpret_cast<float*>(smem + (q_group * 2 + s) * kSlotB); };
-  auto put = [&](float* sl) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sl[((qb * 2 + db) * 16 + e) * 64 + lane] = oacc[qb][db][e];
-      sl[(64 + qb * 2) * 64 + lane] = mref[qb];
-      sl[(64 + qb * 2 + 1) * 64 + lane] = l_run[qb];
-    }
+  f32x4* const xo = reinterpret_cast<f32x4*>(smem);          // [group][owner][3 sources][4][64]
+  f32x4* const xml = xo + kQGroups * 4 * 3 * 4 * kWave;       // [group][source][64]: m0, l0, m1, l1
+  auto oslot = [&](int owner, int src) {
+    return xo + ((qg * 4 + owner) * 3 + (src > owner ? src - 1 : src)) * 4 * kWave;
   };
-  auto take = [&](const float* sl) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float mo = sl[(64 + qb * 2) * 64 + lane], lo = sl[(64 + qb * 2 + 1) * 64 + lane];
-      const float mm = mref[qb];
-      const float M = fmaxf(mm, mo);
-      if (M == -INFINITY) continue;  // neither side saw a key
-      const float wa = mm == -INFINITY ? 0.0f : exp2_fast(mm - M);
-      const float wb = mo == -INFINITY ? 0.0f : exp2_fast(mo - M);
-      l_run[qb] = l_run[qb] * wa + lo * wb;
+  for (int blk = 0; blk < 4; ++blk) {
+    if (blk == quarter) continue;
+    f32x4* sl = oslot(blk, quarter);
+    const f32x16& o = oacc[blk >> 1][blk & 1];
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+    for (int c = 0; c < 4; ++c) sl[c * kWave + lane] = (f32x4){o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
+  }
+  xml[(qg * 4 + quarter) * kWave + lane] = (f32x4){mref[0], l_run[0], mref[1], l_run[1]};
+  __syncthreads();
+  if (!wave_rows) return;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          oacc[qb][db][e] = oacc[qb][db][e] * wa + sl[((qb * 2 + db) * 16 + e) * 64 + lane] * wb;
-      mref[qb] = M;
+  for (int blk = 0; blk < 4; ++blk) {
+    if (blk != quarter) continue;
+    const int qb = blk >> 1, db = blk & 1;
+    f32x4 ml[4];
+    float M = mref[qb];
+#pragma unroll
+    for (int src = 0; src < 4; ++src) {
+      if (src == blk) continue;
+      ml[src] = xml[(qg * 4 + src) * kWave + lane];
+      M = fmaxf(M, ml[src][2 * qb]);
     }
-  };
-  if (quarter >= 2) put(slot(qg, quarter - 2));
-  __syncthreads();
-  if (quarter < 2) take(slot(qg, quarter));
-  __syncthreads();
-  if (quarter == 1) put(slot(qg, 0));
-  __syncthreads();
-  if (quarter != 0 || !wave_rows) return;
-  take(slot(qg, 0));
-
+    f32x16 o = oacc[qb][db];
+    float l = 0.0f;
+    if (M != -INFINITY) {  // some quarter saw a key of this row
+      const float w = mref[qb] == -INFINITY ? 0.0f : exp2_fast(mref[qb] - M);
+      l = l_run[qb] * w;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+      for (int e = 0; e < 16; ++e) o[e] *= w;
+#pragma unroll
+      for (int src = 0; src < 4; ++src) {
+        if (src == blk) continue;
+        const float ms = ml[src][2 * qb];
+        const float ws = ms == -INFINITY ? 0.0f : exp2_fast(ms - M);
+        l += ml[src][2 * qb + 1] * ws;
+        const f32x4* sl = oslot(blk, src);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x4 v = sl[c * kWave + lane];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) o[4 * c + k] += v[k] * ws;
+        }
+      }
+    }
     const int q = wq0 + 32 * qb + l32;
-    if (q >= seg_end) continue;
-    const float inv = l_run[qb] > 0.0f ? 1.0f / l_run[qb] : 0.0f;
-    f16* orow = O + (win_row0 + q) * kDModel + head * kHeadDim;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
+    if (q < seg_end) {
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      f16* orow = O + (win_row0 + q) * kDModel + head * kHeadDim;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f16x2 lo = pack_rne(oacc[qb][db][4 * i + 0] * inv, oacc[qb][db][4 * i + 1] * inv);
-        const f16x2 hi = pack_rne(oacc[qb][db][4 * i + 2] * inv, oacc[qb][db][4 * i + 3] * inv);
+        const f16x2 lo = pack_rne(o[4 * i + 0] * inv, o[4 * i + 1] * inv);
+        const f16x2 hi = pack_rne(o[4 * i + 2] * inv, o[4 * i + 3] * inv);
         *reinterpret_cast<f16x4*>(orow + 32 * db + 8 * i + 4 * g) = (f16x4){lo[0], lo[1], hi[0], hi[1]};
       }
+    }
   }
 }
 
@@ -496,10 +512,12 @@ hipError_t launch_flash_attn(const void* qkv, void* O, int batch, int seq_len, i
     ValidLens vl;
     for (int b = 0; b < nb; ++b) vl.v[b] = valid_host ? valid_host[w0 + b] : seq_len;
     for (int b = nb; b < kMaxBatchPerLaunch; ++b) vl.v[b] = 0;
-    dim3 grid(nb * n_segs * tiles_per_seg * kHeads);
+    const long nwg = (long)nb * n_segs * tiles_per_seg * kHeads;
+    if (nwg >= (1L << 24)) return hipErrorInvalidValue;  // the decode's division range
+    dim3 grid((unsigned)nwg);
     hipLaunchKernelGGL(flash_attn_kernel, grid, dim3(kThreads), 0, stream,
                        static_cast<const f16*>(qkv), static_cast<f16*>(O), seq_len, seg_len_max,
-                       n_segs, tiles_per_seg, w0, vl);
+                       n_segs, tiles_per_seg, 1.0f / (float)n_segs, 1.0f / (float)tiles_per_seg, w0, vl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
