@@ -49,6 +49,8 @@ extern "C" {
 #define EDDA_HEAD_DIM 64
 #define EDDA_QKV_COLS (3 * EDDA_D_MODEL)
 #define EDDA_MAX_VERIFY_QUERIES 16
+/* Leading bytes of the verification workspace that hold its arrival counters. */
+#define EDDA_VERIFY_COUNTER_BYTES 5120
 
 typedef enum {
   EDDA_OK = 0,
@@ -140,7 +142,13 @@ size_t edda_encoder_workspace_bytes(int32_t batch, int32_t seq_len);
  *  o          [n_q, 20, 64] fp16 output: o[t,h] = softmax_j(q[t,h].k[j,h]/8) v[j,h]
  *             over the admitted slots j.
  *  workspace  device scratch of at least edda_verify_workspace_bytes(n_q, n_kv)
- *             bytes (split-KV partial results; may be 0 bytes when that returns 0).
+ *             bytes (may be NULL / 0 bytes when that returns 0). It holds per-head
+ *             arrival counters in its first EDDA_VERIFY_COUNTER_BYTES bytes, then the
+ *             fp32 partial results of the key splits. The counter bytes must be zero
+ *             before the first call that uses the workspace (e.g. one hipMemset after
+ *             allocating it);
+ *             every call leaves them zero again, so captured graphs may replay it.
+ *             Calls that share a workspace must not overlap (same stream, or ordered).
  * Errors: EDDA_ERR_INVALID_ARGUMENT (NULL q/k/v/o, n_q outside [1,16], n_kv < 1),
  * EDDA_ERR_MISALIGNED (q/k/v/o not 16-byte aligned, mask_rows not 4-byte
  * aligned), EDDA_ERR_WORKSPACE, EDDA_ERR_HIP.
@@ -149,7 +157,10 @@ edda_status edda_verify_attn(const void* q, int32_t n_q, const void* k, const vo
                              const uint32_t* mask_rows, void* o, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace edda_verify_attn needs (0 when one split suffices or the shape is invalid). */
+/* Bytes of workspace edda_verify_attn needs: 0 for caches of at most 128 keys (one workgroup
+ * per head) or an invalid shape; longer caches split the keys into 128-key ranges, one
+ * workgroup each, whose fp32 partial results the last workgroup of each head to finish merges
+ * in the same launch: EDDA_VERIFY_COUNTER_BYTES + splits * n_q * 20 * 66 * 4 bytes. */
 size_t edda_verify_workspace_bytes(int32_t n_q, int32_t n_kv);
 
 /* Text of the calling thread's most recent error ("" after a successful call). */

@@ -46,13 +46,24 @@ def test_version_and_error_text(lib):
     assert b"non-null" in lib.edda_last_error()
 
 
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (EDDA_\w+) (\d+)", text))
+    assert int(consts["EDDA_VERIFY_COUNTER_BYTES"]) == _lib.VERIFY_COUNTER_BYTES
+    assert int(consts["EDDA_MAX_VERIFY_QUERIES"]) == _lib.MAX_VERIFY_QUERIES
+    assert int(consts["EDDA_D_MODEL"]) == _lib.D_MODEL
+
+
 def test_workspace_sizes(lib):
     assert lib.edda_encoder_workspace_bytes(1, 1500) == 1500 * 1280 * 2
     assert lib.edda_encoder_workspace_bytes(16, 1500) == 16 * 1500 * 1280 * 2
     assert lib.edda_encoder_workspace_bytes(0, 1500) == 0
     assert lib.edda_encoder_workspace_bytes(1, -3) == 0
     assert lib.edda_verify_workspace_bytes(16, 100) == 0      # one split: no workspace
-    assert lib.edda_verify_workspace_bytes(16, 1500) > 0
+    assert lib.edda_verify_workspace_bytes(16, 128) == 0
+    C = _lib.VERIFY_COUNTER_BYTES
+    assert lib.edda_verify_workspace_bytes(16, 129) == C + 2 * 16 * 20 * 66 * 4  # counters + partials
+    assert lib.edda_verify_workspace_bytes(3, 1500) == C + 12 * 3 * 20 * 66 * 4
     assert lib.edda_verify_workspace_bytes(17, 1500) == 0      # invalid n_q
     assert lib.edda_verify_workspace_bytes(1, 0) == 0
 

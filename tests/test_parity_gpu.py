@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
+from whisper_asr_encoder_amd import _lib
 from whisper_asr_encoder_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
@@ -196,9 +197,11 @@ def run_verify(torch, case, mask=None, use_mask=True):
     if mask is not None:
         m = mask
     o = torch.full(case.q.shape, float("nan"), dtype=torch.float16, device="cuda")
-    va.workspace.fill_(255)
+    C = _lib.VERIFY_COUNTER_BYTES
+    va.workspace[C:].fill_(255)  # poison the partials; the arrival counters start at zero
     va(dev(torch, case.q), dev(torch, case.k), dev(torch, case.v), va.mask_rows(m), o)
     torch.cuda.synchronize()
+    assert not va.workspace[:C].any().item(), "arrival counters not returned to zero"
     return host(o), m
 
 
@@ -221,7 +224,8 @@ def test_verify_workload(torch, trial):
 @pytest.mark.parametrize("n_q,n_kv,kind", [
     (1, 1, "none"), (1, 33, "causal"), (16, 16, "causal"), (16, 31, "causal"), (16, 32, "causal"),
     (16, 33, "causal"), (16, 127, "random"), (16, 128, "none"), (16, 129, "causal"),
-    (5, 300, "random"), (16, 1500, "none"), (7, 4096, "random"), (16, 200, "empty_rows")])
+    (5, 300, "random"), (16, 1500, "none"), (7, 4096, "random"), (16, 200, "empty_rows"),
+    (16, 4097, "causal"), (9, 6000, "random"), (16, 5000, "empty_rows")])
 def test_verify_edges(torch, n_q, n_kv, kind):
     say(f"verify edge n_q={n_q} n_kv={n_kv} {kind}")
     r = np.random.default_rng(n_q * 7919 + n_kv)
@@ -242,3 +246,52 @@ def test_verify_edges(torch, n_q, n_kv, kind):
     check(got, ref, "o")
     if kind == "empty_rows":
         assert np.all(got[[0, 5, 15]] == 0)
+
+
+def test_verify_graph_replay(torch):
+    """The verification launches captured in a HIP graph (as a decoder replays them) give the
+    eager results on every replay, with eager work between replays, and leave the workspace's
+    arrival counters at zero (the graph's arguments, counters included, are fixed)."""
+    from whisper_asr_encoder_amd.encoder import VerifyAttention
+    say("verify graph replay: causal L=360, cross 1500, random mask 5000")
+    r = np.random.default_rng(4242)
+    va = VerifyAttention(5000)
+    cases = []
+    for n_kv, kind in ((360, "causal"), (1500, "none"), (5000, "random")):
+        q = r.standard_normal((16, 20, 64)).astype(np.float16)
+        k = r.standard_normal((n_kv, 20, 64)).astype(np.float16)
+        v = r.standard_normal((n_kv, 20, 64)).astype(np.float16)
+        mask = {"causal": oracle.causal_rows(16, n_kv), "none": None,
+                "random": r.random((16, n_kv)) < 0.3}[kind]
+        cases.append((dev(torch, q), dev(torch, k), dev(torch, v), va.mask_rows(mask),
+                      torch.empty((16, 20, 64), dtype=torch.float16, device="cuda"), (q, k, v, mask)))
+
+    def run():
+        for q, k, v, m, o, _ in cases:
+            va(q, k, v, m, o)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [host(c[4]) for c in cases]
+    for got, c in zip(eager, cases):
+        check(got, oracle.verify_attention(*c[5]), "eager")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        for c in cases:
+            c[4].fill_(float("nan"))
+        va.workspace[_lib.VERIFY_COUNTER_BYTES:].fill_(255)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, c in enumerate(cases):
+            assert np.array_equal(host(c[4]), eager[i]), f"replay {rep} case {i}"
+        assert not va.workspace[:_lib.VERIFY_COUNTER_BYTES].any().item(), f"replay {rep}: arrival counters not zero"
+        run()  # eager work between replays
+        torch.cuda.synchronize()

@@ -21,6 +21,7 @@ N_HEADS = 20
 HEAD_DIM = 64
 QKV_COLS = 3 * D_MODEL
 MAX_VERIFY_QUERIES = 16
+VERIFY_COUNTER_BYTES = 5120  # leading workspace bytes of edda_verify_attn: zero before first use
 
 STATUS = {0: "EDDA_OK", 1: "EDDA_ERR_INVALID_ARGUMENT", 2: "EDDA_ERR_UNSUPPORTED",
           3: "EDDA_ERR_MISALIGNED", 4: "EDDA_ERR_WORKSPACE", 5: "EDDA_ERR_HIP"}

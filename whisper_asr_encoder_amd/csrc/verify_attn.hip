@@ -3,20 +3,24 @@
 // whose slot j holds position j, under per-query bitset mask rows (causal,
 // token-tree ancestors, or none for cross-attention).
 //
-// The work is memory bound (each K/V byte is used by at most 16 queries), so
-// the key sequence is split across workgroups: workgroup (split, head) covers
-// kSplitKeys keys, each of its 4 waves 32 of them.  Per wave, on 16x16x32
-// MFMAs: S^T = K Q^T (lane l holds 8 scores of query l % 16), masked online
-// softmax statistics via cross-lane max/sum, then O^T = V^T P^T with P kept in
-// registers as the B operand and V^T staged through a wave-private LDS tile.
-// The 4 waves merge in LDS; with more than one split, fp32 partials
-// (m, l, unnormalized o) go to the workspace and a second kernel merges them:
-//   m = max_s m_s,  l = sum_s l_s 2^(m_s - m),  O = sum_s o_s 2^(m_s - m) / l.
-// A query with no admitted key gets O = 0.
+// The work is memory bound (each K/V byte is used by at most 16 queries) and small
+// (a few MB per call), so the time is latency: the key sequence is split across
+// many workgroups, one launch covers the call, and every load a wave needs is
+// issued at kernel start.  Workgroup (split, head) covers kSplitKeys keys, each of
+// its 4 waves 32 of them.  Per wave, on 16x16x32 MFMAs: S^T = K Q^T (lane l holds 8
+// scores of query l % 16), masked softmax statistics via cross-lane max/sum (lane
+// swaps between 16- and 32-lane halves), then O^T = V^T P^T with P kept in
+// registers as the B operand and V^T staged through a wave-private LDS tile.  The 4
+// waves merge in LDS.  With more than one split, each workgroup writes fp32 partials
+// (m, l, unnormalized o) to the workspace and counts itself in on a per-head arrival
+// counter; the last to arrive merges every split of its head:
+//   m = max_s m_s,  l = sum_s l_s 2^(m_s - m),  O = sum_s o_s 2^(m_s - m) / l,
+// and sets the counter back to zero.  A query with no admitted key gets O = 0.
 #include <math.h>
 
 #include "device.hpp"
 #include "kernels.hpp"
+#include "../../include/edda.h"
 
 namespace edda {
 namespace {
@@ -27,55 +31,112 @@ constexpr int kWaveKeys = 32;
 constexpr int kSplitKeys = kVWaves * kWaveKeys;
 constexpr int kMaxQ = 16;
 constexpr int kVtLd = kWaveKeys + 4;  // V^T row stride (halves): 72 B, 8-byte aligned
+// Per-head arrival counters at the workspace start, one per 256-byte line so that the
+// heads' atomics do not queue on a shared line.
+constexpr int kCounterStride = 64;  // uint32 words
+constexpr size_t kCounterBytes = (size_t)kHeads * kCounterStride * sizeof(uint32_t);
+static_assert(kCounterBytes == EDDA_VERIFY_COUNTER_BYTES, "counter region size in the public header");
 
-__global__ __launch_bounds__(kVThreads) void verify_split_kernel(
+// s_waitcnt immediate: vmcnt 0, expcnt and lgkmcnt at their maxima (no wait).
+constexpr int kWaitVmcnt0 = 0x0F70;
+constexpr int kMergeBatch = 16;  // splits whose partials the merging workgroup loads at once
+
+// Two floats (8-byte aligned) as one agent-scope atomic access.
+__device__ __forceinline__ void store_coherent(float* p, float a, float b) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, (f32x2){a, b}),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2 load_coherent(const float* p) {
+  return __builtin_bit_cast(f32x2, __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)),
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+__device__ __forceinline__ float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ uint32_t as_u32(float x) { return __builtin_bit_cast(uint32_t, x); }
+
+// Max / sum over lanes {l, l ^ 16, l ^ 32, l ^ 48}.  The gfx950 lane swaps exchange
+// odd and even 16-lane rows (permlane16) and the two 32-lane halves (permlane32)
+// between two registers; with both operands x, the two results hold x of lane l and
+// of lane l ^ 16 (resp. l ^ 32), in the same order in both lanes of a pair, so the
+// combined value is bitwise equal across the four lanes.
+__device__ __forceinline__ float quad_max(float x) {
+  auto p = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+  x = fmaxf(as_f32(p[0]), as_f32(p[1]));
+  auto r = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  return fmaxf(as_f32(r[0]), as_f32(r[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  auto p = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+  x = as_f32(p[0]) + as_f32(p[1]);
+  auto r = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  return as_f32(r[0]) + as_f32(r[1]);
+}
+
+// grid (n_splits, 20 heads), 256 threads.  counters / part_ml / part_o are used only
+// when n_splits > 1 (they are written by other workgroups, so not restrict).
+template <bool kMasked>
+__global__ __launch_bounds__(kVThreads) void verify_kernel(
     const f16* __restrict__ q, int n_q, const f16* __restrict__ k, const f16* __restrict__ v,
     int n_kv, const uint32_t* __restrict__ mask, int mask_words, f16* __restrict__ o,
-    float* __restrict__ part_ml, float* __restrict__ part_o, int n_splits) {
+    uint32_t* counters, float* part_ml, float* part_o) {
   __shared__ __attribute__((aligned(16))) f16 Vt[kVWaves][kHeadDim * kVtLd];
   __shared__ float mw[kVWaves][kMaxQ], lw[kVWaves][kMaxQ];
-  __shared__ float ow[kVWaves][kMaxQ][kHeadDim + 4];
+  __shared__ __attribute__((aligned(16))) float ow[kVWaves][kMaxQ][kHeadDim + 4];
+  __shared__ int last_arrival;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, G = lane >> 4;
-  const int split = blockIdx.x, head = blockIdx.y;
+  const int split = blockIdx.x, head = blockIdx.y, n_splits = gridDim.x;
   const int key0 = split * kSplitKeys + wave * kWaveKeys;  // multiple of 32
-  const size_t kv_stride = (size_t)kHeads * kHeadDim;
+  constexpr int kKvStride = kHeads * kHeadDim;
+  const int last_key = n_kv - 1;
   const f16x8 z8 = {};
 
-  // Q^T fragments: lane holds Q[r16][head][32 s + 8 G .. +7].
+  // Every global load first, unconditionally (rows past the cache end are clamped to
+  // its last row and masked out below; element offsets fit 32 bits for any valid n_kv).
   const bool q_ok = r16 < n_q;
-  f16x8 qf[2];
+  const int q_row = min(r16, n_q - 1);
+  uint32_t bits = 0xffffffffu;
+  if constexpr (kMasked) bits = mask[(uint32_t)(q_row * mask_words + min(key0 >> 5, mask_words - 1))];
+  f16x8 qf[2], kf[2][2], va[2], vb[2];
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
-    qf[s] = q_ok ? load16(q + ((size_t)r16 * kHeads + head) * kHeadDim + 32 * s + 8 * G) : z8;
+  for (int s = 0; s < 2; ++s) qf[s] = load16(q + (uint32_t)((q_row * kHeads + head) * kHeadDim + 32 * s + 8 * G));
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int key = min(key0 + 16 * blk + r16, last_key);
+    const uint32_t off = (uint32_t)(key * kKvStride + head * kHeadDim + 8 * G);
+    kf[blk][0] = load16(k + off);
+    kf[blk][1] = load16(k + (off + 32));
+  }
+  // V rows as two keys per 16-byte group, for the transposed LDS staging.
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int u = lane + kWave * r;
+    const int kp = u >> 3, c8 = u & 7;
+    const int key = key0 + 2 * kp;
+    va[r] = load16(v + (uint32_t)(min(key, last_key) * kKvStride + head * kHeadDim + 8 * c8));
+    vb[r] = load16(v + (uint32_t)(min(key + 1, last_key) * kKvStride + head * kHeadDim + 8 * c8));
+  }
+  if (!q_ok) qf[0] = qf[1] = z8;
 
   // Stage this wave's V tile transposed: Vt[d][key - key0]; key pairs share a 32-bit word.
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int u = lane + kWave * r;
-    const int kp = u >> 3, c = u & 7;
-    const int key = key0 + 2 * kp;
-    const f16x8 a = key < n_kv ? load16(v + key * kv_stride + head * kHeadDim + 8 * c) : z8;
-    const f16x8 b = key + 1 < n_kv ? load16(v + (key + 1) * kv_stride + head * kHeadDim + 8 * c) : z8;
+    const int kp = u >> 3, c8 = u & 7;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<f16x2*>(&Vt[wave][(8 * c + e) * kVtLd + 2 * kp]) = (f16x2){a[e], b[e]};
+      *reinterpret_cast<f16x2*>(&Vt[wave][(8 * c8 + e) * kVtLd + 2 * kp]) = (f16x2){va[r][e], vb[r][e]};
   }
 
   // S^T for keys key0 + 16 blk + 4 G + r, query r16.
   f32x4 sacc[2];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    const int key = key0 + 16 * blk + r16;
-    const f16* kp = k + key * kv_stride + head * kHeadDim + 8 * G;
-    const f16x8 k0 = key < n_kv ? load16(kp) : z8;
-    const f16x8 k1 = key < n_kv ? load16(kp + 32) : z8;
-    sacc[blk] = mfma_16x16x32(k0, qf[0], (f32x4){});
-    sacc[blk] = mfma_16x16x32(k1, qf[1], sacc[blk]);
+    sacc[blk] = mfma_16x16x32(kf[blk][0], qf[0], (f32x4){});
+    sacc[blk] = mfma_16x16x32(kf[blk][1], qf[1], sacc[blk]);
   }
-  uint32_t bits = 0;
-  if (q_ok && key0 < n_kv) bits = mask ? mask[(size_t)r16 * mask_words + (key0 >> 5)] : 0xffffffffu;
+  if (!q_ok) bits = 0;
   const float c_scale = kLog2e / 8.0f;
   float sc[8];
   float m = -INFINITY;
@@ -89,8 +150,7 @@ __global__ __launch_bounds__(kVThreads) void verify_split_kernel(
       sc[4 * blk + r] = s;
       m = fmaxf(m, s);
     }
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
+  m = quad_max(m);
   float l = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -98,8 +158,7 @@ __global__ __launch_bounds__(kVThreads) void verify_split_kernel(
     sc[i] = p;
     l += p;
   }
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = quad_sum(l);
 
   __syncthreads();  // V^T tiles visible to every lane
   const f16x8 pf = pack8(sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7]);
@@ -119,7 +178,7 @@ __global__ __launch_bounds__(kVThreads) void verify_split_kernel(
   }
   __syncthreads();
 
-  // Merge the 4 waves: thread -> (query, 4 consecutive dims).
+  // Merge the 4 waves: thread -> (query mq, dims d0 .. d0 + 3).
   const int mq = tid >> 4, d0 = (tid & 15) * 4;
   float M = -INFINITY;
 #pragma unroll
@@ -130,42 +189,87 @@ __global__ __launch_bounds__(kVThreads) void verify_split_kernel(
     for (int w = 0; w < kVWaves; ++w) {
       const float wt = exp2_fast(mw[w][mq] - M);
       L += lw[w][mq] * wt;
+      const f32x4 ov = *reinterpret_cast<const f32x4*>(&ow[w][mq][d0]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += ow[w][mq][d0 + j] * wt;
+      for (int j = 0; j < 4; ++j) acc[j] += ov[j] * wt;
     }
   }
-  if (mq >= n_q) return;
+  const bool row_ok = mq < n_q;
+  f16* out = o + ((size_t)mq * kHeads + head) * kHeadDim + d0;
   if (n_splits == 1) {
+    if (!row_ok) return;
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     const f16x2 lo = pack_rne(acc[0] * inv, acc[1] * inv), hi = pack_rne(acc[2] * inv, acc[3] * inv);
-    *reinterpret_cast<f16x4*>(o + ((size_t)mq * kHeads + head) * kHeadDim + d0) =
-        (f16x4){lo[0], lo[1], hi[0], hi[1]};
-  } else {
-    const size_t slot = ((size_t)split * n_q + mq) * kHeads + head;
-    *reinterpret_cast<f32x4*>(part_o + slot * kHeadDim + d0) = (f32x4){acc[0], acc[1], acc[2], acc[3]};
-    if (d0 == 0) *reinterpret_cast<f32x2*>(part_ml + slot * 2) = (f32x2){M, L};
+    *reinterpret_cast<f16x4*>(out) = (f16x4){lo[0], lo[1], hi[0], hi[1]};
+    return;
   }
-}
 
-// grid (n_q, 20 heads), 64 threads: lane -> one output dimension.
-__global__ __launch_bounds__(kWave) void verify_merge_kernel(const float* __restrict__ part_ml,
-                                                             const float* __restrict__ part_o,
-                                                             int n_splits, int n_q,
-                                                             f16* __restrict__ o) {
-  const int qi = blockIdx.x, head = blockIdx.y, d = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s)
-    M = fmaxf(M, part_ml[(((size_t)s * n_q + qi) * kHeads + head) * 2]);
-  float L = 0.0f, acc = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const size_t slot = ((size_t)s * n_q + qi) * kHeads + head;
-      const float wt = exp2_fast(part_ml[slot * 2] - M);
-      L += part_ml[slot * 2 + 1] * wt;
-      acc += part_o[slot * kHeadDim + d] * wt;
-    }
+  // Partials of this split, then the arrival count.  The partials and the counter are
+  // accessed with agent-scope atomics, which the XCDs' separate L2 caches keep coherent
+  // without whole-cache write-back or invalidation.  Each wave waits until its stores
+  // are acknowledged before the workgroup barrier, so they are visible device-wide
+  // before thread 0 counts the workgroup in; the last workgroup's loads are issued
+  // after the count returned.
+  // Slot (split s, query mq, head): (m, l) at part_ml[2 slot], o at part_o[64 slot + d0];
+  // slot = (s n_q + mq) 20 + head, all offsets below 2^31 for any valid call.
+  const int slot0 = mq * kHeads + head, slot_step = n_q * kHeads;
+  if (row_ok) {
+    const int slot = split * slot_step + slot0;
+    store_coherent(part_o + (uint32_t)(slot * kHeadDim + d0), acc[0], acc[1]);
+    store_coherent(part_o + (uint32_t)(slot * kHeadDim + d0 + 2), acc[2], acc[3]);
+    if (d0 == 0) store_coherent(part_ml + (uint32_t)(slot * 2), M, L);
   }
-  o[((size_t)qi * kHeads + head) * kHeadDim + d] = (f16)(L > 0.0f ? acc / L : 0.0f);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (tid == 0)
+    last_arrival = __hip_atomic_fetch_add(&counters[head * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   (uint32_t)(n_splits - 1);
+  __syncthreads();
+  if (!last_arrival) return;
+  // Every split has arrived: reset the counter for the next call.
+  if (tid == 0) __hip_atomic_store(&counters[head * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!row_ok) return;
+  // Merge the splits kMergeBatch at a time: every load of a batch is issued before any
+  // is used (indices past the last split are clamped and their weights dropped), and
+  // the running (M, L, sum) is rescaled to each batch's maximum.
+  M = -INFINITY;
+  L = 0.0f;
+  f32x4 sum = {};
+  for (int s0 = 0; s0 < n_splits; s0 += kMergeBatch) {
+    float pm[kMergeBatch], pl[kMergeBatch];
+    f32x4 po[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int slot = min(s0 + i, n_splits - 1) * slot_step + slot0;
+      const f32x2 ml = load_coherent(part_ml + (uint32_t)(slot * 2));
+      const f32x2 o01 = load_coherent(part_o + (uint32_t)(slot * kHeadDim + d0));
+      const f32x2 o23 = load_coherent(part_o + (uint32_t)(slot * kHeadDim + d0 + 2));
+      pm[i] = ml[0];
+      pl[i] = ml[1];
+      po[i] = (f32x4){o01[0], o01[1], o23[0], o23[1]};
+    }
+    float mb = M;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (s0 + i < n_splits) mb = fmaxf(mb, pm[i]);
+    if (mb == -INFINITY) continue;  // no admitted key so far
+    const float a = M == -INFINITY ? 0.0f : exp2_fast(M - mb);
+    L *= a;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sum[j] *= a;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      // 0 for a split with no admitted key (m = -inf) and for indices past the last split.
+      const float wt = s0 + i < n_splits ? exp2_fast(pm[i] - mb) : 0.0f;
+      L += pl[i] * wt;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sum[j] += po[i][j] * wt;
+    }
+    M = mb;
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const f16x2 lo = pack_rne(sum[0] * inv, sum[1] * inv), hi = pack_rne(sum[2] * inv, sum[3] * inv);
+  *reinterpret_cast<f16x4*>(out) = (f16x4){lo[0], lo[1], hi[0], hi[1]};
 }
 
 }  // namespace
@@ -175,27 +279,30 @@ int verify_num_splits(int n_kv) { return (n_kv + kSplitKeys - 1) / kSplitKeys; }
 size_t verify_workspace_bytes(int n_q, int n_kv) {
   const int s = verify_num_splits(n_kv);
   if (s <= 1) return 0;
-  return (size_t)s * n_q * kHeads * (2 + kHeadDim) * sizeof(float);
+  return kCounterBytes + (size_t)s * n_q * kHeads * (2 + kHeadDim) * sizeof(float);
 }
 
 hipError_t launch_verify(const void* q, int n_q, const void* k, const void* v, int n_kv,
                          const uint32_t* mask, void* o, void* workspace, hipStream_t stream) {
   const int n_splits = verify_num_splits(n_kv);
+  const int mask_words = (n_kv + 31) / 32;
+  uint32_t* counters = nullptr;
   float* part_ml = nullptr;
   float* part_o = nullptr;
   if (n_splits > 1) {
-    part_ml = static_cast<float*>(workspace);
+    counters = static_cast<uint32_t*>(workspace);
+    part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
     part_o = part_ml + (size_t)n_splits * n_q * kHeads * 2;
   }
-  const int mask_words = (n_kv + 31) / 32;
-  hipLaunchKernelGGL(verify_split_kernel, dim3(n_splits, kHeads), dim3(kVThreads), 0, stream,
-                     static_cast<const f16*>(q), n_q, static_cast<const f16*>(k),
-                     static_cast<const f16*>(v), n_kv, mask, mask_words, static_cast<f16*>(o),
-                     part_ml, part_o, n_splits);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || n_splits == 1) return e;
-  hipLaunchKernelGGL(verify_merge_kernel, dim3(n_q, kHeads), dim3(kWave), 0, stream, part_ml, part_o,
-                     n_splits, n_q, static_cast<f16*>(o));
+  const dim3 grid(n_splits, kHeads);
+  if (mask)
+    hipLaunchKernelGGL(verify_kernel<true>, grid, dim3(kVThreads), 0, stream, static_cast<const f16*>(q), n_q,
+                       static_cast<const f16*>(k), static_cast<const f16*>(v), n_kv, mask, mask_words,
+                       static_cast<f16*>(o), counters, part_ml, part_o);
+  else
+    hipLaunchKernelGGL(verify_kernel<false>, grid, dim3(kVThreads), 0, stream, static_cast<const f16*>(q), n_q,
+                       static_cast<const f16*>(k), static_cast<const f16*>(v), n_kv, mask, mask_words,
+                       static_cast<f16*>(o), counters, part_ml, part_o);
   return hipGetLastError();
 }
 

@@ -58,8 +58,9 @@ class VerifyAttention:
     def __init__(self, max_kv: int, device="cuda"):
         import torch
         self.torch = torch
-        nbytes = max(_lib.verify_workspace_bytes(_lib.MAX_VERIFY_QUERIES, max_kv), 16)
-        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        nbytes = max(_lib.verify_workspace_bytes(_lib.MAX_VERIFY_QUERIES, max_kv), _lib.VERIFY_COUNTER_BYTES)
+        # Zero-filled once: the leading arrival counters must start at zero (calls keep them so).
+        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         self.device = device
 
     def mask_rows(self, mask):
