@@ -304,6 +304,9 @@ def verify_bench(args, torch):
         graph.replay()
     ms = timer(graph.replay, args.steps)
     L = I.cache_length(trial)
+    dig = source_digest(["verify_attn.hip"])
+    t_causal, t_cross = measured_traffic("verify_causal", dig), measured_traffic("verify_cross", dig)
+    traffic = round((t_causal + t_cross) / 2) if t_causal and t_cross else None
     return {
         "metric": "verification attention pass (32 layers x causal self + cross attention) on 1 MI355X",
         "value": round(bytes_alg / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
@@ -314,9 +317,12 @@ def verify_bench(args, torch):
         "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
         "config": {"workload": f"speculative block verification: 16 queries, self cache L={L}, "
                                f"cross 1500 encoder frames, 32 layers", "parallelism": "single GPU"},
+        # Per launch on average (32 causal + 32 cross launches per pass); traffic is the
+        # mean of the two kernels' measured HBM bytes per launch.
         "roofline": {"bound": "hbm", "achieved": round(bytes_alg / (ms * 1e-3) / 1e9, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(bytes_alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None},
+                     "frac": round(bytes_alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "bytes_per_launch": round(bytes_alg / (2 * layers)), "traffic": traffic},
     }
 
 

@@ -9,11 +9,12 @@ passes (FETCH_SIZE, then WRITE_SIZE) write, and produces
   of known size in the same run (bench.py --calibrate-copy issues that copy).
 
     python -m whisper_asr_encoder_amd.profiling TRACE_DIR FETCH_DIR WRITE_DIR OUT_DIR \
-        --command "<the rocprofv3 command lines>"
+        --workload window|verify --command "<the rocprofv3 command lines>"
 
-writes OUT_DIR/<kernel>_window.md for each kernel and OUT_DIR/traffic.json, keyed by the
-names bench.py reports (qkv_gemm, flash_attn, out_gemm), each with the digest of the
-kernel sources the counters were taken on.
+writes OUT_DIR/<kernel>_<workload>.md for each kernel of the workload and updates
+OUT_DIR/traffic.json, keyed by the names bench.py reports (qkv_gemm, flash_attn, out_gemm;
+verify_causal, verify_cross), each with the digest of the kernel sources the counters were
+taken on.
 """
 from __future__ import annotations
 
@@ -28,13 +29,21 @@ import statistics
 HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
 
-# Kernel symbol fragment -> (report key, source files).  The window workload launches
-# the 128x192 GEMM variant for the QKV projection (N = 3840) and the 128x64 variant for
-# the output projection (N = 1280).
-KERNELS = {
-    "gemm_bias_kernelILi128ELi192E": ("qkv_gemm", ["gemm.hip"]),
-    "flash_attn_kernel": ("flash_attn", ["flash_attn.hip"]),
-    "gemm_bias_kernelILi128ELi64E": ("out_gemm", ["gemm.hip"]),
+# Per workload: kernel symbol fragment -> (report key, source files).  The window workload
+# launches the 128x192 GEMM variant for the QKV projection (N = 3840) and the 128x64
+# variant for the output projection (N = 1280); the verification pass launches the masked
+# kernel for causal self-attention and the unmasked one for cross-attention.
+WORKLOADS = {
+    "window": ("one 30 s window (1500 frames), 32 attention sublayers", {
+        "gemm_bias_kernelILi128ELi192E": ("qkv_gemm", ["gemm.hip"]),
+        "flash_attn_kernel": ("flash_attn", ["flash_attn.hip"]),
+        "gemm_bias_kernelILi128ELi64E": ("out_gemm", ["gemm.hip"]),
+    }),
+    "verify": ("block verification, 16 queries, 32 layers (causal self-attention over a "
+               "360-slot cache, cross-attention over 1500 frames)", {
+        "verify_kernelILb1E": ("verify_causal", ["verify_attn.hip"]),
+        "verify_kernelILb0E": ("verify_cross", ["verify_attn.hip"]),
+    }),
 }
 COPY_KERNEL = "copyBuffer"
 
@@ -77,7 +86,8 @@ def _match(values, fragment):
     return [x for h in hits for x in h]
 
 
-def summarize(trace_dir, fetch_dir, write_dir, out_dir, command):
+def summarize(trace_dir, fetch_dir, write_dir, out_dir, command, workload="window"):
+    title, kernels = WORKLOADS[workload]
     stats = kernel_stats(trace_dir)
     fetch = counter_values(fetch_dir, "FETCH_SIZE")
     write = counter_values(write_dir, "WRITE_SIZE")
@@ -87,10 +97,15 @@ def summarize(trace_dir, fetch_dir, write_dir, out_dir, command):
     f_scale = COPY_BYTES / (max(copy_f) * 1024.0)
     w_scale = COPY_BYTES / (max(copy_w) * 1024.0)
     os.makedirs(out_dir, exist_ok=True)
-    traffic = {"_method": (f"median per-dispatch FETCH_SIZE x {f_scale:.3f} + WRITE_SIZE x {w_scale:.3f} "
+    tpath = os.path.join(out_dir, "traffic.json")
+    traffic = {}
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            traffic = json.load(f)
+    traffic["_method"] = (f"median per-dispatch FETCH_SIZE x {f_scale:.3f} + WRITE_SIZE x {w_scale:.3f} "
                            f"(KiB -> bytes; factors make a {COPY_BYTES >> 20} MiB device copy read its "
-                           "true size)")}
-    for frag, (key, srcs) in KERNELS.items():
+                           "true size)")
+    for frag, (key, srcs) in kernels.items():
         st = [v for k, v in stats.items() if frag in k]
         fv, wv = _match(fetch, frag), _match(write, frag)
         if not st or not fv or not wv:
@@ -102,8 +117,8 @@ def summarize(trace_dir, fetch_dir, write_dir, out_dir, command):
         traffic[key] = {"bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
                         "source_digest": digest}
         name = [k for k in stats if frag in k][0]
-        with open(os.path.join(out_dir, f"{key}_window.md"), "w") as f:
-            f.write(f"# {key}: one 30 s window (1500 frames), 32 attention sublayers\n\n")
+        with open(os.path.join(out_dir, f"{key}_{workload}.md"), "w") as f:
+            f.write(f"# {key}: {title}\n\n")
             f.write(f"Kernel symbol: `{name}`\n\n")
             f.write("Commands (run from the repository root on one MI355X):\n\n```\n" + command.strip() + "\n```\n\n")
             f.write("| figure | value |\n|---|---|\n")
@@ -115,7 +130,7 @@ def summarize(trace_dir, fetch_dir, write_dir, out_dir, command):
             f.write(f"| HBM bytes per launch (scaled) | {(fb + wb) / 1e6:.2f} MB "
                     f"(read {fb / 1e6:.2f}, write {wb / 1e6:.2f}) |\n")
             f.write(f"| kernel sources digest | {digest} |\n")
-    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
+    with open(tpath, "w") as f:
         json.dump(traffic, f, indent=1)
         f.write("\n")
     return traffic
@@ -128,8 +143,10 @@ def main():
     ap.add_argument("write_dir")
     ap.add_argument("out_dir")
     ap.add_argument("--command", required=True)
+    ap.add_argument("--workload", default="window", choices=sorted(WORKLOADS))
     a = ap.parse_args()
-    print(json.dumps(summarize(a.trace_dir, a.fetch_dir, a.write_dir, a.out_dir, a.command), indent=1))
+    print(json.dumps(summarize(a.trace_dir, a.fetch_dir, a.write_dir, a.out_dir, a.command, a.workload),
+                     indent=1))
 
 
 if __name__ == "__main__":
