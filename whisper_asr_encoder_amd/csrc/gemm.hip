@@ -7,17 +7,22 @@
 // C^T tiles (weights as the A operand); fp32 accumulation, bias added in fp32,
 // one round-to-nearest-even to fp16.
 //
-// Data movement (one workgroup of 4 waves per BM x BN tile, K step BK = 64):
+// Data movement (one workgroup per BM x BN tile, K step BK = 64): 4 compute waves
+// issue the MFMAs and 4 producer waves (one of each per SIMD) the global -> LDS copies.
 //  * global -> LDS by direct-to-LDS DMA (global_load_lds_dwordx4) into a ring of
-//    STAGES tiles; STAGES tiles are in flight before the first MFMA and the stage
-//    of tile k is refilled with tile k+STAGES once every wave has read it: each wave
-//    spreads its DMA instructions for that tile over the k16 steps of tile k+1 (a
-//    burst of them right after the barrier would stall on the address unit).
+//    STAGES tiles.  A DMA instruction is accepted only as fast as the CU's address
+//    unit drains (~16 clk per KB), and a wave waiting to issue one issues nothing
+//    else, so the copies and the MFMAs overlap only when different waves issue them.
+//    The producers fill all STAGES stages, then per tile k: wait for tile k (vmcnt),
+//    join barrier k, and refill the stage of tile k-1 with tile k-1+STAGES (every
+//    compute wave finished reading tile k-1 before joining barrier k).  (Joining
+//    barrier 0 right after tile 0 measured slower: at kernel start every CU pulls its
+//    first tiles at once, and the compute waves then wait at the next barriers.)  They leave
+//    after the last barrier of the K loop, with no copy in flight.
 //    A DMA instruction writes 1 KB = 8 rows of 128 bytes contiguously, so rows are
 //    not padded; instead the eight 16-byte chunks of row r are XOR-permuted with
 //    (r >> 1) & 7, which keeps the 16 rows of a fragment read on distinct banks.
-//    The DMA is issued from inline asm and waited for with explicit vmcnt counts,
-//    so the compiler's own LDS wait tracking stays exact.
+//    The DMA is issued from inline asm and waited for with explicit vmcnt counts.
 //  * LDS -> registers: the fragments of k16 step s+1 are read while the MFMAs of
 //    step s run (one read slotted after each MFMA), double-buffered in VGPRs.
 //  * epilogue: accumulators (+ bias, fp16) are staged through LDS and written back
@@ -37,7 +42,10 @@ namespace {
 constexpr int kBK = 64;             // K elements per tile
 constexpr int kRowBytes = kBK * 2;  // 128 bytes per tile row
 constexpr int kKSteps = kBK / 16;   // 16-deep MFMA steps per tile
-constexpr int kGemmThreads = 256;
+constexpr int kComputeWaves = 4;
+constexpr int kProducerWaves = 4;
+constexpr int kComputeThreads = kComputeWaves * kWave;
+constexpr int kGemmThreads = (kComputeWaves + kProducerWaves) * kWave;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -62,6 +70,19 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(n) : "memory");
 }
 
+// Workgroup barrier with no memory wait (the producers wait for the copies); the
+// memory clobber keeps LDS accesses on their side of it.
+__device__ __forceinline__ void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>());
+    static_for<N, I + 1>(f);
+  }
+}
+
 // Compiler-visible wait for every outstanding LDS read of this wave.
 __device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
@@ -84,14 +105,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
                                                                  const f16* __restrict__ bias,
                                                                  f16* __restrict__ C, int M, int N,
                                                                  int K, TileMap map) {
-  static_assert(WM * WN * kWave == kGemmThreads, "wave grid must use 256 threads");
+  static_assert(WM * WN == kComputeWaves, "wave grid must use the compute waves");
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32-aligned");
-  constexpr int kWaves = kGemmThreads / kWave;
-  static_assert((BM / 8) % kWaves == 0 && (BN / 8) % kWaves == 0, "DMA groups must split evenly");
-  constexpr int AGW = BM / 8 / kWaves, BGW = BN / 8 / kWaves;
-  constexpr int IPW = AGW + BGW;  // DMA instructions per wave per tile
+  static_assert((BM / 8) % kProducerWaves == 0 && (BN / 8) % kProducerWaves == 0,
+                "DMA groups must split evenly");
+  constexpr int AGW = BM / 8 / kProducerWaves, BGW = BN / 8 / kProducerWaves;
+  constexpr int IPW = AGW + BGW;  // DMA instructions per producer wave per tile
+  static_assert(IPW * (STAGES - 1) < 64, "vmcnt range");
   constexpr int kStageBytes = (BM + BN) * kRowBytes;
   constexpr int kCld = BN + 8;    // epilogue tile row stride (halves)
   static_assert(BM * kCld * 2 <= STAGES * kStageBytes, "epilogue tile must fit in the ring");
@@ -130,42 +152,52 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
 
   // DMA sources: lane i of an 8-row group fetches row group*8 + i/8, physical chunk i%8,
   // i.e. logical chunk (i%8) ^ swz(row).
-  const int dr = lane >> 3, dpc = lane & 7;
-  const f16* a_src[AGW];
-  const f16* b_src[BGW];
+  if (wave >= kComputeWaves) {
+    // Producer wave pw: DMA groups pw * AGW .. of A and pw * BGW .. of B.  Lane i of an
+    // 8-row group fetches row group*8 + i/8, physical chunk i%8, i.e. logical chunk
+    // (i%8) ^ swz(row).
+    const int pw = wave - kComputeWaves;
+    const int dr = lane >> 3, dpc = lane & 7;
+    const f16* a_src[AGW];
+    const f16* b_src[BGW];
 #pragma unroll
-  for (int j = 0; j < AGW; ++j) {
-    const int row = (wave * AGW + j) * 8 + dr;
-    a_src[j] = A + (size_t)min(m0 + row, M - 1) * K + (dpc ^ swz(row)) * 8;
-  }
-#pragma unroll
-  for (int j = 0; j < BGW; ++j) {
-    const int row = (wave * BGW + j) * 8 + dr;
-    b_src[j] = Bt + (size_t)(n0 + row) * K + (dpc ^ swz(row)) * 8;
-  }
-  const uint32_t smem_addr = __builtin_amdgcn_readfirstlane(lds_address(smem));
-  // DMA instruction j (0 .. IPW-1) of this wave's share of tile kt.
-  auto issue_part = [&](int kt, int j) {
-    const uint32_t st = smem_addr + (kt % STAGES) * kStageBytes;
-    const int k0 = kt * kBK;
-    if (j < AGW) {
-      dma16(a_src[j] + k0, st + (wave * AGW + j) * 1024);
-    } else {
-      dma16(b_src[j - AGW] + k0, st + BM * kRowBytes + (wave * BGW + j - AGW) * 1024);
+    for (int j = 0; j < AGW; ++j) {
+      const int row = (pw * AGW + j) * 8 + dr;
+      a_src[j] = A + (size_t)min(m0 + row, M - 1) * K + (dpc ^ swz(row)) * 8;
     }
-  };
-  auto issue = [&](int kt) {
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) issue_part(kt, j);
-  };
-  // Parts [lo, hi) of tile dma (nothing when dma < 0).
-  auto issue_range = [&](int dma, int lo, int hi) {
-    if (dma >= 0) {
-#pragma unroll
-      for (int j = lo; j < hi; ++j) issue_part(dma, j);
+    for (int j = 0; j < BGW; ++j) {
+      const int row = (pw * BGW + j) * 8 + dr;
+      b_src[j] = Bt + (size_t)(n0 + row) * K + (dpc ^ swz(row)) * 8;
     }
-  };
-  constexpr int kPart1 = (IPW + 3) / 4, kPart2 = (IPW + 1) / 2, kPart3 = (3 * IPW + 3) / 4;
+    const uint32_t smem_addr = __builtin_amdgcn_readfirstlane(lds_address(smem));
+    auto issue = [&](int kt) {
+      const uint32_t st = smem_addr + (kt % STAGES) * kStageBytes;
+      const int k0 = kt * kBK;
+#pragma unroll
+      for (int j = 0; j < AGW; ++j) dma16(a_src[j] + k0, st + (pw * AGW + j) * 1024);
+#pragma unroll
+      for (int j = 0; j < BGW; ++j) dma16(b_src[j] + k0, st + BM * kRowBytes + (pw * BGW + j) * 1024);
+    };
+    // Wait until tile j has landed, with `after` (< STAGES) later tiles still allowed in
+    // flight, then join barrier j.
+    auto wait_tile = [&](int after) {
+      static_for<STAGES>([&](auto c) {
+        constexpr int n = decltype(c)::value;
+        if (after == n) wait_vmcnt_barrier<IPW * n>();
+      });
+    };
+#pragma unroll
+    for (int p = 0; p < STAGES; ++p)
+      if (p < nk) issue(p);
+    wait_tile(min(STAGES, nk) - 1);  // barrier 0
+    for (int j = 1; j < nk; ++j) {
+      // Tiles issued so far: 0 .. min(j - 2 + STAGES, nk - 1).
+      wait_tile(min(STAGES - 2, nk - 1 - j));  // barrier j
+      if (j - 1 + STAGES < nk) issue(j - 1 + STAGES);
+    }
+    return;
+  }
 
   // Fragment byte offsets inside a stage: row l32 (+ multiples of 32), chunk (2s+g) ^ swz(row).
   int frag_off[kKSteps];
@@ -173,13 +205,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
   for (int s = 0; s < kKSteps; ++s) frag_off[s] = l32 * kRowBytes + (((2 * s + g) ^ swz(l32)) << 4);
 
   // Bias values of this lane's output columns, loaded now so the epilogue does not wait.
+  // One uniform branch around all of the loads, so they are in flight together.
   f16x4 bias_v[FN][4];
+  if (bias) {
 #pragma unroll
-  for (int fn = 0; fn < FN; ++fn)
+    for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      bias_v[fn][i] = bias ? *reinterpret_cast<const f16x4*>(bias + n0 + wn * WTN + 32 * fn + 8 * i + 4 * g)
-                           : (f16x4){};
+      for (int i = 0; i < 4; ++i)
+        bias_v[fn][i] = *reinterpret_cast<const f16x4*>(bias + n0 + wn * WTN + 32 * fn + 8 * i + 4 * g);
+  } else {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bias_v[fn][i] = (f16x4){};
+  }
 
   f32x16 acc[FN][FM];
 #pragma unroll
@@ -220,64 +259,47 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
   using S1 = std::integral_constant<int, 1>;
   static_assert(kKSteps == 4, "the step schedule below assumes four k16 steps per tile");
 
-  // Steps 0..2 of tile kt: read step s+1 while the MFMAs of step s run; the DMA of
-  // tile dma is spread over the steps (the rest follows step 3).
-  auto first_steps = [&](int kt, int dma) {
+  // Steps 0..2 of tile kt: read step s+1 while the MFMAs of step s run.
+  auto first_steps = [&](int kt) {
     __builtin_amdgcn_sched_barrier(0);
     read_frags(kt, 1, S1());
     mfmas(S0());
     interleave();
     __builtin_amdgcn_sched_barrier(0);
-    issue_range(dma, 0, kPart1);
     read_frags(kt, 2, S0());
     mfmas(S1());
     interleave();
     __builtin_amdgcn_sched_barrier(0);
-    issue_range(dma, kPart1, kPart2);
     read_frags(kt, 3, S1());
     mfmas(S0());
     interleave();
     __builtin_amdgcn_sched_barrier(0);
-    issue_range(dma, kPart2, kPart3);
   };
 
-#pragma unroll
-  for (int p = 0; p < STAGES; ++p)
-    if (p < nk) issue(p);
-  if (nk > STAGES - 1) {
-    wait_vmcnt_barrier<IPW * (STAGES - 1)>();
-  } else {
-    wait_vmcnt_barrier<0>();
-  }
+  plain_barrier();  // barrier 0: tile 0 has landed
   read_frags(0, 0, S0());
   for (int kt = 0; kt + 1 < nk; ++kt) {
-    // Tile kt refills the stage freed before it with tile kt + STAGES - 1.
-    const int dma = kt >= 1 && kt + STAGES - 1 < nk ? kt + STAGES - 1 : -1;
-    first_steps(kt, dma);
-    issue_range(dma, kPart3, IPW);
-    // Tile kt is fully read once its last fragments are in registers: publish that,
-    // wait for tile kt+1 (tiles issued after it: min(STAGES-2, nk-2-kt)), refill the
-    // freed stage, and read step 0 of tile kt+1 during the last MFMAs of tile kt.
+    first_steps(kt);
+    // Tile kt is fully read once its last fragments are in registers: barrier kt+1
+    // publishes that (the producers then refill its stage) and, on the producers' side,
+    // that tile kt+1 has landed; step 0 of tile kt+1 is read during the last MFMAs of
+    // tile kt.
     wait_lds_reads();
-    if (kt + STAGES - 1 < nk) {
-      wait_vmcnt_barrier<IPW * (STAGES - 2)>();
-    } else if (STAGES > 3 && kt + 2 < nk) {
-      wait_vmcnt_barrier<IPW>();
-    } else {
-      wait_vmcnt_barrier<0>();
-    }
+    plain_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_frags(kt + 1, 0, S0());
     mfmas(S1());
     interleave();
     __builtin_amdgcn_sched_barrier(0);
   }
-  first_steps(nk - 1, -1);
+  first_steps(nk - 1);
   mfmas(S1());
 
   // Epilogue: bias, fp16, stage the tile in LDS, then coalesced 16-byte row stores.
+  // Only the compute waves are left (the producers ended after the K loop, which a
+  // workgroup barrier no longer waits for).
   wait_lds_reads();
-  __syncthreads();  // every wave is done reading the ring
+  __syncthreads();  // every compute wave is done reading the ring
   f16* cs = reinterpret_cast<f16*>(smem);
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
@@ -298,7 +320,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
   constexpr int kChunksPerRow = BN / 8;
   constexpr int kChunks = BM * kChunksPerRow;
 #pragma unroll 4
-  for (int c = tid; c < kChunks; c += kGemmThreads) {
+  for (int c = tid; c < kChunks; c += kComputeThreads) {
     const int ml = c / kChunksPerRow, cc = c % kChunksPerRow;
     const int m = m0 + ml;
     if (m < M) store16(C + (size_t)m * N + n0 + cc * 8, load16(cs + ml * kCld + cc * 8));
@@ -350,10 +372,10 @@ hipError_t launch_tile(const void* A, const void* Bt, const void* bias, void* C,
 hipError_t launch_gemm_bias(const void* A, const void* Bt, const void* bias, void* C, int M, int N,
                             int K, hipStream_t stream) {
   if (N % 192 == 0 && (long)((M + 127) / 128) * (N / 192) >= 160)
-    return launch_tile<128, 192, 2, 2, 3>(A, Bt, bias, C, M, N, K, stream);
+    return launch_tile<128, 192, 2, 2, 4>(A, Bt, bias, C, M, N, K, stream);
   if (N % 128 == 0 && (long)((M + 127) / 128) * (N / 128) >= 160)
     return launch_tile<128, 128, 2, 2, 4>(A, Bt, bias, C, M, N, K, stream);
-  return launch_tile<128, 64, 2, 2, 4>(A, Bt, bias, C, M, N, K, stream);
+  return launch_tile<128, 64, 2, 2, 6>(A, Bt, bias, C, M, N, K, stream);
 }
 
 }  // namespace edda
