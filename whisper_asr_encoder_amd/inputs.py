@@ -236,3 +236,95 @@ def verify_tree_case(trial: int, layer: int, seed: int = 0, n_kv: int | None = N
     q = normal_f16(rng_for(seed, 4, layer, T_Q, trial), (BEAMS, N_HEADS, HEAD_DIM), 1.0)
     return VerifyCase(q=q, k=k, v=v, mask=mask, kind="tree", parents=parents, query_slots=query_slots)
 
+
+
+# --------------------------------------------------------------------------------------
+# The rest of a Whisper-large-v3 encoder around the attention path (pre-norm layer with a
+# GELU MLP, convolutional stem, positional embedding, final LayerNorm). Shapes follow the
+# public Whisper-large-v3 configuration; the pages give none of these tensors.
+# --------------------------------------------------------------------------------------
+
+D_FF = 4 * D_MODEL        # MLP hidden width
+N_MELS = 128              # mel bins of the large-v3 front end
+MEL_FRAMES = 2 * FRAMES_PER_WINDOW  # 3000 mel frames per 30 s window (conv2 halves them)
+
+(T_LN1G, T_LN1B, T_LN2G, T_LN2B, T_W1, T_B1, T_W2, T_B2, T_BO, T_MEL, T_C1W, T_C1B, T_C2W,
+ T_C2B, T_LNPG, T_LNPB) = range(20, 36)
+
+LN_SCALE_VAR = 0.01   # LayerNorm scale 1 + N(0, 0.01); shift N(0, 0.01)
+
+
+@dataclass
+class FullLayerWeights:
+    """Math layout (y = x w): w [in, out]."""
+    ln1_g: np.ndarray
+    ln1_b: np.ndarray
+    w_qkv: np.ndarray      # [1280, 3840]
+    b_qkv: np.ndarray      # [3840], K third zero
+    w_o: np.ndarray        # [1280, 1280]
+    b_o: np.ndarray        # [1280]
+    ln2_g: np.ndarray
+    ln2_b: np.ndarray
+    w_fc1: np.ndarray      # [1280, 5120]
+    b_fc1: np.ndarray      # [5120]
+    w_fc2: np.ndarray      # [5120, 1280]
+    b_fc2: np.ndarray      # [1280]
+
+
+def _ln_params(seed, cfg, layer, tg, tb, d=D_MODEL):
+    g = (1.0 + rng_for(seed, cfg, layer, tg).standard_normal(d) * math.sqrt(LN_SCALE_VAR)).astype(np.float16)
+    b = normal_f16(rng_for(seed, cfg, layer, tb), (d,), LN_SCALE_VAR)
+    return g, b
+
+
+def full_layer_weights(cfg: int, layer: int, seed: int = 0) -> FullLayerWeights:
+    """Attention weights as in encoder_layer_weights (same streams) plus an output bias,
+    two LayerNorms and the MLP: W1 ~ N(0, 1/1280), W2 ~ N(0, 1/5120), biases N(0, 0.02)."""
+    a = encoder_layer_weights(cfg, layer, seed)
+    ln1_g, ln1_b = _ln_params(seed, cfg, layer, T_LN1G, T_LN1B)
+    ln2_g, ln2_b = _ln_params(seed, cfg, layer, T_LN2G, T_LN2B)
+    return FullLayerWeights(
+        ln1_g=ln1_g, ln1_b=ln1_b, w_qkv=a.w_qkv, b_qkv=a.b_qkv, w_o=a.w_o,
+        b_o=normal_f16(rng_for(seed, cfg, layer, T_BO), (D_MODEL,), B_VAR),
+        ln2_g=ln2_g, ln2_b=ln2_b,
+        w_fc1=normal_f16(rng_for(seed, cfg, layer, T_W1), (D_MODEL, D_FF), 1.0 / D_MODEL),
+        b_fc1=normal_f16(rng_for(seed, cfg, layer, T_B1), (D_FF,), B_VAR),
+        w_fc2=normal_f16(rng_for(seed, cfg, layer, T_W2), (D_FF, D_MODEL), 1.0 / D_FF),
+        b_fc2=normal_f16(rng_for(seed, cfg, layer, T_B2), (D_MODEL,), B_VAR))
+
+
+@dataclass
+class StemWeights:
+    conv1_w: np.ndarray   # [1280, 128, 3] (out, in, tap)
+    conv1_b: np.ndarray   # [1280]
+    conv2_w: np.ndarray   # [1280, 1280, 3]
+    conv2_b: np.ndarray   # [1280]
+    pos_emb: np.ndarray   # [1500, 1280]
+    lnp_g: np.ndarray     # final LayerNorm
+    lnp_b: np.ndarray
+
+
+def sinusoidal_positions(length: int, channels: int) -> np.ndarray:
+    """Fixed sinusoidal position table [length, channels]: the first half of the channels
+    holds sin(t * w_i), the second half cos(t * w_i), with w_i = 10000^(-i / (channels/2 - 1))
+    for i = 0 .. channels/2 - 1. Returned in fp16."""
+    half = channels // 2
+    w = np.exp(-math.log(10000.0) * np.arange(half) / (half - 1))
+    t = np.arange(length)[:, None] * w[None, :]
+    return np.concatenate([np.sin(t), np.cos(t)], axis=1).astype(np.float16)
+
+
+def stem_weights(cfg: int = 1, seed: int = 0, frames: int = FRAMES_PER_WINDOW) -> StemWeights:
+    """conv1 ~ N(0, 1/384) (fan-in 3 * 128), conv2 ~ N(0, 1/3840), biases N(0, 0.02)."""
+    lnp_g, lnp_b = _ln_params(seed, cfg, 0, T_LNPG, T_LNPB)
+    return StemWeights(
+        conv1_w=normal_f16(rng_for(seed, cfg, 0, T_C1W), (D_MODEL, N_MELS, 3), 1.0 / (3 * N_MELS)),
+        conv1_b=normal_f16(rng_for(seed, cfg, 0, T_C1B), (D_MODEL,), B_VAR),
+        conv2_w=normal_f16(rng_for(seed, cfg, 0, T_C2W), (D_MODEL, D_MODEL, 3), 1.0 / (3 * D_MODEL)),
+        conv2_b=normal_f16(rng_for(seed, cfg, 0, T_C2B), (D_MODEL,), B_VAR),
+        pos_emb=sinusoidal_positions(frames, D_MODEL), lnp_g=lnp_g, lnp_b=lnp_b)
+
+
+def mel_input(batch: int = 1, cfg: int = 1, seed: int = 0, frames: int = MEL_FRAMES) -> np.ndarray:
+    """Synthetic log-mel input [batch, 128, frames] ~ N(0, 1), fp16 (channel-major per window)."""
+    return normal_f16(rng_for(seed, cfg, 0, T_MEL), (batch, N_MELS, frames), 1.0)
