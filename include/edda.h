@@ -49,6 +49,7 @@ extern "C" {
 #define EDDA_HEAD_DIM 64
 #define EDDA_QKV_COLS (3 * EDDA_D_MODEL)
 #define EDDA_MAX_VERIFY_QUERIES 16
+#define EDDA_D_FF 5120
 /* Leading bytes of the verification workspace that hold its arrival counters. */
 #define EDDA_VERIFY_COUNTER_BYTES 5120
 
@@ -162,6 +163,115 @@ edda_status edda_verify_attn(const void* q, int32_t n_q, const void* k, const vo
  * workgroup each, whose fp32 partial results the last workgroup of each head to finish merges
  * in the same launch: EDDA_VERIFY_COUNTER_BYTES + splits * n_q * 20 * 66 * 4 bytes. */
 size_t edda_verify_workspace_bytes(int32_t n_q, int32_t n_kv);
+
+/* ------------------------------------------------------------------------------------
+ * The rest of the encoder around the attention path. The pages time the whole encoder of
+ * a 30 s window ("audio.cpp PR #1223", encoder commit message) and count its 32 layers
+ * ("BuzzASR/danish discussion #1"); they do not spell out the layer. It follows the public
+ * Whisper-large-v3 architecture: pre-norm residual layers
+ *   x1 = x + Attn(LN1(x)),  y = x1 + GELU(LN2(x1) W1 + b1) W2 + b2   (hidden width 5120),
+ * LayerNorm with eps 1e-5 and the exact GELU x * Phi(x); a stem of two kernel-3 convolutions
+ * (128 mel bins -> 1280, then stride 2) each followed by GELU, plus a positional table.
+ * ------------------------------------------------------------------------------------ */
+
+typedef enum { EDDA_ACT_NONE = 0, EDDA_ACT_GELU = 1 } edda_activation;
+
+/*
+ * Fused linear layer: y = act(x * W + bias) + residual.
+ *
+ *  x            [rows, in_features] fp16.
+ *  w            [out_features, in_features] fp16, output-feature major (Linear layout;
+ *               W = w^T).
+ *  bias         [out_features] fp16 or NULL.
+ *  activation   EDDA_ACT_NONE or EDDA_ACT_GELU (exact, x * Phi(x)), applied before the
+ *               residual is added.
+ *  residual     [residual_rows, out_features] fp16 or NULL; output row r adds residual row
+ *               r % residual_rows (residual_rows = rows for an ordinary residual; a smaller
+ *               period repeats one table, e.g. positions, over stacked windows). It may be
+ *               y itself (in-place residual); it must not overlap y otherwise.
+ *  y            [rows, out_features] fp16; must not overlap x.
+ *  in_features, out_features: multiples of 64; rows >= 1.
+ * One rounding to fp16 at the end (fp32 accumulation, bias, activation and residual).
+ * Errors: EDDA_ERR_INVALID_ARGUMENT (NULL x/w/y, sizes out of range, unknown activation,
+ * residual_rows < 1 when residual is given), EDDA_ERR_UNSUPPORTED (a feature count not a
+ * multiple of 64), EDDA_ERR_MISALIGNED, EDDA_ERR_HIP.
+ */
+edda_status edda_linear(const void* x, int64_t rows, int32_t in_features, const void* w,
+                        int32_t out_features, const void* bias, int32_t activation, const void* residual,
+                        int64_t residual_rows, void* y, void* stream);
+
+/*
+ * LayerNorm over the last dimension: y = (x - mean) / sqrt(var + 1e-5) * gamma + beta with
+ * the biased variance, statistics in fp32.
+ *  x, y         [rows, features] fp16 (y may equal x).
+ *  gamma, beta  [features] fp16.
+ *  features     a multiple of 256, at most 4096 (1280 for this model).
+ * Errors: EDDA_ERR_INVALID_ARGUMENT, EDDA_ERR_UNSUPPORTED (features), EDDA_ERR_MISALIGNED,
+ * EDDA_ERR_HIP.
+ */
+edda_status edda_layer_norm(const void* x, int64_t rows, int32_t features, const void* gamma,
+                            const void* beta, void* y, void* stream);
+
+/* Weights of one encoder layer, all fp16 device pointers, Linear layout ([out, in]). */
+typedef struct {
+  const void* ln1_gamma;  /* [1280] */
+  const void* ln1_beta;   /* [1280] */
+  const void* w_qkv;      /* [3840, 1280], as for edda_qkv_pack */
+  const void* b_qkv;      /* [3840] or NULL */
+  const void* w_o;        /* [1280, 1280] */
+  const void* b_o;        /* [1280] or NULL */
+  const void* ln2_gamma;  /* [1280] */
+  const void* ln2_beta;   /* [1280] */
+  const void* w_fc1;      /* [5120, 1280] */
+  const void* b_fc1;      /* [5120] or NULL */
+  const void* w_fc2;      /* [1280, 5120] */
+  const void* b_fc2;      /* [1280] or NULL */
+} edda_encoder_layer_weights;
+
+/*
+ * One pre-norm encoder layer over `batch` windows of `seq_len` rows:
+ *   h = LN1(x); o = attention(h W_qkv + b_qkv) (as edda_flash_attn, with chunk_len and
+ *   valid_len); x1 = x + o W_o + b_o; y = x1 + GELU(LN2(x1) W1 + b1) W2 + b2.
+ *  x, y       [batch*seq_len, 1280] fp16; y may equal x (in-place layer).
+ *  chunk_len, valid_len: as for edda_encoder_attn.
+ *  weights    host pointer to the layer's weight pointers; every LayerNorm and matrix
+ *             pointer is required, biases may be NULL.
+ *  workspace  at least edda_encoder_layer_workspace_bytes(batch, seq_len) device bytes
+ *             (holds h, QKV / the MLP hidden layer, O, x1); contents on entry ignored.
+ * Errors: as for edda_encoder_attn.
+ */
+edda_status edda_encoder_layer(const void* x, int32_t batch, int32_t seq_len, int32_t chunk_len,
+                               const int32_t* valid_len, const edda_encoder_layer_weights* weights, void* y,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace edda_encoder_layer needs: batch*seq_len*(5120 + 1280 + 1280)*2
+ * (0 if the shape is invalid). */
+size_t edda_encoder_layer_workspace_bytes(int32_t batch, int32_t seq_len);
+
+/*
+ * Convolutional stem: y = GELU(conv2(GELU(conv1(mel)))) + pos, per window.
+ *  mel       [batch, n_mels, n_frames] fp16, channel-major per window (a log-mel
+ *            spectrogram as usually stored).
+ *  conv1_w   [1280, 3 * n_mels] fp16: column tap*n_mels + c holds the weight of input
+ *            channel c at tap (frame t + tap - 1); i.e. a [1280, n_mels, 3] convolution
+ *            weight with its last two axes swapped and flattened.
+ *  conv2_w   [1280, 3 * 1280] likewise; conv2 has stride 2 (frame 2t + tap - 1).
+ *  conv1_b, conv2_b  [1280] fp16 or NULL.
+ *  pos       [(n_frames + 1) / 2, 1280] fp16 positional table, added to every window.
+ *  y         [batch * (n_frames + 1) / 2, 1280] fp16.
+ *  n_mels    a multiple of 64 (128 for large-v3); n_frames >= 1 (3000 for 30 s).
+ *  workspace at least edda_encoder_stem_workspace_bytes(batch, n_mels, n_frames) bytes.
+ * Convolutions use padding 1 (zero frames outside the window).
+ * Errors: EDDA_ERR_INVALID_ARGUMENT, EDDA_ERR_UNSUPPORTED (n_mels), EDDA_ERR_MISALIGNED,
+ * EDDA_ERR_WORKSPACE, EDDA_ERR_HIP.
+ */
+edda_status edda_encoder_stem(const void* mel, int32_t batch, int32_t n_mels, int32_t n_frames,
+                              const void* conv1_w, const void* conv1_b, const void* conv2_w,
+                              const void* conv2_b, const void* pos, void* y, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace edda_encoder_stem needs (0 if the shape is invalid). */
+size_t edda_encoder_stem_workspace_bytes(int32_t batch, int32_t n_mels, int32_t n_frames);
 
 /* Text of the calling thread's most recent error ("" after a successful call). */
 const char* edda_last_error(void);

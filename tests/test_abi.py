@@ -140,3 +140,80 @@ def test_mask_packing_bit_order():
     assert w.shape == (2, 2) and w.dtype == np.uint32
     assert w[0, 0] == (1 | (1 << 5) | (1 << 31)) and w[0, 1] == (1 | (1 << 7))
     assert w[1, 0] == 0xFFFFFFFF and w[1, 1] == 0xFF
+
+
+# ---------------------------------------------------------------------------
+# The rest of the encoder: linear, LayerNorm, encoder layer, stem.
+# ---------------------------------------------------------------------------
+
+def lin(lib, x=A, rows=100, k=1280, w=A, n=1280, bias=None, act=0, res=None, res_rows=0, y=B):
+    return lib.edda_linear(x, rows, k, w, n, bias, act, res, res_rows, y, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(w=None), INVALID), (dict(y=None), INVALID), (dict(rows=0), INVALID),
+    (dict(k=0), INVALID), (dict(n=-64), INVALID), (dict(act=2), INVALID), (dict(res=A, res_rows=0), INVALID),
+    (dict(rows=1 << 30), INVALID), (dict(k=100), UNSUPPORTED), (dict(n=1000), UNSUPPORTED),
+    (dict(x=ODD), MISALIGNED), (dict(y=ODD), MISALIGNED), (dict(bias=ODD), MISALIGNED),
+    (dict(res=ODD, res_rows=10), MISALIGNED),
+])
+def test_linear_rejects(lib, kw, status):
+    assert lin(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(g=None), INVALID), (dict(rows=0), INVALID), (dict(f=1000), UNSUPPORTED),
+    (dict(f=8192), UNSUPPORTED), (dict(x=ODD), MISALIGNED), (dict(b=ODD), MISALIGNED),
+])
+def test_layer_norm_rejects(lib, kw, status):
+    a = dict(x=A, rows=10, f=1280, g=A, b=A, y=B)
+    a.update(kw)
+    assert lib.edda_layer_norm(a["x"], a["rows"], a["f"], a["g"], a["b"], a["y"], None) == status
+
+
+def layer_weights(**over):
+    w = _lib.LayerWeights(*([A] * 12))
+    for k, v in over.items():
+        setattr(w, k, v)
+    return w
+
+
+@pytest.mark.parametrize("kw,wover,status", [
+    (dict(x=None), {}, INVALID), (dict(batch=0), {}, INVALID), (dict(chunk=500), {}, INVALID),
+    (dict(), dict(w_fc1=None), INVALID), (dict(), dict(ln2_gamma=None), INVALID),
+    (dict(), dict(w_o=ODD), MISALIGNED), (dict(y=ODD), {}, MISALIGNED),
+    (dict(ws=None), {}, WORKSPACE), (dict(ws_bytes=200 * 7680 * 2 - 1), {}, WORKSPACE),
+])
+def test_encoder_layer_rejects(lib, kw, wover, status):
+    a = dict(x=A, batch=1, seq=200, chunk=0, y=B, ws=B + (1 << 24), ws_bytes=1 << 30)
+    a.update(kw)
+    w = layer_weights(**wover)
+    assert lib.edda_encoder_layer(a["x"], a["batch"], a["seq"], a["chunk"], None, ctypes.byref(w), a["y"],
+                                  a["ws"], a["ws_bytes"], None) == status
+
+
+def test_encoder_layer_allows_null_biases_in_validation(lib):
+    # Biases may be NULL: with a too-small workspace the call still fails on the workspace only.
+    w = layer_weights(b_qkv=None, b_o=None, b_fc1=None, b_fc2=None)
+    assert lib.edda_encoder_layer(A, 1, 200, 0, None, ctypes.byref(w), B, None, 0, None) == WORKSPACE
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mel=None), INVALID), (dict(pos=None), INVALID), (dict(batch=0), INVALID), (dict(frames=0), INVALID),
+    (dict(mels=100), UNSUPPORTED), (dict(mel=ODD), MISALIGNED), (dict(c1b=ODD), MISALIGNED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=1000), WORKSPACE),
+])
+def test_encoder_stem_rejects(lib, kw, status):
+    a = dict(mel=A, batch=1, mels=128, frames=3000, c1w=A, c1b=None, c2w=A, c2b=None, pos=A, y=B,
+             ws=B + (1 << 24), ws_bytes=1 << 30)
+    a.update(kw)
+    assert lib.edda_encoder_stem(a["mel"], a["batch"], a["mels"], a["frames"], a["c1w"], a["c1b"], a["c2w"],
+                                 a["c2b"], a["pos"], a["y"], a["ws"], a["ws_bytes"], None) == status
+
+
+def test_layer_and_stem_workspace_sizes(lib):
+    assert lib.edda_encoder_layer_workspace_bytes(1, 1500) == 1500 * (5120 + 2 * 1280) * 2
+    assert lib.edda_encoder_layer_workspace_bytes(0, 1500) == 0
+    assert lib.edda_encoder_stem_workspace_bytes(1, 128, 3000) == (3000 * 384 + 3000 * 1280 + 1500 * 3840) * 2
+    assert lib.edda_encoder_stem_workspace_bytes(2, 128, 7) == (14 * 384 + 14 * 1280 + 8 * 3840) * 2
+    assert lib.edda_encoder_stem_workspace_bytes(1, 128, 0) == 0

@@ -1,0 +1,232 @@
+"""GPU parity of the rest of the encoder (LayerNorm, fused linear epilogues, convolutional
+stem, pre-norm layer, whole encoder) against the fp64 oracle, through the C ABI.
+
+Bar: |delta| <= 3e-3 + 1e-3 |ref| per element and relative Frobenius error <= 1e-3, all
+outputs finite. The outputs are fp16 with magnitudes up to ~7 (a residual stream of unit
+variance), and every intermediate the kernels store is fp16: a CPU emulation that rounds
+exactly those intermediates gives, for one layer, max(|delta| - 1e-3 |ref|) = 1.3e-3 and a
+relative Frobenius error of 3.4e-4, so the bar leaves a margin of 2-3x above the rounding
+floor for the fp32-versus-fp64 accumulation order.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle.encoder_layer as L
+from whisper_asr_encoder_amd import _lib
+from whisper_asr_encoder_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL, REL_FRO = 3e-3, 1e-3, 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def check(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    excess = np.abs(got - ref) - (ATOL + RTOL * np.abs(ref))
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    say(f"  {what}: max|d| {np.abs(got - ref).max():.3e}  worst excess {excess.max():.3e}  rel_fro {rel:.3e}")
+    assert excess.max() <= 0, f"{what}: |delta| beyond 3e-3 + 1e-3|ref| by {excess.max():.3e}"
+    assert rel <= REL_FRO, f"{what}: relative Frobenius error {rel:.3e}"
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.load()
+    return t
+
+
+def dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy()
+
+
+def nan_like(torch, shape):
+    return torch.full(shape, float("nan"), dtype=torch.float16, device="cuda")
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,features", [(1, 1280), (7, 1280), (1500, 1280), (33, 256), (33, 4096), (5, 768)])
+def test_layer_norm(torch, rows, features):
+    say(f"layer_norm rows={rows} features={features}")
+    r = np.random.default_rng(rows * 7 + features)
+    x = (r.standard_normal((rows, features)) * 1.7 + 0.6).astype(np.float16)
+    g = (1 + r.standard_normal(features) * 0.1).astype(np.float16)
+    b = (r.standard_normal(features) * 0.1).astype(np.float16)
+    y = nan_like(torch, (rows, features))
+    _lib.edda_layer_norm(dev(torch, x), dev(torch, g), dev(torch, b), y)
+    torch.cuda.synchronize()
+    check(host(y), L.layer_norm(x, g, b), "y")
+
+
+# ---------------------------------------------------------------------------
+# Fused linear layer
+# ---------------------------------------------------------------------------
+
+LINEAR_CASES = [
+    # rows, in, out, act, bias, residual period (0 = none, -1 = in place), name
+    (200, 1280, 5120, 1, True, 0, "fc1 shape, GELU"),
+    (300, 1280, 1280, 0, True, 300, "output projection + residual"),
+    (1500, 5120, 1280, 0, True, 1500, "fc2 at a full window + residual"),
+    (131, 384, 1280, 1, True, 0, "conv1 shape, GELU, ragged rows"),
+    (300, 3840, 1280, 1, True, 150, "conv2 shape, GELU + a 150-row table over two windows"),
+    (100, 1280, 1280, 0, False, -1, "no bias, residual in place"),
+    (64, 1280, 3840, 0, True, 0, "QKV shape, 64 rows"),
+]
+
+
+@pytest.mark.parametrize("rows,k,n,act,with_bias,res,name", LINEAR_CASES)
+def test_linear(torch, rows, k, n, act, with_bias, res, name):
+    say(f"linear {name}: rows={rows} in={k} out={n}")
+    r = np.random.default_rng(rows + k + n + act)
+    x = r.standard_normal((rows, k)).astype(np.float16)
+    w = (r.standard_normal((k, n)) / np.sqrt(k)).astype(np.float16)
+    b = (r.standard_normal(n) * 0.1).astype(np.float16) if with_bias else None
+    ref = L.linear(x, w, b)
+    if act:
+        ref = L.gelu(ref)
+    y = nan_like(torch, (rows, n))
+    residual, rrows = None, None
+    if res > 0:
+        table = r.standard_normal((res, n)).astype(np.float16)
+        residual, rrows = dev(torch, table), res
+        ref = ref + table.astype(np.float64)[np.arange(rows) % res]
+    elif res == -1:
+        start = r.standard_normal((rows, n)).astype(np.float16)
+        y = dev(torch, start)
+        residual, rrows = y, rows
+        ref = ref + start.astype(np.float64)
+    _lib.edda_linear(dev(torch, x), dev(torch, _lib.linear_layout(w)), None if b is None else dev(torch, b), y,
+                     activation=act, residual=residual, residual_rows=rrows)
+    torch.cuda.synchronize()
+    check(host(y), ref, "y")
+
+
+# ---------------------------------------------------------------------------
+# Convolutional stem
+# ---------------------------------------------------------------------------
+
+def run_stem(torch, mel, sw, frames):
+    batch = mel.shape[0]
+    t2 = (frames - 1) // 2 + 1
+    y = nan_like(torch, (batch * t2, 1280))
+    ws = torch.empty(_lib.encoder_stem_workspace_bytes(batch, mel.shape[1], frames), dtype=torch.uint8, device="cuda")
+    _lib.edda_encoder_stem(dev(torch, mel), dev(torch, _lib.conv_layout(sw.conv1_w)), dev(torch, sw.conv1_b),
+                           dev(torch, _lib.conv_layout(sw.conv2_w)), dev(torch, sw.conv2_b),
+                           dev(torch, sw.pos_emb[:t2]), y, ws)
+    torch.cuda.synchronize()
+    return host(y).reshape(batch, t2, 1280)
+
+
+@pytest.mark.parametrize("batch,frames", [(2, 64), (1, 37), (1, 3000)])
+def test_stem(torch, batch, frames):
+    say(f"stem batch={batch} frames={frames}")
+    sw = I.stem_weights(frames=(frames - 1) // 2 + 1)
+    mel = I.mel_input(batch, frames=frames)
+    got = run_stem(torch, mel, sw, frames)
+    for b in range(batch):
+        check(got[b], L.encoder_stem(mel[b], sw.conv1_w, sw.conv1_b, sw.conv2_w, sw.conv2_b, sw.pos_emb), f"window {b}")
+
+
+# ---------------------------------------------------------------------------
+# Pre-norm encoder layer
+# ---------------------------------------------------------------------------
+
+def make_encoder(torch, layers, batch, seq_len, chunk_len, valid_len, stem=None):
+    from whisper_asr_encoder_amd.encoder import FullEncoder
+    return FullEncoder(layers, stem=stem, batch=batch, seq_len=seq_len, chunk_len=chunk_len,
+                       valid_len=valid_len)
+
+
+@pytest.mark.parametrize("batch,seq_len,chunk_len,valid", [
+    (1, 200, 0, None), (1, 400, 200, [350]), (2, 300, 0, [300, 170]), (1, 33, 0, None)])
+def test_encoder_layer_small(torch, batch, seq_len, chunk_len, valid):
+    say(f"encoder layer batch={batch} seq_len={seq_len} chunk={chunk_len} valid={valid}")
+    w = I.full_layer_weights(1, 3)
+    enc = make_encoder(torch, [w], batch, seq_len, chunk_len, valid)
+    x = I.encoder_workload(1, batch=batch, seq_len=seq_len, layers=1).x
+    y = nan_like(torch, x.shape)
+    enc.layer(dev(torch, x), 0, y)
+    torch.cuda.synchronize()
+    ref = L.encoder_layer(x, w, batch, seq_len, chunk_len, seq_len if valid is None else valid, 20)
+    check(host(y), ref["y"], "y")
+
+
+def test_encoder_layer_full_window_sampled_rows(torch):
+    say("encoder layer, one 30 s window (1500 rows), 160 sampled rows")
+    w = I.full_layer_weights(1, 31)
+    enc = make_encoder(torch, [w], 1, 1500, 0, None)
+    x = I.encoder_workload(1, layers=1).x
+    y = nan_like(torch, x.shape)
+    enc.layer(dev(torch, x), 0, y)
+    torch.cuda.synchronize()
+    got = host(y)
+    assert np.isfinite(got).all()
+    rows = np.unique(np.concatenate([np.arange(0, 1500, 13), [1, 127, 128, 1499]]))
+    ref = L.encoder_layer(x, w, 1, 1500, 0, 1500, 20, rows=rows)
+    check(got[rows], ref["y"], "sampled rows")
+
+
+def test_encoder_layer_in_place_matches(torch):
+    say("encoder layer in place (y = x) equals out of place")
+    w = I.full_layer_weights(1, 5)
+    enc = make_encoder(torch, [w], 1, 200, 0, None)
+    x = dev(torch, I.encoder_workload(1, seq_len=200, layers=1).x)
+    y = nan_like(torch, tuple(x.shape))
+    enc.layer(x, 0, y)
+    xi = x.clone()
+    enc.layer(xi, 0, xi)
+    torch.cuda.synchronize()
+    assert torch.equal(xi, y)
+
+
+def test_full_encoder_small(torch):
+    """Stem -> 2 layers -> final LayerNorm; each stage is compared with the oracle applied to
+    the GPU's own input to that stage, and the whole chain end to end."""
+    say("full encoder: stem (400 mel frames) + 2 layers + final LayerNorm")
+    seq = 200
+    sw = I.stem_weights(frames=seq)
+    layers = [I.full_layer_weights(1, l) for l in range(2)]
+    enc = make_encoder(torch, layers, 1, seq, 0, None, stem=sw)
+    mel = I.mel_input(1, frames=2 * seq)
+    out = nan_like(torch, (seq, 1280))
+    enc.forward(dev(torch, mel), out)
+    torch.cuda.synchronize()
+    # Stage by stage from the GPU's intermediate values.
+    xs = nan_like(torch, (seq, 1280))
+    enc.stem(dev(torch, mel), xs)
+    torch.cuda.synchronize()
+    cur = host(xs)
+    check(cur, L.encoder_stem(mel[0], sw.conv1_w, sw.conv1_b, sw.conv2_w, sw.conv2_b, sw.pos_emb), "stem")
+    for l, w in enumerate(layers):
+        y = nan_like(torch, (seq, 1280))
+        enc.layer(dev(torch, cur.astype(np.float16)), l, y)
+        torch.cuda.synchronize()
+        nxt = host(y)
+        check(nxt, L.encoder_layer(cur.astype(np.float16), w, 1, seq, 0, seq, 20)["y"], f"layer {l}")
+        cur = nxt
+    check(host(out), L.layer_norm(cur.astype(np.float16), sw.lnp_g, sw.lnp_b), "final LayerNorm")
+    # End to end against the oracle chain in fp64.
+    ref = L.encoder_stem(mel[0], sw.conv1_w, sw.conv1_b, sw.conv2_w, sw.conv2_b, sw.pos_emb)
+    for w in layers:
+        ref = L.encoder_layer(ref, w, 1, seq, 0, seq, 20)["y"]
+    ref = L.layer_norm(ref, sw.lnp_g, sw.lnp_b)
+    check(host(out), ref, "end to end")

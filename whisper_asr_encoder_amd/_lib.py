@@ -28,7 +28,19 @@ STATUS = {0: "EDDA_OK", 1: "EDDA_ERR_INVALID_ARGUMENT", 2: "EDDA_ERR_UNSUPPORTED
 
 # Every symbol include/edda.h declares.
 EXPORTS = ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_encoder_workspace_bytes", "edda_verify_attn",
-           "edda_verify_workspace_bytes", "edda_last_error", "edda_version")
+           "edda_verify_workspace_bytes", "edda_linear", "edda_layer_norm", "edda_encoder_layer",
+           "edda_encoder_layer_workspace_bytes", "edda_encoder_stem", "edda_encoder_stem_workspace_bytes",
+           "edda_last_error", "edda_version")
+
+D_FF = 5120
+ACT_NONE, ACT_GELU = 0, 1
+
+
+class LayerWeights(ctypes.Structure):
+    """edda_encoder_layer_weights: device pointers (Linear layout)."""
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_gamma", "ln2_beta",
+        "w_fc1", "b_fc1", "w_fc2", "b_fc2")]
 
 
 class EddaError(RuntimeError):
@@ -58,9 +70,19 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edda_verify_attn.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.edda_verify_workspace_bytes.argtypes = [i32, i32]
     lib.edda_verify_workspace_bytes.restype = sz
+    lib.edda_linear.argtypes = [vp, i64, i32, vp, i32, vp, i32, vp, i64, vp, vp]
+    lib.edda_layer_norm.argtypes = [vp, i64, i32, vp, vp, vp, vp]
+    lib.edda_encoder_layer.argtypes = [vp, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(LayerWeights), vp,
+                                       vp, sz, vp]
+    lib.edda_encoder_layer_workspace_bytes.argtypes = [i32, i32]
+    lib.edda_encoder_layer_workspace_bytes.restype = sz
+    lib.edda_encoder_stem.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.edda_encoder_stem_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.edda_encoder_stem_workspace_bytes.restype = sz
     lib.edda_last_error.restype = ctypes.c_char_p
     lib.edda_version.restype = ctypes.c_char_p
-    for name in ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_verify_attn"):
+    for name in ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_verify_attn", "edda_linear",
+                 "edda_layer_norm", "edda_encoder_layer", "edda_encoder_stem"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -108,6 +130,13 @@ def linear_layout(w_in_out: np.ndarray) -> np.ndarray:
     """Weight packing: a [in, out] matrix W (y = x W) -> its output-feature-major
     copy [out, in] (the layout the library reads; rows of a stacked q/k/v Linear weight)."""
     return np.ascontiguousarray(np.asarray(w_in_out, dtype=np.float16).T)
+
+
+def conv_layout(w_out_in_tap: np.ndarray) -> np.ndarray:
+    """Convolution weight [out, in, 3] -> [out, 3*in] with column tap*in + c (the layout of
+    the stem's column-gathered GEMM)."""
+    w = np.asarray(w_out_in_tap, dtype=np.float16)
+    return np.ascontiguousarray(w.transpose(0, 2, 1).reshape(w.shape[0], -1))
 
 
 def pack_mask_rows(mask: np.ndarray) -> np.ndarray:
@@ -201,3 +230,76 @@ def edda_verify_attn(q, k, v, mask_rows, o, workspace=None, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.edda_verify_attn(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, _ptr(mask_rows), _ptr(o),
                                 _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def edda_linear(x, w, bias, y, activation=ACT_NONE, residual=None, residual_rows=None, stream=None):
+    """y[rows, out] = act(x[rows, in] * w^T + bias) + residual[row % residual_rows]; w is [out, in]."""
+    lib = load()
+    torch = _require(x, "x")
+    rows, k = x.shape
+    n = w.shape[0]
+    _require(x, "x", (rows, k), torch.float16)
+    _require(w, "w", (n, k), torch.float16)
+    if bias is not None:
+        _require(bias, "bias", (n,), torch.float16)
+    _require(y, "y", (rows, n), torch.float16)
+    if residual is not None:
+        residual_rows = residual.shape[0] if residual_rows is None else residual_rows
+        _require(residual, "residual", (residual.shape[0], n), torch.float16)
+        if residual.shape[0] < min(residual_rows, rows):
+            raise ValueError("residual has fewer rows than residual_rows")
+    _check(lib.edda_linear(_ptr(x), rows, k, _ptr(w), n, _ptr(bias), activation, _ptr(residual),
+                           residual_rows or 0, _ptr(y), _stream(stream)))
+
+
+def edda_layer_norm(x, gamma, beta, y, stream=None):
+    lib = load()
+    torch = _require(x, "x")
+    rows, f = x.shape
+    _require(x, "x", (rows, f), torch.float16)
+    _require(gamma, "gamma", (f,), torch.float16)
+    _require(beta, "beta", (f,), torch.float16)
+    _require(y, "y", (rows, f), torch.float16)
+    _check(lib.edda_layer_norm(_ptr(x), rows, f, _ptr(gamma), _ptr(beta), _ptr(y), _stream(stream)))
+
+
+def encoder_layer_workspace_bytes(batch: int, seq_len: int) -> int:
+    return int(load().edda_encoder_layer_workspace_bytes(batch, seq_len))
+
+
+def edda_encoder_layer(x, batch, seq_len, chunk_len, valid_len, weights: "LayerWeights", y, workspace,
+                       stream=None):
+    """One pre-norm encoder layer; weights: a LayerWeights of device pointers (kept alive by the caller)."""
+    lib = load()
+    torch = _require(x, "x")
+    rows = batch * seq_len
+    _require(x, "x", (rows, D_MODEL), torch.float16)
+    _require(y, "y", (rows, D_MODEL), torch.float16)
+    vl = None
+    if valid_len is not None:
+        arr = (ctypes.c_int32 * batch)(*[int(v) for v in valid_len])
+        vl = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.edda_encoder_layer(_ptr(x), batch, seq_len, chunk_len, vl, ctypes.byref(weights), _ptr(y),
+                                  _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def encoder_stem_workspace_bytes(batch: int, n_mels: int, n_frames: int) -> int:
+    return int(load().edda_encoder_stem_workspace_bytes(batch, n_mels, n_frames))
+
+
+def edda_encoder_stem(mel, conv1_w, conv1_b, conv2_w, conv2_b, pos, y, workspace, stream=None):
+    """mel [batch, n_mels, n_frames] -> y [batch * ((n_frames + 1) // 2), 1280]; conv weights in
+    conv_layout ([1280, 3 * in])."""
+    lib = load()
+    torch = _require(mel, "mel")
+    batch, n_mels, n_frames = mel.shape
+    t2 = (n_frames - 1) // 2 + 1
+    _require(mel, "mel", (batch, n_mels, n_frames), torch.float16)
+    _require(conv1_w, "conv1_w", (D_MODEL, 3 * n_mels), torch.float16)
+    _require(conv2_w, "conv2_w", (D_MODEL, 3 * D_MODEL), torch.float16)
+    _require(pos, "pos", (t2, D_MODEL), torch.float16)
+    _require(y, "y", (batch * t2, D_MODEL), torch.float16)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.edda_encoder_stem(_ptr(mel), batch, n_mels, n_frames, _ptr(conv1_w), _ptr(conv1_b), _ptr(conv2_w),
+                                 _ptr(conv2_b), _ptr(pos), _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)))

@@ -38,6 +38,9 @@ edda_status from_hip(hipError_t e, const char* what) {
 
 constexpr int64_t kMaxRows = (int64_t)1 << 31;
 
+// The GEMM's tile map handles fewer than 65536 tiles (128 rows by at least 64 columns).
+bool gemm_tiles_ok(int64_t rows, int64_t n) { return ((rows + 127) / 128) * (n / 64) < 65536; }
+
 }  // namespace
 
 extern "C" {
@@ -142,6 +145,160 @@ edda_status edda_verify_attn(const void* q, int32_t n_q, const void* k, const vo
   return from_hip(edda::launch_verify(q, n_q, k, v, n_kv, mask_rows, o, workspace,
                                       static_cast<hipStream_t>(stream)),
                   "edda_verify_attn launch");
+}
+
+
+// ---------------------------------------------------------------------------------------
+// The rest of the encoder: fused linear layers, LayerNorm, the pre-norm layer, the stem.
+// ---------------------------------------------------------------------------------------
+
+edda_status edda_linear(const void* x, int64_t rows, int32_t in_features, const void* w, int32_t out_features,
+                        const void* bias, int32_t activation, const void* residual, int64_t residual_rows,
+                        void* y, void* stream) {
+  if (!x || !w || !y) return fail(EDDA_ERR_INVALID_ARGUMENT, "edda_linear: x, w and y must be non-null");
+  if (rows < 1 || in_features < 1 || out_features < 1)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "edda_linear: rows, in_features and out_features must be >= 1");
+  if (activation != EDDA_ACT_NONE && activation != EDDA_ACT_GELU)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "edda_linear: unknown activation %d", activation);
+  if (residual && residual_rows < 1)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "edda_linear: residual_rows = %lld must be >= 1", (long long)residual_rows);
+  if (in_features % 64 || out_features % 64)
+    return fail(EDDA_ERR_UNSUPPORTED, "edda_linear: in_features = %d and out_features = %d must be multiples of 64",
+                in_features, out_features);
+  const int64_t width = in_features > out_features ? in_features : out_features;
+  if (rows >= kMaxRows / width || (residual && residual_rows >= kMaxRows / out_features) ||
+      !gemm_tiles_ok(rows, out_features))
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "edda_linear: rows = %lld too large", (long long)rows);
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || (bias && !aligned(bias, 16)) ||
+      (residual && !aligned(residual, 16)))
+    return fail(EDDA_ERR_MISALIGNED, "edda_linear: pointers must be 16-byte aligned");
+  return from_hip(edda::launch_gemm(x, w, bias, residual, residual ? (int)residual_rows : 1, activation, y,
+                                    (int)rows, out_features, in_features, static_cast<hipStream_t>(stream)),
+                  "edda_linear launch");
+}
+
+edda_status edda_layer_norm(const void* x, int64_t rows, int32_t features, const void* gamma, const void* beta,
+                            void* y, void* stream) {
+  if (!x || !gamma || !beta || !y)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "edda_layer_norm: x, gamma, beta and y must be non-null");
+  if (rows < 1 || features < 1)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "edda_layer_norm: rows and features must be >= 1");
+  if (features % 256 || features > 4096)
+    return fail(EDDA_ERR_UNSUPPORTED, "edda_layer_norm: features = %d must be a multiple of 256, at most 4096",
+                features);
+  if (rows >= kMaxRows / features) return fail(EDDA_ERR_INVALID_ARGUMENT, "edda_layer_norm: rows too large");
+  if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(beta, 16) || !aligned(y, 16))
+    return fail(EDDA_ERR_MISALIGNED, "edda_layer_norm: pointers must be 16-byte aligned");
+  return from_hip(edda::launch_layer_norm(x, (int)rows, features, gamma, beta, y, static_cast<hipStream_t>(stream)),
+                  "edda_layer_norm launch");
+}
+
+size_t edda_encoder_layer_workspace_bytes(int32_t batch, int32_t seq_len) {
+  if (batch < 1 || seq_len < 1) return 0;
+  const int64_t rows = (int64_t)batch * seq_len;
+  if (rows >= kMaxRows / EDDA_D_FF) return 0;
+  return (size_t)rows * (EDDA_D_FF + 2 * EDDA_D_MODEL) * 2;
+}
+
+edda_status edda_encoder_layer(const void* x, int32_t batch, int32_t seq_len, int32_t chunk_len,
+                               const int32_t* valid_len, const edda_encoder_layer_weights* wt, void* y,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "edda_encoder_layer";
+  if (!x || !wt || !y) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: x, weights and y must be non-null", fn);
+  const void* required[] = {wt->ln1_gamma, wt->ln1_beta, wt->w_qkv, wt->w_o, wt->ln2_gamma, wt->ln2_beta,
+                            wt->w_fc1, wt->w_fc2};
+  for (const void* p : required)
+    if (!p) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: every LayerNorm and weight-matrix pointer is required", fn);
+  edda_status st = check_encoder_shape(fn, batch, seq_len, chunk_len, valid_len);
+  if (st != EDDA_OK) return st;
+  const int64_t rows = (int64_t)batch * seq_len;
+  if (rows >= kMaxRows / EDDA_D_FF || !gemm_tiles_ok(rows, EDDA_D_FF))
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: batch*seq_len = %lld too large", fn, (long long)rows);
+  const void* all[] = {x, y, workspace, wt->ln1_gamma, wt->ln1_beta, wt->w_qkv, wt->b_qkv, wt->w_o, wt->b_o,
+                       wt->ln2_gamma, wt->ln2_beta, wt->w_fc1, wt->b_fc1, wt->w_fc2, wt->b_fc2};
+  for (const void* p : all)
+    if (p && !aligned(p, 16)) return fail(EDDA_ERR_MISALIGNED, "%s: pointers must be 16-byte aligned", fn);
+  const size_t need = edda_encoder_layer_workspace_bytes(batch, seq_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(EDDA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  // Workspace: big [rows, 5120] (QKV, later the MLP hidden layer), h [rows, 1280] (LN1 out,
+  // then O, then LN2 out), x1 [rows, 1280].
+  char* big = static_cast<char*>(workspace);
+  char* h = big + rows * EDDA_D_FF * 2;
+  char* x1 = h + rows * EDDA_D_MODEL * 2;
+  const int m = (int)rows;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if ((e = edda::launch_layer_norm(x, m, EDDA_D_MODEL, wt->ln1_gamma, wt->ln1_beta, h, s)) != hipSuccess)
+    return from_hip(e, "edda_encoder_layer LN1 launch");
+  if ((e = edda::launch_gemm(h, wt->w_qkv, wt->b_qkv, nullptr, 1, EDDA_ACT_NONE, big, m, EDDA_QKV_COLS,
+                             EDDA_D_MODEL, s)) != hipSuccess)
+    return from_hip(e, "edda_encoder_layer QKV launch");
+  if ((e = edda::launch_flash_attn(big, h, batch, seq_len, chunk_len, valid_len, s)) != hipSuccess)
+    return from_hip(e, "edda_encoder_layer attention launch");
+  if ((e = edda::launch_gemm(h, wt->w_o, wt->b_o, x, m, EDDA_ACT_NONE, x1, m, EDDA_D_MODEL, EDDA_D_MODEL, s)) !=
+      hipSuccess)
+    return from_hip(e, "edda_encoder_layer output-projection launch");
+  if ((e = edda::launch_layer_norm(x1, m, EDDA_D_MODEL, wt->ln2_gamma, wt->ln2_beta, h, s)) != hipSuccess)
+    return from_hip(e, "edda_encoder_layer LN2 launch");
+  if ((e = edda::launch_gemm(h, wt->w_fc1, wt->b_fc1, nullptr, 1, EDDA_ACT_GELU, big, m, EDDA_D_FF, EDDA_D_MODEL,
+                             s)) != hipSuccess)
+    return from_hip(e, "edda_encoder_layer fc1 launch");
+  return from_hip(edda::launch_gemm(big, wt->w_fc2, wt->b_fc2, x1, m, EDDA_ACT_NONE, y, m, EDDA_D_MODEL, EDDA_D_FF, s),
+                  "edda_encoder_layer fc2 launch");
+}
+
+namespace {
+int64_t stem_frames_out(int32_t n_frames) { return (int64_t)(n_frames - 1) / 2 + 1; }
+}  // namespace
+
+size_t edda_encoder_stem_workspace_bytes(int32_t batch, int32_t n_mels, int32_t n_frames) {
+  if (batch < 1 || n_mels < 1 || n_frames < 1) return 0;
+  const int64_t r1 = (int64_t)batch * n_frames, r2 = (int64_t)batch * stem_frames_out(n_frames);
+  if (r1 >= kMaxRows / (3 * EDDA_D_MODEL) || (int64_t)n_mels * 3 >= kMaxRows / r1 ||
+      !gemm_tiles_ok(r1, EDDA_D_MODEL))
+    return 0;
+  return (size_t)(r1 * 3 * n_mels + r1 * EDDA_D_MODEL + r2 * 3 * EDDA_D_MODEL) * 2;
+}
+
+edda_status edda_encoder_stem(const void* mel, int32_t batch, int32_t n_mels, int32_t n_frames,
+                              const void* conv1_w, const void* conv1_b, const void* conv2_w, const void* conv2_b,
+                              const void* pos, void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "edda_encoder_stem";
+  if (!mel || !conv1_w || !conv2_w || !pos || !y)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: mel, conv1_w, conv2_w, pos and y must be non-null", fn);
+  if (batch < 1 || n_mels < 1 || n_frames < 1)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: batch, n_mels and n_frames must be >= 1", fn);
+  if (n_mels % 64) return fail(EDDA_ERR_UNSUPPORTED, "%s: n_mels = %d must be a multiple of 64", fn, n_mels);
+  const size_t need = edda_encoder_stem_workspace_bytes(batch, n_mels, n_frames);
+  if (need == 0) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: batch * n_frames too large", fn);
+  const void* all[] = {mel, conv1_w, conv1_b, conv2_w, conv2_b, pos, y, workspace};
+  for (const void* p : all)
+    if (p && !aligned(p, 16)) return fail(EDDA_ERR_MISALIGNED, "%s: pointers must be 16-byte aligned", fn);
+  if (!workspace || workspace_bytes < need)
+    return fail(EDDA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  const int64_t t2 = stem_frames_out(n_frames);
+  const int64_t r1 = (int64_t)batch * n_frames, r2 = (int64_t)batch * t2;
+  char* cols1 = static_cast<char*>(workspace);
+  char* h1 = cols1 + r1 * 3 * n_mels * 2;
+  char* cols2 = h1 + r1 * EDDA_D_MODEL * 2;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  // Frame t, channel c of window b sits at mel[b][c][t].
+  if ((e = edda::launch_im2col3(mel, batch, (long)n_mels * n_frames, n_frames, n_mels, 1, n_frames, 1, cols1, s)) !=
+      hipSuccess)
+    return from_hip(e, "edda_encoder_stem column gather (conv1) launch");
+  if ((e = edda::launch_gemm(cols1, conv1_w, conv1_b, nullptr, 1, EDDA_ACT_GELU, h1, (int)r1, EDDA_D_MODEL,
+                             3 * n_mels, s)) != hipSuccess)
+    return from_hip(e, "edda_encoder_stem conv1 launch");
+  if ((e = edda::launch_im2col3(h1, batch, (long)n_frames * EDDA_D_MODEL, n_frames, EDDA_D_MODEL, EDDA_D_MODEL, 1, 2,
+                                cols2, s)) != hipSuccess)
+    return from_hip(e, "edda_encoder_stem column gather (conv2) launch");
+  return from_hip(edda::launch_gemm(cols2, conv2_w, conv2_b, pos, (int)t2, EDDA_ACT_GELU, y, (int)r2, EDDA_D_MODEL,
+                                    3 * EDDA_D_MODEL, s),
+                  "edda_encoder_stem conv2 launch");
 }
 
 }  // extern "C"

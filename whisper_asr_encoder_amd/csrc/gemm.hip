@@ -1,11 +1,13 @@
-// Kernel 1: fp16 GEMM with bias on gfx950 matrix cores, used for the packed QKV
-// projection (N = 3840) and the attention output projection (N = 1280).
+// Kernel 1: fp16 GEMM on gfx950 matrix cores with a fused epilogue, used for the packed
+// QKV projection (N = 3840), the attention output projection (N = 1280), the MLP
+// (N = 5120 with GELU, N = 1280 with the residual) and the convolutional stem.
 //
-// C[M, N] = A[M, K] * Bt[N, K]^T + bias[N].  A (activations) and Bt (weights in
-// output-feature-major "Linear" layout) are both K-contiguous, so a 16-byte LDS
-// read yields one MFMA operand fragment with no transpose.  The MFMA computes
-// C^T tiles (weights as the A operand); fp32 accumulation, bias added in fp32,
-// one round-to-nearest-even to fp16.
+// C[M, N] = act(A[M, K] * Bt[N, K]^T + bias[N]) + residual[m % period, N].  A
+// (activations) and Bt (weights in output-feature-major "Linear" layout) are both
+// K-contiguous, so a 16-byte LDS read yields one MFMA operand fragment with no
+// transpose.  The MFMA computes C^T tiles (weights as the A operand); fp32
+// accumulation, the epilogue in fp32 (act: none or the exact GELU x * Phi(x)), one
+// round-to-nearest-even to fp16.
 //
 // Data movement (one workgroup per BM x BN tile, K step BK = 64): 4 compute waves
 // issue the MFMAs and 4 producer waves (one of each per SIMD) the global -> LDS copies.
@@ -25,8 +27,11 @@
 //    The DMA is issued from inline asm and waited for with explicit vmcnt counts.
 //  * LDS -> registers: the fragments of k16 step s+1 are read while the MFMAs of
 //    step s run (one read slotted after each MFMA), double-buffered in VGPRs.
-//  * epilogue: accumulators (+ bias, fp16) are staged through LDS and written back
-//    as full rows with 16-byte stores, instead of 8-byte pieces of 32 rows.
+//  * epilogue: bias and residual values are loaded at kernel start in the accumulator
+//    layout; the results (fp16) are staged through LDS and written back as full rows
+//    with 16-byte stores, instead of 8-byte pieces of 32 rows.  Every residual element
+//    a workgroup reads belongs to its own tile and is read before any store, so the
+//    residual may be the output buffer itself.
 // Workgroups are mapped to tiles XCD-aware: workgroup w runs on XCD w % 8, and each
 // XCD gets one rectangular region of the output (the 8 regions chosen to minimise the
 // A and B bytes the eight L2s fetch), so operands are fetched once per region.  Rows of A beyond M are fetched from row M-1
@@ -99,12 +104,22 @@ struct TileMap {
   uint64_t inv[kXcds];
 };
 
+// Fused epilogue: bias [N] or null; residual [*, N] (row m reads row m % res_period) or
+// null; act 0 = none, 1 = GELU (applied before the residual).
+struct Epilogue {
+  const f16* bias;
+  const f16* residual;
+  int res_period;
+  int act;
+};
+
+__device__ __forceinline__ float gelu_exact(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+
 template <int BM, int BN, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __restrict__ A,
                                                                  const f16* __restrict__ Bt,
-                                                                 const f16* __restrict__ bias,
-                                                                 f16* __restrict__ C, int M, int N,
-                                                                 int K, TileMap map) {
+                                                                 f16* C, int M, int N, int K,
+                                                                 TileMap map, Epilogue ep) {
   static_assert(WM * WN == kComputeWaves, "wave grid must use the compute waves");
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -205,19 +220,40 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
   for (int s = 0; s < kKSteps; ++s) frag_off[s] = l32 * kRowBytes + (((2 * s + g) ^ swz(l32)) << 4);
 
   // Bias values of this lane's output columns, loaded now so the epilogue does not wait.
-  // One uniform branch around all of the loads, so they are in flight together.
+  // One uniform branch around each group of loads, so they are in flight together.
   f16x4 bias_v[FN][4];
-  if (bias) {
+  if (ep.bias) {
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        bias_v[fn][i] = *reinterpret_cast<const f16x4*>(bias + n0 + wn * WTN + 32 * fn + 8 * i + 4 * g);
+        bias_v[fn][i] = *reinterpret_cast<const f16x4*>(ep.bias + n0 + wn * WTN + 32 * fn + 8 * i + 4 * g);
   } else {
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
       for (int i = 0; i < 4; ++i) bias_v[fn][i] = (f16x4){};
+  }
+  // Residual values of this lane's outputs (row m0 + wm*WTM + 32 fm + l32, 4 columns);
+  // rows past M read row M-1 and are never stored.
+  f16x4 res_v[FN][4][FM];
+  if (ep.residual) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int m = min(m0 + wm * WTM + 32 * fm + l32, M - 1) % ep.res_period;
+      const f16* rrow = ep.residual + (size_t)m * N + n0 + wn * WTN + 4 * g;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) res_v[fn][i][fm] = *reinterpret_cast<const f16x4*>(rrow + 32 * fn + 8 * i);
+    }
+  } else {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) res_v[fn][i][fm] = (f16x4){};
   }
 
   f32x16 acc[FN][FM];
@@ -295,7 +331,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
   first_steps(nk - 1);
   mfmas(S1());
 
-  // Epilogue: bias, fp16, stage the tile in LDS, then coalesced 16-byte row stores.
+  // Epilogue: bias, activation, residual, fp16; stage the tile in LDS, then coalesced
+  // 16-byte row stores.
   // Only the compute waves are left (the producers ended after the K loop, which a
   // workgroup barrier no longer waits for).
   wait_lds_reads();
@@ -310,8 +347,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const int ml = wm * WTM + 32 * fm + l32;
-        const f16x2 lo = pack_rne(acc[fn][fm][4 * i + 0] + (float)bb[0], acc[fn][fm][4 * i + 1] + (float)bb[1]);
-        const f16x2 hi = pack_rne(acc[fn][fm][4 * i + 2] + (float)bb[2], acc[fn][fm][4 * i + 3] + (float)bb[3]);
+        const f16x4 rr = res_v[fn][i][fm];
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[j] = acc[fn][fm][4 * i + j] + (float)bb[j];
+          if (ep.act) v[j] = gelu_exact(v[j]);
+          v[j] += (float)rr[j];
+        }
+        const f16x2 lo = pack_rne(v[0], v[1]);
+        const f16x2 hi = pack_rne(v[2], v[3]);
         *reinterpret_cast<f16x4*>(cs + ml * kCld + nl) = (f16x4){lo[0], lo[1], hi[0], hi[1]};
       }
     }
@@ -328,7 +373,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES>
-hipError_t launch_tile(const void* A, const void* Bt, const void* bias, void* C, int M, int N, int K,
+hipError_t launch_tile(const void* A, const void* Bt, void* C, int M, int N, int K, const Epilogue& ep,
                        hipStream_t stream) {
   const int mt = (M + BM - 1) / BM, nt = N / BN;
   // XCD regions: reg_m x reg_n = 8 minimising the operand bytes fetched into the eight L2s,
@@ -362,20 +407,27 @@ hipError_t launch_tile(const void* A, const void* Bt, const void* bias, void* C,
   if ((long)mt * nt >= 65536) return hipErrorInvalidValue;  // the quotient trick needs u < 2^16
   dim3 grid(nt * mt);
   hipLaunchKernelGGL((gemm_bias_kernel<BM, BN, WM, WN, STAGES>), grid, dim3(kGemmThreads), 0, stream,
-                     static_cast<const f16*>(A), static_cast<const f16*>(Bt),
-                     static_cast<const f16*>(bias), static_cast<f16*>(C), M, N, K, map);
+                     static_cast<const f16*>(A), static_cast<const f16*>(Bt), static_cast<f16*>(C), M, N,
+                     K, map, ep);
   return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_gemm(const void* A, const void* Bt, const void* bias, const void* residual, int res_period,
+                       int act, void* C, int M, int N, int K, hipStream_t stream) {
+  const Epilogue ep{static_cast<const f16*>(bias), static_cast<const f16*>(residual),
+                    residual ? res_period : 1, act};
+  if (N % 192 == 0 && (long)((M + 127) / 128) * (N / 192) >= 160)
+    return launch_tile<128, 192, 2, 2, 4>(A, Bt, C, M, N, K, ep, stream);
+  if (N % 128 == 0 && (long)((M + 127) / 128) * (N / 128) >= 160)
+    return launch_tile<128, 128, 2, 2, 4>(A, Bt, C, M, N, K, ep, stream);
+  return launch_tile<128, 64, 2, 2, 6>(A, Bt, C, M, N, K, ep, stream);
+}
+
 hipError_t launch_gemm_bias(const void* A, const void* Bt, const void* bias, void* C, int M, int N,
                             int K, hipStream_t stream) {
-  if (N % 192 == 0 && (long)((M + 127) / 128) * (N / 192) >= 160)
-    return launch_tile<128, 192, 2, 2, 4>(A, Bt, bias, C, M, N, K, stream);
-  if (N % 128 == 0 && (long)((M + 127) / 128) * (N / 128) >= 160)
-    return launch_tile<128, 128, 2, 2, 4>(A, Bt, bias, C, M, N, K, stream);
-  return launch_tile<128, 64, 2, 2, 6>(A, Bt, bias, C, M, N, K, stream);
+  return launch_gemm(A, Bt, bias, nullptr, 1, 0, C, M, N, K, stream);
 }
 
 }  // namespace edda

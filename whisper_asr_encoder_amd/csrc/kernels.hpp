@@ -13,6 +13,21 @@ namespace edda {
 hipError_t launch_gemm_bias(const void* A, const void* Bt, const void* bias, void* C, int M, int N,
                             int K, hipStream_t stream);
 
+// C = act(A * Bt^T + bias) + residual[m % res_period] (act 0 none, 1 GELU; bias and
+// residual may be null; residual may be C itself). Same shape rules as launch_gemm_bias.
+hipError_t launch_gemm(const void* A, const void* Bt, const void* bias, const void* residual, int res_period,
+                       int act, void* C, int M, int N, int K, hipStream_t stream);
+
+// Row-wise LayerNorm over `features` (multiple of 256, at most 4096), eps 1e-5.
+hipError_t launch_layer_norm(const void* x, int rows, int features, const void* gamma, const void* beta,
+                             void* y, hipStream_t stream);
+
+// Columns of a kernel-3, padding-1 convolution: cols[b*T_out + t][tap*C + c] =
+// x_b[stride*t + tap - 1][c] (0 outside), x_b element (t, c) at x + b*x_batch + t*ts + c*cs.
+// C % 8 == 0.
+hipError_t launch_im2col3(const void* x, int batch, long x_batch, int t_in, int channels, long ts, long cs,
+                          int stride, void* cols, hipStream_t stream);
+
 // Flash attention over a packed [batch*seq_len, 3840] QKV buffer into O [batch*seq_len, 1280].
 // chunk_len 0 = whole window; valid[b] = number of admitted key positions of window b.
 hipError_t launch_flash_attn(const void* qkv, void* O, int batch, int seq_len, int chunk_len,

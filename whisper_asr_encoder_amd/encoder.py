@@ -70,3 +70,67 @@ class VerifyAttention:
 
     def __call__(self, q, k, v, mask_rows, o, stream=None):
         _lib.edda_verify_attn(q, k, v, mask_rows, o, self.workspace, stream)
+
+
+class FullEncoder:
+    """Whole encoder: convolutional stem, pre-norm layers and the final LayerNorm, for
+    `batch` windows of `seq_len` positions (2 * seq_len mel frames each). Weights are held on
+    the device in the library's layout; every step runs in libedda.so."""
+
+    def __init__(self, layer_weights, stem=None, batch: int = 1, seq_len: int = 1500, chunk_len: int = 0,
+                 valid_len=None, n_mels: int = 128, device="cuda"):
+        import torch
+        self.torch = torch
+        self.batch, self.seq_len, self.chunk_len = int(batch), int(seq_len), int(chunk_len)
+        self.valid_len = None if valid_len is None else [int(v) for v in np.asarray(valid_len).reshape(-1)]
+        self.rows = self.batch * self.seq_len
+        self.device = device
+        self._keep = []          # device tensors the pointer structs refer to
+        self.structs = []
+        for w in layer_weights:
+            t = dict(ln1_gamma=self._dev(w.ln1_g), ln1_beta=self._dev(w.ln1_b),
+                     w_qkv=self._dev(_lib.linear_layout(w.w_qkv)), b_qkv=self._dev(w.b_qkv),
+                     w_o=self._dev(_lib.linear_layout(w.w_o)), b_o=self._opt(w.b_o),
+                     ln2_gamma=self._dev(w.ln2_g), ln2_beta=self._dev(w.ln2_b),
+                     w_fc1=self._dev(_lib.linear_layout(w.w_fc1)), b_fc1=self._opt(w.b_fc1),
+                     w_fc2=self._dev(_lib.linear_layout(w.w_fc2)), b_fc2=self._opt(w.b_fc2))
+            self._keep.append(t)
+            self.structs.append(_lib.LayerWeights(**{k: (None if v is None else v.data_ptr()) for k, v in t.items()}))
+        self.stem_w = None
+        if stem is not None:
+            self.n_mels = int(n_mels)
+            self.stem_w = dict(c1w=self._dev(_lib.conv_layout(stem.conv1_w)), c1b=self._dev(stem.conv1_b),
+                               c2w=self._dev(_lib.conv_layout(stem.conv2_w)), c2b=self._dev(stem.conv2_b),
+                               pos=self._dev(stem.pos_emb[:self.seq_len]), lnp_g=self._dev(stem.lnp_g),
+                               lnp_b=self._dev(stem.lnp_b))
+            sb = _lib.encoder_stem_workspace_bytes(self.batch, self.n_mels, 2 * self.seq_len)
+            self.stem_ws = torch.empty(max(sb, 16), dtype=torch.uint8, device=device)
+        lb = _lib.encoder_layer_workspace_bytes(self.batch, self.seq_len)
+        self.workspace = torch.empty(max(lb, 16), dtype=torch.uint8, device=device)
+        self.x = torch.empty((self.rows, _lib.D_MODEL), dtype=torch.float16, device=device)
+
+    def _dev(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a)).to(self.device)
+
+    def _opt(self, a):
+        return None if a is None else self._dev(a)
+
+    @property
+    def layers(self) -> int:
+        return len(self.structs)
+
+    def layer(self, x, layer: int, y, stream=None):
+        """y = encoder layer `layer` applied to x (device fp16 [rows, 1280]); y may be x."""
+        _lib.edda_encoder_layer(x, self.batch, self.seq_len, self.chunk_len, self.valid_len, self.structs[layer], y,
+                                self.workspace, stream)
+
+    def stem(self, mel, y, stream=None):
+        s = self.stem_w
+        _lib.edda_encoder_stem(mel, s["c1w"], s["c1b"], s["c2w"], s["c2b"], s["pos"], y, self.stem_ws, stream)
+
+    def forward(self, mel, out, stream=None):
+        """out[rows, 1280] = LN_post(layers(stem(mel))); mel [batch, n_mels, 2*seq_len] device fp16."""
+        self.stem(mel, self.x, stream)
+        for layer in range(self.layers):
+            self.layer(self.x, layer, self.x, stream)
+        _lib.edda_layer_norm(self.x, self.stem_w["lnp_g"], self.stem_w["lnp_b"], out, stream)
