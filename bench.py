@@ -255,6 +255,110 @@ def cpu_model():
 
 
 # ---------------------------------------------------------------------------
+# Whole encoder: convolutional stem + 32 pre-norm layers + final LayerNorm, one window.
+# ---------------------------------------------------------------------------
+
+PAGES_ENCODER_MS = 285.0  # the pages' whole-encoder time per 30 s window (Radeon 8060S)
+
+
+def full_encoder_bench(args, torch):
+    from whisper_asr_encoder_amd import _lib, inputs as I
+    from whisper_asr_encoder_amd.encoder import FullEncoder
+
+    seq, layers = I.FRAMES_PER_WINDOW, I.ENCODER_LAYERS
+    weights = [I.full_layer_weights(1, l) for l in range(layers)]
+    sw = I.stem_weights()
+    enc = FullEncoder(weights, stem=sw, batch=1, seq_len=seq)
+    mel = torch.from_numpy(I.mel_input(1)).cuda()
+    out = torch.empty((seq, D), dtype=torch.float16, device="cuda")
+
+    # Algorithmic work: stem convolutions as GEMMs, per layer QKV + attention + output
+    # projection + the two MLP GEMMs (LayerNorm, GELU and residual adds are not counted).
+    f_stem = gemm_flops(2 * seq, D, 3 * I.N_MELS) + gemm_flops(seq, D, 3 * D)
+    f_qkv, f_out = gemm_flops(seq, QKV, D), gemm_flops(seq, D, D)
+    f_attn = attn_flops(seq * seq)
+    f_fc = gemm_flops(seq, I.D_FF, D)
+    f_layer = f_qkv + f_attn + f_out + 2 * f_fc
+    f_total = f_stem + layers * f_layer
+
+    def step():
+        enc.forward(mel, out)
+
+    for _ in range(args.warmup):
+        step()
+    timer = Timer(torch)
+    ms = timer(step, args.steps)
+
+    # Components: back-to-back launches of one step, cycling through the layers.
+    reps = max(2, args.steps // 2)
+    kw = enc._keep
+    h = torch.empty((seq, D), dtype=torch.float16, device="cuda")
+    x1 = torch.empty((seq, D), dtype=torch.float16, device="cuda")
+    qkv = torch.empty((seq, QKV), dtype=torch.float16, device="cuda")
+    f = torch.empty((seq, I.D_FF), dtype=torch.float16, device="cuda")
+    xw = torch.empty((seq, D), dtype=torch.float16, device="cuda")
+    enc.stem(mel, xw)
+
+    def run(fn):
+        return timer(lambda: [fn(l) for l in range(layers)], reps) / layers
+
+    t = {
+        "stem": timer(lambda: enc.stem(mel, xw), reps),
+        "layer": run(lambda l: enc.layer(xw, l, x1)),
+        "layer_norm": run(lambda l: _lib.edda_layer_norm(xw, kw[l]["ln1_gamma"], kw[l]["ln1_beta"], h)),
+        "qkv_gemm": run(lambda l: _lib.edda_qkv_pack(h, kw[l]["w_qkv"], kw[l]["b_qkv"], qkv)),
+        "flash_attn": run(lambda l: _lib.edda_flash_attn(qkv, 1, seq, 0, None, h)),
+        "out_gemm": run(lambda l: _lib.edda_linear(h, kw[l]["w_o"], kw[l]["b_o"], x1, residual=xw)),
+        "fc1_gemm": run(lambda l: _lib.edda_linear(h, kw[l]["w_fc1"], kw[l]["b_fc1"], f, activation=_lib.ACT_GELU)),
+        "fc2_gemm": run(lambda l: _lib.edda_linear(f, kw[l]["w_fc2"], kw[l]["b_fc2"], x1, residual=xw)),
+    }
+    flops = {"qkv_gemm": f_qkv, "flash_attn": f_attn, "out_gemm": f_out, "fc1_gemm": f_fc, "fc2_gemm": f_fc,
+             "layer": f_layer, "stem": f_stem}
+    kernels = {k: {"ms": round(v, 5), **({"tflops": round(flops[k] / (v * 1e-3) / 1e12, 2)} if k in flops else {})}
+               for k, v in t.items()}
+    dom = max(("qkv_gemm", "flash_attn", "out_gemm", "fc1_gemm", "fc2_gemm"), key=lambda k: t[k])
+    src = ["flash_attn.hip"] if dom == "flash_attn" else ["gemm.hip"]
+    achieved = flops[dom] / (t[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "flops_per_launch": flops[dom],
+                "ms_per_launch": round(t[dom], 5), "traffic": measured_traffic(dom, source_digest(src))}
+    result = {
+        "metric": "whole-encoder ms per 30 s window (stem + 32 layers + final LayerNorm) on 1 MI355X",
+        "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "tflops": round(f_total / (ms * 1e-3) / 1e12, 3),
+        "frac_of_fp16_peak": round(f_total / (ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
+        "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": round(ms / PAGES_ENCODER_MS, 6),
+        "vs_baseline_note": "value / the pages' ~285 ms per 30 s window for the whole encoder, measured on a "
+                            "Radeon 8060S (gfx1151) with trained weights: context, another machine",
+        "dtype": "fp16", "data": "synthetic (seeded weights and log-mel input; no trained weights or audio)",
+        "config": {"workload": "Whisper-large-v3 encoder, one 30 s window: 128 x 3000 log-mel in, conv stem, "
+                               "32 pre-norm layers (1500 x 1280, 20 heads, MLP 5120), final LayerNorm",
+                   "gflop_per_step": round(f_total / 1e9, 3), "parallelism": "single GPU"},
+        "kernels": kernels, "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_full_encoder(weights, f_layer, layers, args.cpu_seconds)
+    return result
+
+
+def cpu_baseline_full_encoder(weights, f_layer, layers, budget_s):
+    """The oracle's whole layers on one window until the time budget is used."""
+    import oracle.encoder_layer as OL
+    from whisper_asr_encoder_amd import inputs as I
+    threads = blas_threads()
+    x = I.encoder_workload(1, layers=1).x
+    done, t0 = 0, time.perf_counter()
+    while done < layers and (done == 0 or time.perf_counter() - t0 < budget_s):
+        OL.encoder_layer(x, weights[done], 1, I.FRAMES_PER_WINDOW, 0, I.FRAMES_PER_WINDOW, H)
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": round(f_layer * done / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {layers} encoder layers of one window (1500 rows), fp64 NumPy, {el:.1f} s",
+            "ms_per_layer": round(el / done * 1e3, 1), "cpu": cpu_model()}
+
+
+# ---------------------------------------------------------------------------
 # Verification workload: 32 decoder layers x (causal self-attention + cross-attention).
 # ---------------------------------------------------------------------------
 
@@ -331,7 +435,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="window", choices=["small", "window", "chunked", "batched", "verify"])
+    ap.add_argument("--workload", default="window", choices=["small", "window", "chunked", "batched", "verify", "encoder"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -357,6 +461,8 @@ def main():
         del src, dst
     if args.workload == "verify":
         res = verify_bench(args, torch)
+    elif args.workload == "encoder":
+        res = full_encoder_bench(args, torch)
     else:
         cfg = {"small": 0, "window": 1, "chunked": 2, "batched": 3}[args.workload]
         res = encoder_bench(args, torch, cfg)

@@ -115,7 +115,9 @@ struct Epilogue {
 
 __device__ __forceinline__ float gelu_exact(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+// ACT (0 none, 1 GELU) and RES (residual present) are compile-time, so a kernel carries
+// only the epilogue code it runs (the GELU is inlined per output element).
+template <int BM, int BN, int WM, int WN, int STAGES, int ACT, bool RES>
 __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __restrict__ A,
                                                                  const f16* __restrict__ Bt,
                                                                  f16* C, int M, int N, int K,
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
   // Residual values of this lane's outputs (row m0 + wm*WTM + 32 fm + l32, 4 columns);
   // rows past M read row M-1 and are never stored.
   f16x4 res_v[FN][4][FM];
-  if (ep.residual) {
+  if constexpr (RES) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       const int m = min(m0 + wm * WTM + 32 * fm + l32, M - 1) % ep.res_period;
@@ -352,8 +354,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           v[j] = acc[fn][fm][4 * i + j] + (float)bb[j];
-          if (ep.act) v[j] = gelu_exact(v[j]);
-          v[j] += (float)rr[j];
+          if constexpr (ACT == 1) v[j] = gelu_exact(v[j]);
+          if constexpr (RES) v[j] += (float)rr[j];
         }
         const f16x2 lo = pack_rne(v[0], v[1]);
         const f16x2 hi = pack_rne(v[2], v[3]);
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
   }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES>
+template <int BM, int BN, int WM, int WN, int STAGES, int ACT, bool RES>
 hipError_t launch_tile(const void* A, const void* Bt, void* C, int M, int N, int K, const Epilogue& ep,
                        hipStream_t stream) {
   const int mt = (M + BM - 1) / BM, nt = N / BN;
@@ -406,11 +408,20 @@ hipError_t launch_tile(const void* A, const void* Bt, void* C, int M, int N, int
   map.first[kXcds] = acc;
   if ((long)mt * nt >= 65536) return hipErrorInvalidValue;  // the quotient trick needs u < 2^16
   dim3 grid(nt * mt);
-  hipLaunchKernelGGL((gemm_bias_kernel<BM, BN, WM, WN, STAGES>), grid, dim3(kGemmThreads), 0, stream,
+  hipLaunchKernelGGL((gemm_bias_kernel<BM, BN, WM, WN, STAGES, ACT, RES>), grid, dim3(kGemmThreads), 0, stream,
                      static_cast<const f16*>(A), static_cast<const f16*>(Bt), static_cast<f16*>(C), M, N,
                      K, map, ep);
   return hipGetLastError();
 }
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+struct Tile {
+  template <int ACT, bool RES>
+  static hipError_t run(const void* A, const void* Bt, void* C, int M, int N, int K, const Epilogue& ep,
+                        hipStream_t stream) {
+    return launch_tile<BM, BN, WM, WN, STAGES, ACT, RES>(A, Bt, C, M, N, K, ep, stream);
+  }
+};
 
 }  // namespace
 
@@ -418,11 +429,17 @@ hipError_t launch_gemm(const void* A, const void* Bt, const void* bias, const vo
                        int act, void* C, int M, int N, int K, hipStream_t stream) {
   const Epilogue ep{static_cast<const f16*>(bias), static_cast<const f16*>(residual),
                     residual ? res_period : 1, act};
-  if (N % 192 == 0 && (long)((M + 127) / 128) * (N / 192) >= 160)
-    return launch_tile<128, 192, 2, 2, 4>(A, Bt, C, M, N, K, ep, stream);
-  if (N % 128 == 0 && (long)((M + 127) / 128) * (N / 128) >= 160)
-    return launch_tile<128, 128, 2, 2, 4>(A, Bt, C, M, N, K, ep, stream);
-  return launch_tile<128, 64, 2, 2, 6>(A, Bt, C, M, N, K, ep, stream);
+  auto with_epilogue = [&](auto tile) {
+    using T = decltype(tile);
+    if (act == 1)
+      return residual ? T::template run<1, true>(A, Bt, C, M, N, K, ep, stream)
+                      : T::template run<1, false>(A, Bt, C, M, N, K, ep, stream);
+    return residual ? T::template run<0, true>(A, Bt, C, M, N, K, ep, stream)
+                    : T::template run<0, false>(A, Bt, C, M, N, K, ep, stream);
+  };
+  if (N % 192 == 0 && (long)((M + 127) / 128) * (N / 192) >= 160) return with_epilogue(Tile<128, 192, 2, 2, 4>());
+  if (N % 128 == 0 && (long)((M + 127) / 128) * (N / 128) >= 160) return with_epilogue(Tile<128, 128, 2, 2, 4>());
+  return with_epilogue(Tile<128, 64, 2, 2, 6>());
 }
 
 hipError_t launch_gemm_bias(const void* A, const void* Bt, const void* bias, void* C, int M, int N,
