@@ -90,6 +90,8 @@ LINEAR_CASES = [
     (300, 3840, 1280, 1, True, 150, "conv2 shape, GELU + a 150-row table over two windows"),
     (100, 1280, 1280, 0, False, -1, "no bias, residual in place"),
     (64, 1280, 3840, 0, True, 0, "QKV shape, 64 rows"),
+    (1500, 1280, 5120, 1, True, 0, "fc1 at a full window (128x256 tiles), GELU"),
+    (3000, 1280, 3840, 0, False, 0, "QKV shape, two windows"),
 ]
 
 

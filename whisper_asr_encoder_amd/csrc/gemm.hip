@@ -52,6 +52,7 @@ constexpr int kProducerWaves = 4;
 constexpr int kComputeThreads = kComputeWaves * kWave;
 constexpr int kGemmThreads = (kComputeWaves + kProducerWaves) * kWave;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
+constexpr int kCus = 256;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -419,7 +420,11 @@ struct Tile {
   template <int ACT, bool RES>
   static hipError_t run(const void* A, const void* Bt, void* C, int M, int N, int K, const Epilogue& ep,
                         hipStream_t stream) {
-    return launch_tile<BM, BN, WM, WN, STAGES, ACT, RES>(A, Bt, C, M, N, K, ep, stream);
+    if constexpr (BN == 256 && RES) {
+      return hipErrorInvalidValue;  // never selected (see launch_gemm)
+    } else {
+      return launch_tile<BM, BN, WM, WN, STAGES, ACT, RES>(A, Bt, C, M, N, K, ep, stream);
+    }
   }
 };
 
@@ -437,9 +442,26 @@ hipError_t launch_gemm(const void* A, const void* Bt, const void* bias, const vo
     return residual ? T::template run<0, true>(A, Bt, C, M, N, K, ep, stream)
                     : T::template run<0, false>(A, Bt, C, M, N, K, ep, stream);
   };
-  if (N % 192 == 0 && (long)((M + 127) / 128) * (N / 192) >= 160) return with_epilogue(Tile<128, 192, 2, 2, 4>());
-  if (N % 128 == 0 && (long)((M + 127) / 128) * (N / 128) >= 160) return with_epilogue(Tile<128, 128, 2, 2, 4>());
-  return with_epilogue(Tile<128, 64, 2, 2, 6>());
+  // Tile width by a cost model of one launch: rounds of tiles over the CUs times the
+  // cost of a K step, the larger of its copy time (operand bytes at ~38 B/clk per CU,
+  // measured) and its MFMA time (4096 FLOP/clk per CU).  The 256-wide tile has no
+  // register room for the residual values.
+  const int bns[] = {256, 192, 128, 64};
+  int best = 64;
+  double best_cost = -1.0;
+  for (int bn : bns) {
+    if (N % bn || (bn == 256 && residual)) continue;
+    const long tiles = (long)((M + 127) / 128) * (N / bn);
+    const double step = fmax((128.0 + bn) * 128.0 / 38.0, 128.0 * bn * 128.0 / 4096.0);
+    const double cost = (double)((tiles + kCus - 1) / kCus) * step;
+    if (best_cost < 0 || cost < best_cost) best_cost = cost, best = bn;
+  }
+  switch (best) {
+    case 256: return with_epilogue(Tile<128, 256, 2, 2, 3>());
+    case 192: return with_epilogue(Tile<128, 192, 2, 2, 4>());
+    case 128: return with_epilogue(Tile<128, 128, 2, 2, 4>());
+    default: return with_epilogue(Tile<128, 64, 2, 2, 6>());
+  }
 }
 
 hipError_t launch_gemm_bias(const void* A, const void* Bt, const void* bias, void* C, int M, int N,

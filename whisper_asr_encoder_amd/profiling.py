@@ -44,7 +44,17 @@ WORKLOADS = {
         "verify_kernelILb1E": ("verify_causal", ["verify_attn.hip"]),
         "verify_kernelILb0E": ("verify_cross", ["verify_attn.hip"]),
     }),
+    # The whole encoder: fc1 is the only 128x128-tile GEMM (N = 5120, GELU, no residual).
+    "encoder": ("whole encoder of one 30 s window (stem, 32 pre-norm layers, final LayerNorm)", {
+        "gemm_bias_kernelILi128ELi128ELi2ELi2ELi4ELi1ELb0E": ("fc1_gemm", ["gemm.hip"]),
+        "layer_norm_kernelILi5E": ("layer_norm", ["norm_im2col.hip"]),
+        "im2col3_kernel": ("im2col3", ["norm_im2col.hip"]),
+    }),
 }
+
+# Optional extra counter pass (one rocprofv3 --pmc run): median per dispatch.
+EXTRA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+                  "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_VALU_TRANS_F32")
 COPY_KERNEL = "copyBuffer"
 
 
@@ -86,8 +96,9 @@ def _match(values, fragment):
     return [x for h in hits for x in h]
 
 
-def summarize(trace_dir, fetch_dir, write_dir, out_dir, command, workload="window"):
+def summarize(trace_dir, fetch_dir, write_dir, out_dir, command, workload="window", extra_dir=None):
     title, kernels = WORKLOADS[workload]
+    extra = {c: counter_values(extra_dir, c) for c in EXTRA_COUNTERS} if extra_dir else {}
     stats = kernel_stats(trace_dir)
     fetch = counter_values(fetch_dir, "FETCH_SIZE")
     write = counter_values(write_dir, "WRITE_SIZE")
@@ -130,6 +141,10 @@ def summarize(trace_dir, fetch_dir, write_dir, out_dir, command, workload="windo
             f.write(f"| HBM bytes per launch (scaled) | {(fb + wb) / 1e6:.2f} MB "
                     f"(read {fb / 1e6:.2f}, write {wb / 1e6:.2f}) |\n")
             f.write(f"| kernel sources digest | {digest} |\n")
+            for c, vals in extra.items():
+                v = _match(vals, frag)
+                if v:
+                    f.write(f"| {c} median per dispatch | {statistics.median(v):.0f} |\n")
     with open(tpath, "w") as f:
         json.dump(traffic, f, indent=1)
         f.write("\n")
@@ -144,9 +159,10 @@ def main():
     ap.add_argument("out_dir")
     ap.add_argument("--command", required=True)
     ap.add_argument("--workload", default="window", choices=sorted(WORKLOADS))
+    ap.add_argument("--extra-pmc", default=None, help="directory of a rocprofv3 --pmc run of EXTRA_COUNTERS")
     a = ap.parse_args()
-    print(json.dumps(summarize(a.trace_dir, a.fetch_dir, a.write_dir, a.out_dir, a.command, a.workload),
-                     indent=1))
+    print(json.dumps(summarize(a.trace_dir, a.fetch_dir, a.write_dir, a.out_dir, a.command, a.workload,
+                               a.extra_pmc), indent=1))
 
 
 if __name__ == "__main__":
