@@ -44,9 +44,9 @@ WORKLOADS = {
         "verify_kernelILb1E": ("verify_causal", ["verify_attn.hip"]),
         "verify_kernelILb0E": ("verify_cross", ["verify_attn.hip"]),
     }),
-    # The whole encoder: fc1 is the only 128x128-tile GEMM (N = 5120, GELU, no residual).
+    # The whole encoder: fc1 is the only 128x256-tile GEMM (N = 5120, GELU, no residual).
     "encoder": ("whole encoder of one 30 s window (stem, 32 pre-norm layers, final LayerNorm)", {
-        "gemm_bias_kernelILi128ELi128ELi2ELi2ELi4ELi1ELb0E": ("fc1_gemm", ["gemm.hip"]),
+        "gemm_bias_kernelILi128ELi256E": ("fc1_gemm", ["gemm.hip"]),
         "layer_norm_kernelILi5E": ("layer_norm", ["norm_im2col.hip"]),
         "im2col3_kernel": ("im2col3", ["norm_im2col.hip"]),
     }),
