@@ -328,3 +328,65 @@ def stem_weights(cfg: int = 1, seed: int = 0, frames: int = FRAMES_PER_WINDOW) -
 def mel_input(batch: int = 1, cfg: int = 1, seed: int = 0, frames: int = MEL_FRAMES) -> np.ndarray:
     """Synthetic log-mel input [batch, 128, frames] ~ N(0, 1), fp16 (channel-major per window)."""
     return normal_f16(rng_for(seed, cfg, 0, T_MEL), (batch, N_MELS, frames), 1.0)
+
+
+# --------------------------------------------------------------------------------------
+# The decoder's verification layer (self-attention over the KV cache, cross-attention over
+# the encoder output, MLP), Whisper-large-v3 decoder geometry (same width and heads).
+# --------------------------------------------------------------------------------------
+
+(T_DLN1G, T_DLN1B, T_DLN2G, T_DLN2B, T_DLN3G, T_DLN3B, T_DWQKV, T_DBQ, T_DBV, T_DWO, T_DBO, T_DWQC, T_DBQC,
+ T_DWOC, T_DBOC, T_DWCK, T_DWCV, T_DBCV, T_DW1, T_DB1, T_DW2, T_DB2, T_DX) = range(40, 63)
+
+
+@dataclass
+class DecoderLayerWeights:
+    """Math layout (y = x w): w [in, out]."""
+    ln1_g: np.ndarray
+    ln1_b: np.ndarray
+    w_qkv: np.ndarray      # [1280, 3840], K third of b_qkv zero
+    b_qkv: np.ndarray
+    w_o: np.ndarray
+    b_o: np.ndarray
+    ln2_g: np.ndarray
+    ln2_b: np.ndarray
+    w_qc: np.ndarray       # cross-attention query projection [1280, 1280]
+    b_qc: np.ndarray
+    w_oc: np.ndarray
+    b_oc: np.ndarray
+    w_ck: np.ndarray       # cross-attention key / value projections of the encoder output
+    w_cv: np.ndarray
+    b_cv: np.ndarray
+    ln3_g: np.ndarray
+    ln3_b: np.ndarray
+    w_fc1: np.ndarray
+    b_fc1: np.ndarray
+    w_fc2: np.ndarray
+    b_fc2: np.ndarray
+
+
+def decoder_layer_weights(layer: int, seed: int = 0, cfg: int = 4) -> DecoderLayerWeights:
+    """Distributions as for the encoder layer: matrices N(0, 1/fan-in), biases N(0, 0.02),
+    LayerNorm scale 1 + N(0, 0.01) and shift N(0, 0.01); no key biases."""
+    g = lambda tid, shape, var: normal_f16(rng_for(seed, cfg, layer, tid), shape, var)
+    ln = lambda tg, tb: _ln_params(seed, cfg, layer, tg, tb)
+    ln1_g, ln1_b = ln(T_DLN1G, T_DLN1B)
+    ln2_g, ln2_b = ln(T_DLN2G, T_DLN2B)
+    ln3_g, ln3_b = ln(T_DLN3G, T_DLN3B)
+    b_qkv = np.zeros(QKV_COLS, dtype=np.float16)
+    b_qkv[:D_MODEL] = g(T_DBQ, (D_MODEL,), B_VAR)
+    b_qkv[2 * D_MODEL:] = g(T_DBV, (D_MODEL,), B_VAR)
+    return DecoderLayerWeights(
+        ln1_g=ln1_g, ln1_b=ln1_b, w_qkv=g(T_DWQKV, (D_MODEL, QKV_COLS), W_VAR), b_qkv=b_qkv,
+        w_o=g(T_DWO, (D_MODEL, D_MODEL), W_VAR), b_o=g(T_DBO, (D_MODEL,), B_VAR),
+        ln2_g=ln2_g, ln2_b=ln2_b, w_qc=g(T_DWQC, (D_MODEL, D_MODEL), W_VAR), b_qc=g(T_DBQC, (D_MODEL,), B_VAR),
+        w_oc=g(T_DWOC, (D_MODEL, D_MODEL), W_VAR), b_oc=g(T_DBOC, (D_MODEL,), B_VAR),
+        w_ck=g(T_DWCK, (D_MODEL, D_MODEL), W_VAR), w_cv=g(T_DWCV, (D_MODEL, D_MODEL), W_VAR),
+        b_cv=g(T_DBCV, (D_MODEL,), B_VAR),
+        ln3_g=ln3_g, ln3_b=ln3_b, w_fc1=g(T_DW1, (D_MODEL, D_FF), 1.0 / D_MODEL), b_fc1=g(T_DB1, (D_FF,), B_VAR),
+        w_fc2=g(T_DW2, (D_FF, D_MODEL), 1.0 / D_FF), b_fc2=g(T_DB2, (D_MODEL,), B_VAR))
+
+
+def decoder_block_input(trial: int = 0, n_q: int = VERIFY_BLOCK, seed: int = 0, cfg: int = 4) -> np.ndarray:
+    """Residual-stream rows of the n_q block tokens [n_q, 1280] ~ N(0, 1)."""
+    return normal_f16(rng_for(seed, cfg, 0, T_DX, trial), (n_q, D_MODEL), 1.0)
