@@ -359,6 +359,75 @@ def cpu_baseline_full_encoder(weights, f_layer, layers, budget_s):
 
 
 # ---------------------------------------------------------------------------
+# Decoder verification pass: 32 whole decoder layers for one block of 16 tokens.
+# ---------------------------------------------------------------------------
+
+def decoder_bench(args, torch):
+    from whisper_asr_encoder_amd import _lib, inputs as I
+    from whisper_asr_encoder_amd.encoder import DecoderVerifier
+
+    layers, n_q, trial = I.ENCODER_LAYERS, I.VERIFY_BLOCK, 0
+    L = I.cache_length(trial)
+    weights = [I.decoder_layer_weights(l) for l in range(layers)]
+    dv = DecoderVerifier(weights, max_kv=L)
+    enc = torch.from_numpy(I.encoder_workload(1, layers=1).x).cuda()
+    dv.set_encoder_output(enc)
+    caches = []
+    for l in range(layers):
+        c = I.verify_self_case(trial, l)
+        caches.append((torch.from_numpy(c.k).cuda(), torch.from_numpy(c.v).cuda()))
+    mask = torch.from_numpy(_lib.pack_mask_rows(I.causal_block_mask(n_q, L)).view(np.int32)).cuda()
+    slots = list(range(L - n_q, L))
+    x = torch.from_numpy(I.decoder_block_input(trial)).cuda()
+    y = torch.empty_like(x)
+
+    def step():
+        for l in range(layers):
+            dv.layer(x if l == 0 else y, l, slots, caches[l][0], caches[l][1], L, mask, y)
+
+    for _ in range(args.warmup):
+        step()
+    timer = Timer(torch)
+    eager_ms = timer(step, args.steps)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    ms = timer(graph.replay, args.steps)
+
+    # Algorithmic bytes per layer: every weight once, the self and cross K/V read, the block's
+    # K/V rows written, activations and the mask (small).
+    # Matrices: W_qkv (3 D^2), self output, cross query and output (3 D^2), fc1 and fc2;
+    # biases: qkv, self output, cross query and output, fc1, fc2; three LayerNorms.
+    w_bytes = 2 * (6 * D * D + 2 * D * I.D_FF) + 2 * (3 * D + 3 * D + I.D_FF + D) + 2 * 6 * D
+    kv_bytes = 2 * 2 * D * (L + I.FRAMES_PER_WINDOW) + 2 * 2 * D * n_q
+    act_bytes = 2 * n_q * D * 4 + n_q * ((L + 31) // 32) * 4
+    per_layer = w_bytes + kv_bytes + act_bytes
+    gbs = per_layer * layers / (ms * 1e-3) / 1e9
+    flops = layers * (gemm_flops(n_q, QKV, D) + 2 * gemm_flops(n_q, D, D) + gemm_flops(n_q, D, D)
+                      + 2 * gemm_flops(n_q, I.D_FF, D) + attn_flops(n_q * L) + attn_flops(n_q * I.FRAMES_PER_WINDOW))
+    return {
+        "metric": "decoder verification pass (32 decoder layers, 16-token block) on 1 MI355X",
+        "value": round(ms * 1e3, 2), "unit": "us per pass", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp16", "data": "synthetic (seeded weights, caches and block rows)",
+        "launch": "hip graph of the pass", "eager_ms_per_step": round(eager_ms, 4),
+        "us_per_layer": round(ms * 1e3 / layers, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+        "config": {"workload": f"Whisper-large-v3 decoder verification layers: 16 block tokens, causal self-attention "
+                               f"over a {L}-slot cache (block appended), cross-attention over 1500 frames, "
+                               "GELU MLP 5120; 32 layers", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_layer": per_layer, "traffic": None},
+    }
+
+
+# ---------------------------------------------------------------------------
 # Verification workload: 32 decoder layers x (causal self-attention + cross-attention).
 # ---------------------------------------------------------------------------
 
@@ -435,7 +504,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="window", choices=["small", "window", "chunked", "batched", "verify", "encoder"])
+    ap.add_argument("--workload", default="window", choices=["small", "window", "chunked", "batched", "verify", "encoder", "decoder"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -463,6 +532,8 @@ def main():
         res = verify_bench(args, torch)
     elif args.workload == "encoder":
         res = full_encoder_bench(args, torch)
+    elif args.workload == "decoder":
+        res = decoder_bench(args, torch)
     else:
         cfg = {"small": 0, "window": 1, "chunked": 2, "batched": 3}[args.workload]
         res = encoder_bench(args, torch, cfg)

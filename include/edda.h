@@ -273,6 +273,78 @@ edda_status edda_encoder_stem(const void* mel, int32_t batch, int32_t n_mels, in
 /* Bytes of workspace edda_encoder_stem needs (0 if the shape is invalid). */
 size_t edda_encoder_stem_workspace_bytes(int32_t batch, int32_t n_mels, int32_t n_frames);
 
+/* ------------------------------------------------------------------------------------
+ * The decoder's verification layer. "audio.cpp PR #1223" (PR description, commit messages):
+ * the target decoder verifies an anchor plus up to 15 drafted tokens in one pass over KV
+ * slots indexed by position, beams share one token-tree cache whose mask rows admit only a
+ * beam's ancestors, and the decoder attends to the encoder output. The layer itself follows
+ * the public Whisper-large-v3 decoder: pre-norm self-attention (block K/V appended to the
+ * cache first), cross-attention over projected encoder frames, GELU MLP (width 5120).
+ * ------------------------------------------------------------------------------------ */
+
+/* Weights of one decoder layer, all fp16 device pointers, Linear layout ([out, in]). */
+typedef struct {
+  const void* ln1_gamma;  /* [1280] */
+  const void* ln1_beta;
+  const void* w_qkv;      /* [3840, 1280]: q | k | v rows, as for edda_qkv_pack */
+  const void* b_qkv;      /* [3840] or NULL (no key bias in Whisper: pass zeros there) */
+  const void* w_o;        /* [1280, 1280] self-attention output projection */
+  const void* b_o;        /* or NULL */
+  const void* ln2_gamma;
+  const void* ln2_beta;
+  const void* w_q_cross;  /* [1280, 1280] cross-attention query projection */
+  const void* b_q_cross;  /* or NULL */
+  const void* w_o_cross;  /* [1280, 1280] cross-attention output projection */
+  const void* b_o_cross;  /* or NULL */
+  const void* ln3_gamma;
+  const void* ln3_beta;
+  const void* w_fc1;      /* [5120, 1280] */
+  const void* b_fc1;      /* or NULL */
+  const void* w_fc2;      /* [1280, 5120] */
+  const void* b_fc2;      /* or NULL */
+} edda_decoder_layer_weights;
+
+/*
+ * One decoder layer over the n_q block tokens:
+ *   h = LN1(x); qkv = h W_qkv + b_qkv; the K and V rows of token t are written to cache slot
+ *   slots[t]; o = verify attention of the Q rows over cache slots 0..n_kv-1 under mask_rows
+ *   (as edda_verify_attn); x1 = x + o W_o + b_o;
+ *   x2 = x1 + verify attention of (LN2(x1) W_qc + b_qc) over cross_k / cross_v (no mask),
+ *        projected by W_oc + b_oc;
+ *   y = x2 + GELU(LN3(x2) W1 + b1) W2 + b2.
+ *  x, y        [n_q, 1280] fp16 (y may equal x); n_q in [1, 16].
+ *  slots       HOST int32[n_q]: distinct cache slots in [0, n_kv) of the block tokens (the
+ *              last n_q slots for a chain; a beam's fresh slots for a token tree).
+ *  k_cache, v_cache  [cache_slots, 20, 64] fp16, updated in place at `slots`.
+ *  n_kv        slots the self-attention reads, 1 <= n_kv <= cache_slots.
+ *  mask_rows   DEVICE uint32 [n_q][ceil(n_kv/32)] or NULL, as for edda_verify_attn.
+ *  cross_k, cross_v  [n_frames, 20, 64] fp16 (edda_cross_kv of the encoder output).
+ *  workspace   at least edda_decoder_verify_workspace_bytes(n_q, n_kv, n_frames) bytes; its
+ *              first EDDA_VERIFY_COUNTER_BYTES bytes must be zero before its first use (every
+ *              call leaves them zero); the rest is scratch. Calls sharing it must not overlap.
+ * Errors: EDDA_ERR_INVALID_ARGUMENT (NULL pointers, n_q, slots out of range or repeated,
+ * n_kv, n_frames), EDDA_ERR_MISALIGNED, EDDA_ERR_WORKSPACE, EDDA_ERR_HIP.
+ */
+edda_status edda_decoder_verify_layer(const void* x, int32_t n_q, const int32_t* slots, void* k_cache,
+                                      void* v_cache, int32_t cache_slots, int32_t n_kv,
+                                      const uint32_t* mask_rows, const void* cross_k, const void* cross_v,
+                                      int32_t n_frames, const edda_decoder_layer_weights* weights, void* y,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace edda_decoder_verify_layer needs (0 if the shape is invalid). */
+size_t edda_decoder_verify_workspace_bytes(int32_t n_q, int32_t n_kv, int32_t n_frames);
+
+/*
+ * Cross-attention keys and values of the encoder output, once per utterance and layer:
+ * cross_k = enc W_k (no bias), cross_v = enc W_v + b_v.
+ *  enc            [n_frames, 1280] fp16.
+ *  w_k, w_v       [1280, 1280] fp16, Linear layout; b_v [1280] or NULL.
+ *  cross_k, cross_v [n_frames, 1280] = [n_frames, 20, 64] fp16.
+ * Errors: EDDA_ERR_INVALID_ARGUMENT, EDDA_ERR_MISALIGNED, EDDA_ERR_HIP.
+ */
+edda_status edda_cross_kv(const void* enc, int32_t n_frames, const void* w_k, const void* w_v, const void* b_v,
+                          void* cross_k, void* cross_v, void* stream);
+
 /* Text of the calling thread's most recent error ("" after a successful call). */
 const char* edda_last_error(void);
 

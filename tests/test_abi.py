@@ -217,3 +217,49 @@ def test_layer_and_stem_workspace_sizes(lib):
     assert lib.edda_encoder_stem_workspace_bytes(1, 128, 3000) == (3000 * 384 + 3000 * 1280 + 1500 * 3840) * 2
     assert lib.edda_encoder_stem_workspace_bytes(2, 128, 7) == (14 * 384 + 14 * 1280 + 8 * 3840) * 2
     assert lib.edda_encoder_stem_workspace_bytes(1, 128, 0) == 0
+
+
+# ---------------------------------------------------------------------------
+# Decoder verification layer and cross K/V.
+# ---------------------------------------------------------------------------
+
+def dec(lib, x=A, n_q=16, slots=tuple(range(24, 40)), kc=A, vc=A, cap=448, n_kv=40, mask=None, ck=A, cv=A,
+        frames=1500, wover=None, y=B, ws=B + (1 << 24), ws_bytes=1 << 30):
+    w = _lib.DecoderLayerWeights(*([A] * 18))
+    for k, v in (wover or {}).items():
+        setattr(w, k, v)
+    arr = None
+    if slots is not None:
+        arr = ctypes.cast((ctypes.c_int32 * max(len(slots), 1))(*slots), ctypes.POINTER(ctypes.c_int32))
+    return lib.edda_decoder_verify_layer(x, n_q, arr, kc, vc, cap, n_kv, mask, ck, cv, frames, ctypes.byref(w), y,
+                                         ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(slots=None), INVALID), (dict(kc=None), INVALID), (dict(ck=None), INVALID),
+    (dict(n_q=0, slots=(1,)), INVALID), (dict(n_q=17, slots=tuple(range(17))), INVALID),
+    (dict(n_kv=0), INVALID), (dict(n_kv=500), INVALID), (dict(frames=0), INVALID),
+    (dict(n_q=2, slots=(3, 40)), INVALID), (dict(n_q=2, slots=(-1, 3)), INVALID), (dict(n_q=2, slots=(5, 5)), INVALID),
+    (dict(wover=dict(w_fc2=None)), INVALID), (dict(wover=dict(ln3_beta=None)), INVALID),
+    (dict(x=ODD), MISALIGNED), (dict(wover=dict(b_o_cross=ODD)), MISALIGNED), (dict(mask=A + 2), MISALIGNED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=1000), WORKSPACE),
+])
+def test_decoder_verify_layer_rejects(lib, kw, status):
+    assert dec(lib, **kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 1500, A, A, None, B, B), INVALID), ((A, 0, A, A, None, B, B), INVALID),
+    ((A, 1500, A, None, None, B, B), INVALID), ((A, 1500, A, A, ODD, B, B), MISALIGNED),
+    ((A, 1500, A, A, None, B, ODD), MISALIGNED),
+])
+def test_cross_kv_rejects(lib, args, status):
+    assert lib.edda_cross_kv(*args, None) == status
+
+
+def test_decoder_workspace_sizes(lib):
+    n = lib.edda_decoder_verify_workspace_bytes(16, 360, 1500)
+    verify = max(lib.edda_verify_workspace_bytes(16, 360), lib.edda_verify_workspace_bytes(16, 1500))
+    assert n >= verify + 16 * (4 * 1280 + 3840 + 5120) * 2  # h, o, x1, x2, qkv, MLP hidden
+    assert lib.edda_decoder_verify_workspace_bytes(17, 360, 1500) == 0
+    assert lib.edda_decoder_verify_workspace_bytes(1, 0, 1500) == 0

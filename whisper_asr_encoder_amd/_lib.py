@@ -30,6 +30,7 @@ STATUS = {0: "EDDA_OK", 1: "EDDA_ERR_INVALID_ARGUMENT", 2: "EDDA_ERR_UNSUPPORTED
 EXPORTS = ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_encoder_workspace_bytes", "edda_verify_attn",
            "edda_verify_workspace_bytes", "edda_linear", "edda_layer_norm", "edda_encoder_layer",
            "edda_encoder_layer_workspace_bytes", "edda_encoder_stem", "edda_encoder_stem_workspace_bytes",
+           "edda_decoder_verify_layer", "edda_decoder_verify_workspace_bytes", "edda_cross_kv",
            "edda_last_error", "edda_version")
 
 D_FF = 5120
@@ -41,6 +42,13 @@ class LayerWeights(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in (
         "ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_gamma", "ln2_beta",
         "w_fc1", "b_fc1", "w_fc2", "b_fc2")]
+
+
+class DecoderLayerWeights(ctypes.Structure):
+    """edda_decoder_layer_weights: device pointers (Linear layout)."""
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_gamma", "ln2_beta", "w_q_cross",
+        "b_q_cross", "w_o_cross", "b_o_cross", "ln3_gamma", "ln3_beta", "w_fc1", "b_fc1", "w_fc2", "b_fc2")]
 
 
 class EddaError(RuntimeError):
@@ -79,10 +87,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edda_encoder_stem.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.edda_encoder_stem_workspace_bytes.argtypes = [i32, i32, i32]
     lib.edda_encoder_stem_workspace_bytes.restype = sz
+    lib.edda_decoder_verify_layer.argtypes = [vp, i32, ctypes.POINTER(i32), vp, vp, i32, i32, vp, vp, vp, i32,
+                                              ctypes.POINTER(DecoderLayerWeights), vp, vp, sz, vp]
+    lib.edda_decoder_verify_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.edda_decoder_verify_workspace_bytes.restype = sz
+    lib.edda_cross_kv.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
     lib.edda_last_error.restype = ctypes.c_char_p
     lib.edda_version.restype = ctypes.c_char_p
     for name in ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_verify_attn", "edda_linear",
-                 "edda_layer_norm", "edda_encoder_layer", "edda_encoder_stem"):
+                 "edda_layer_norm", "edda_encoder_layer", "edda_encoder_stem", "edda_decoder_verify_layer",
+                 "edda_cross_kv"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -303,3 +317,46 @@ def edda_encoder_stem(mel, conv1_w, conv1_b, conv2_w, conv2_b, pos, y, workspace
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib.edda_encoder_stem(_ptr(mel), batch, n_mels, n_frames, _ptr(conv1_w), _ptr(conv1_b), _ptr(conv2_w),
                                  _ptr(conv2_b), _ptr(pos), _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def decoder_verify_workspace_bytes(n_q: int, n_kv: int, n_frames: int) -> int:
+    return int(load().edda_decoder_verify_workspace_bytes(n_q, n_kv, n_frames))
+
+
+def edda_decoder_verify_layer(x, slots, k_cache, v_cache, n_kv, mask_rows, cross_k, cross_v,
+                              weights: "DecoderLayerWeights", y, workspace, stream=None):
+    """One decoder layer over the block rows x [n_q, 1280]; slots: host ints; caches
+    [cache_slots, 20, 64] updated in place; mask_rows as for edda_verify_attn (or None)."""
+    lib = load()
+    torch = _require(x, "x")
+    n_q = x.shape[0]
+    _require(x, "x", (n_q, D_MODEL), torch.float16)
+    _require(y, "y", (n_q, D_MODEL), torch.float16)
+    cache_slots = k_cache.shape[0]
+    _require(k_cache, "k_cache", (cache_slots, N_HEADS, HEAD_DIM), torch.float16)
+    _require(v_cache, "v_cache", (cache_slots, N_HEADS, HEAD_DIM), torch.float16)
+    n_frames = cross_k.shape[0]
+    _require(cross_k, "cross_k", (n_frames, N_HEADS, HEAD_DIM), torch.float16)
+    _require(cross_v, "cross_v", (n_frames, N_HEADS, HEAD_DIM), torch.float16)
+    if mask_rows is not None:
+        _require(mask_rows, "mask_rows", (n_q, (n_kv + 31) // 32))
+    arr = (ctypes.c_int32 * n_q)(*[int(v) for v in slots])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.edda_decoder_verify_layer(_ptr(x), n_q, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)),
+                                         _ptr(k_cache), _ptr(v_cache), cache_slots, n_kv, _ptr(mask_rows),
+                                         _ptr(cross_k), _ptr(cross_v), n_frames, ctypes.byref(weights), _ptr(y),
+                                         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def edda_cross_kv(enc, w_k, w_v, b_v, cross_k, cross_v, stream=None):
+    """cross_k = enc w_k^T, cross_v = enc w_v^T + b_v; enc [n_frames, 1280], outputs [n_frames, 20, 64]."""
+    lib = load()
+    torch = _require(enc, "enc")
+    n = enc.shape[0]
+    _require(enc, "enc", (n, D_MODEL), torch.float16)
+    _require(w_k, "w_k", (D_MODEL, D_MODEL), torch.float16)
+    _require(w_v, "w_v", (D_MODEL, D_MODEL), torch.float16)
+    _require(cross_k, "cross_k", (n, N_HEADS, HEAD_DIM), torch.float16)
+    _require(cross_v, "cross_v", (n, N_HEADS, HEAD_DIM), torch.float16)
+    _check(lib.edda_cross_kv(_ptr(enc), n, _ptr(w_k), _ptr(w_v), _ptr(b_v), _ptr(cross_k), _ptr(cross_v),
+                             _stream(stream)))

@@ -142,7 +142,7 @@ edda_status edda_verify_attn(const void* q, int32_t n_q, const void* k, const vo
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(EDDA_ERR_WORKSPACE, "edda_verify_attn: workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
-  return from_hip(edda::launch_verify(q, n_q, k, v, n_kv, mask_rows, o, workspace,
+  return from_hip(edda::launch_verify(q, EDDA_D_MODEL, n_q, k, v, n_kv, mask_rows, o, workspace,
                                       static_cast<hipStream_t>(stream)),
                   "edda_verify_attn launch");
 }
@@ -299,6 +299,124 @@ edda_status edda_encoder_stem(const void* mel, int32_t batch, int32_t n_mels, in
   return from_hip(edda::launch_gemm(cols2, conv2_w, conv2_b, pos, (int)t2, EDDA_ACT_GELU, y, (int)r2, EDDA_D_MODEL,
                                     3 * EDDA_D_MODEL, s),
                   "edda_encoder_stem conv2 launch");
+}
+
+
+// ---------------------------------------------------------------------------------------
+// The decoder's verification layer.
+// ---------------------------------------------------------------------------------------
+
+namespace {
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspace of the decoder layer: the verification workspace (counters first), then h, qkv,
+// o, x1, x2 and the MLP hidden layer, each 256-byte aligned.
+struct DecoderWs {
+  size_t verify, h, qkv, o, x1, x2, f, total;
+};
+
+DecoderWs decoder_ws(int32_t n_q, int32_t n_kv, int32_t n_frames) {
+  DecoderWs w{};
+  size_t v1 = edda::verify_workspace_bytes(n_q, n_kv), v2 = edda::verify_workspace_bytes(n_q, n_frames);
+  size_t off = align256(v1 > v2 ? v1 : v2);
+  if (off < EDDA_VERIFY_COUNTER_BYTES) off = EDDA_VERIFY_COUNTER_BYTES;
+  w.verify = 0;
+  const size_t row = (size_t)n_q * 2;
+  w.h = off;
+  w.qkv = w.h + align256(row * EDDA_D_MODEL);
+  w.o = w.qkv + align256(row * EDDA_QKV_COLS);
+  w.x1 = w.o + align256(row * EDDA_D_MODEL);
+  w.x2 = w.x1 + align256(row * EDDA_D_MODEL);
+  w.f = w.x2 + align256(row * EDDA_D_MODEL);
+  w.total = w.f + align256(row * EDDA_D_FF);
+  return w;
+}
+}  // namespace
+
+size_t edda_decoder_verify_workspace_bytes(int32_t n_q, int32_t n_kv, int32_t n_frames) {
+  if (n_q < 1 || n_q > EDDA_MAX_VERIFY_QUERIES || n_kv < 1 || n_frames < 1) return 0;
+  if ((int64_t)n_kv * EDDA_D_MODEL >= kMaxRows || (int64_t)n_frames * EDDA_D_MODEL >= kMaxRows) return 0;
+  return decoder_ws(n_q, n_kv, n_frames).total;
+}
+
+edda_status edda_decoder_verify_layer(const void* x, int32_t n_q, const int32_t* slots, void* k_cache,
+                                      void* v_cache, int32_t cache_slots, int32_t n_kv,
+                                      const uint32_t* mask_rows, const void* cross_k, const void* cross_v,
+                                      int32_t n_frames, const edda_decoder_layer_weights* wt, void* y,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "edda_decoder_verify_layer";
+  if (!x || !slots || !k_cache || !v_cache || !cross_k || !cross_v || !wt || !y)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: x, slots, caches, cross K/V, weights and y must be non-null", fn);
+  const void* required[] = {wt->ln1_gamma, wt->ln1_beta, wt->w_qkv, wt->w_o, wt->ln2_gamma, wt->ln2_beta,
+                            wt->w_q_cross, wt->w_o_cross, wt->ln3_gamma, wt->ln3_beta, wt->w_fc1, wt->w_fc2};
+  for (const void* p : required)
+    if (!p) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: every LayerNorm and weight-matrix pointer is required", fn);
+  if (n_q < 1 || n_q > EDDA_MAX_VERIFY_QUERIES)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_q = %d outside [1, %d]", fn, n_q, EDDA_MAX_VERIFY_QUERIES);
+  if (cache_slots < 1 || n_kv < 1 || n_kv > cache_slots || (int64_t)cache_slots * EDDA_D_MODEL >= kMaxRows)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_kv = %d must be in [1, cache_slots = %d]", fn, n_kv, cache_slots);
+  if (n_frames < 1 || (int64_t)n_frames * EDDA_D_MODEL >= kMaxRows)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_frames = %d out of range", fn, n_frames);
+  edda::Slots sl{};
+  for (int32_t t = 0; t < n_q; ++t) {
+    if (slots[t] < 0 || slots[t] >= n_kv)
+      return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: slots[%d] = %d outside [0, n_kv = %d)", fn, t, slots[t], n_kv);
+    for (int32_t u = 0; u < t; ++u)
+      if (slots[u] == slots[t]) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: slot %d repeated", fn, slots[t]);
+    sl.s[t] = slots[t];
+  }
+  const void* all[] = {x, y, k_cache, v_cache, cross_k, cross_v, workspace, wt->ln1_gamma, wt->ln1_beta, wt->w_qkv,
+                       wt->b_qkv, wt->w_o, wt->b_o, wt->ln2_gamma, wt->ln2_beta, wt->w_q_cross, wt->b_q_cross,
+                       wt->w_o_cross, wt->b_o_cross, wt->ln3_gamma, wt->ln3_beta, wt->w_fc1, wt->b_fc1, wt->w_fc2,
+                       wt->b_fc2};
+  for (const void* p : all)
+    if (p && !aligned(p, 16)) return fail(EDDA_ERR_MISALIGNED, "%s: pointers must be 16-byte aligned", fn);
+  if (mask_rows && !aligned(mask_rows, 4)) return fail(EDDA_ERR_MISALIGNED, "%s: mask_rows must be 4-byte aligned", fn);
+  const DecoderWs L = decoder_ws(n_q, n_kv, n_frames);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(EDDA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  char* ws = static_cast<char*>(workspace);
+  void *h = ws + L.h, *qkv = ws + L.qkv, *o = ws + L.o, *x1 = ws + L.x1, *x2 = ws + L.x2, *f = ws + L.f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = EDDA_D_MODEL;
+  hipError_t e;
+#define EDDA_STEP(call, what) \
+  if ((e = (call)) != hipSuccess) return from_hip(e, "edda_decoder_verify_layer " what " launch")
+  EDDA_STEP(edda::launch_layer_norm(x, n_q, D, wt->ln1_gamma, wt->ln1_beta, h, s), "LN1");
+  EDDA_STEP(edda::launch_gemm(h, wt->w_qkv, wt->b_qkv, nullptr, 1, EDDA_ACT_NONE, qkv, n_q, EDDA_QKV_COLS, D, s), "QKV");
+  EDDA_STEP(edda::launch_append_kv(qkv, n_q, sl, k_cache, v_cache, s), "cache append");
+  EDDA_STEP(edda::launch_verify(qkv, EDDA_QKV_COLS, n_q, k_cache, v_cache, n_kv, mask_rows, o, ws, s), "self-attention");
+  EDDA_STEP(edda::launch_gemm(o, wt->w_o, wt->b_o, x, n_q, EDDA_ACT_NONE, x1, n_q, D, D, s), "self output projection");
+  EDDA_STEP(edda::launch_layer_norm(x1, n_q, D, wt->ln2_gamma, wt->ln2_beta, h, s), "LN2");
+  EDDA_STEP(edda::launch_gemm(h, wt->w_q_cross, wt->b_q_cross, nullptr, 1, EDDA_ACT_NONE, o, n_q, D, D, s), "cross query");
+  EDDA_STEP(edda::launch_verify(o, D, n_q, cross_k, cross_v, n_frames, nullptr, h, ws, s), "cross-attention");
+  EDDA_STEP(edda::launch_gemm(h, wt->w_o_cross, wt->b_o_cross, x1, n_q, EDDA_ACT_NONE, x2, n_q, D, D, s),
+            "cross output projection");
+  EDDA_STEP(edda::launch_layer_norm(x2, n_q, D, wt->ln3_gamma, wt->ln3_beta, h, s), "LN3");
+  EDDA_STEP(edda::launch_gemm(h, wt->w_fc1, wt->b_fc1, nullptr, 1, EDDA_ACT_GELU, f, n_q, EDDA_D_FF, D, s), "fc1");
+  EDDA_STEP(edda::launch_gemm(f, wt->w_fc2, wt->b_fc2, x2, n_q, EDDA_ACT_NONE, y, n_q, D, EDDA_D_FF, s), "fc2");
+#undef EDDA_STEP
+  return ok();
+}
+
+edda_status edda_cross_kv(const void* enc, int32_t n_frames, const void* w_k, const void* w_v, const void* b_v,
+                          void* cross_k, void* cross_v, void* stream) {
+  const char* fn = "edda_cross_kv";
+  if (!enc || !w_k || !w_v || !cross_k || !cross_v)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: enc, w_k, w_v, cross_k and cross_v must be non-null", fn);
+  if (n_frames < 1 || n_frames >= kMaxRows / EDDA_D_MODEL || !gemm_tiles_ok(n_frames, EDDA_D_MODEL))
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_frames = %d out of range", fn, n_frames);
+  const void* all[] = {enc, w_k, w_v, b_v, cross_k, cross_v};
+  for (const void* p : all)
+    if (p && !aligned(p, 16)) return fail(EDDA_ERR_MISALIGNED, "%s: pointers must be 16-byte aligned", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = edda::launch_gemm(enc, w_k, nullptr, nullptr, 1, EDDA_ACT_NONE, cross_k, n_frames, EDDA_D_MODEL,
+                                   EDDA_D_MODEL, s);
+  if (e != hipSuccess) return from_hip(e, "edda_cross_kv key projection launch");
+  return from_hip(edda::launch_gemm(enc, w_v, b_v, nullptr, 1, EDDA_ACT_NONE, cross_v, n_frames, EDDA_D_MODEL,
+                                    EDDA_D_MODEL, s),
+                  "edda_cross_kv value projection launch");
 }
 
 }  // extern "C"

@@ -432,6 +432,8 @@ struct Tile {
 
 hipError_t launch_gemm(const void* A, const void* Bt, const void* bias, const void* residual, int res_period,
                        int act, void* C, int M, int N, int K, hipStream_t stream) {
+  if (M <= 16 && K % 32 == 0 && N % 16 == 0)  // the decoder's block rows: weight streaming
+    return launch_skinny_gemm(A, Bt, bias, residual, residual ? res_period : 1, act, C, M, N, K, stream);
   const Epilogue ep{static_cast<const f16*>(bias), static_cast<const f16*>(residual),
                     residual ? res_period : 1, act};
   auto with_epilogue = [&](auto tile) {

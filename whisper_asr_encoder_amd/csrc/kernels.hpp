@@ -28,6 +28,20 @@ hipError_t launch_layer_norm(const void* x, int rows, int features, const void* 
 hipError_t launch_im2col3(const void* x, int batch, long x_batch, int t_in, int channels, long ts, long cs,
                           int stride, void* cols, hipStream_t stream);
 
+// C = act(A * Bt^T + bias) + residual for M <= 16 rows (N % 16 == 0, K % 32 == 0):
+// weights streamed straight into registers, 8-way K split inside a workgroup.
+hipError_t launch_skinny_gemm(const void* A, const void* Bt, const void* bias, const void* residual, int res_period,
+                              int act, void* C, int M, int N, int K, hipStream_t stream);
+
+// Cache slots of the (at most 16) block tokens, passed by value.
+struct Slots {
+  int32_t s[16];
+};
+
+// k_cache[slots[t]] = K row of qkv[t], v_cache[slots[t]] = its V row (caches [slot][1280]).
+hipError_t launch_append_kv(const void* qkv, int n_q, const Slots& slots, void* k_cache, void* v_cache,
+                            hipStream_t stream);
+
 // Flash attention over a packed [batch*seq_len, 3840] QKV buffer into O [batch*seq_len, 1280].
 // chunk_len 0 = whole window; valid[b] = number of admitted key positions of window b.
 hipError_t launch_flash_attn(const void* qkv, void* O, int batch, int seq_len, int chunk_len,
@@ -36,7 +50,8 @@ hipError_t launch_flash_attn(const void* qkv, void* O, int batch, int seq_len, i
 // Split-KV verification attention. part_ml / part_o may be null when n_splits == 1.
 int verify_num_splits(int n_kv);
 size_t verify_workspace_bytes(int n_q, int n_kv);
-hipError_t launch_verify(const void* q, int n_q, const void* k, const void* v, int n_kv,
+// q rows are q_stride elements apart (1280 for a contiguous [n_q, 20, 64] tensor).
+hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, const void* v, int n_kv,
                          const uint32_t* mask, void* o, void* workspace, hipStream_t stream);
 
 }  // namespace edda

@@ -76,7 +76,7 @@ __device__ __forceinline__ float quad_sum(float x) {
 // when n_splits > 1 (they are written by other workgroups, so not restrict).
 template <bool kMasked>
 __global__ __launch_bounds__(kVThreads) void verify_kernel(
-    const f16* __restrict__ q, int n_q, const f16* __restrict__ k, const f16* __restrict__ v,
+    const f16* __restrict__ q, int q_stride, int n_q, const f16* __restrict__ k, const f16* __restrict__ v,
     int n_kv, const uint32_t* __restrict__ mask, int mask_words, f16* __restrict__ o,
     uint32_t* counters, float* part_ml, float* part_o) {
   __shared__ __attribute__((aligned(16))) f16 Vt[kVWaves][kHeadDim * kVtLd];
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
   if constexpr (kMasked) bits = mask[(uint32_t)(q_row * mask_words + min(key0 >> 5, mask_words - 1))];
   f16x8 qf[2], kf[2][2], va[2], vb[2];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) qf[s] = load16(q + (uint32_t)((q_row * kHeads + head) * kHeadDim + 32 * s + 8 * G));
+  for (int s = 0; s < 2; ++s) qf[s] = load16(q + (uint32_t)(q_row * q_stride + head * kHeadDim + 32 * s + 8 * G));
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     const int key = min(key0 + 16 * blk + r16, last_key);
@@ -282,7 +282,7 @@ size_t verify_workspace_bytes(int n_q, int n_kv) {
   return kCounterBytes + (size_t)s * n_q * kHeads * (2 + kHeadDim) * sizeof(float);
 }
 
-hipError_t launch_verify(const void* q, int n_q, const void* k, const void* v, int n_kv,
+hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, const void* v, int n_kv,
                          const uint32_t* mask, void* o, void* workspace, hipStream_t stream) {
   const int n_splits = verify_num_splits(n_kv);
   const int mask_words = (n_kv + 31) / 32;
@@ -296,11 +296,11 @@ hipError_t launch_verify(const void* q, int n_q, const void* k, const void* v, i
   }
   const dim3 grid(n_splits, kHeads);
   if (mask)
-    hipLaunchKernelGGL(verify_kernel<true>, grid, dim3(kVThreads), 0, stream, static_cast<const f16*>(q), n_q,
+    hipLaunchKernelGGL(verify_kernel<true>, grid, dim3(kVThreads), 0, stream, static_cast<const f16*>(q), q_stride, n_q,
                        static_cast<const f16*>(k), static_cast<const f16*>(v), n_kv, mask, mask_words,
                        static_cast<f16*>(o), counters, part_ml, part_o);
   else
-    hipLaunchKernelGGL(verify_kernel<false>, grid, dim3(kVThreads), 0, stream, static_cast<const f16*>(q), n_q,
+    hipLaunchKernelGGL(verify_kernel<false>, grid, dim3(kVThreads), 0, stream, static_cast<const f16*>(q), q_stride, n_q,
                        static_cast<const f16*>(k), static_cast<const f16*>(v), n_kv, mask, mask_words,
                        static_cast<f16*>(o), counters, part_ml, part_o);
   return hipGetLastError();

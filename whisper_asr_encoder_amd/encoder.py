@@ -134,3 +134,52 @@ class FullEncoder:
         for layer in range(self.layers):
             self.layer(self.x, layer, self.x, stream)
         _lib.edda_layer_norm(self.x, self.stem_w["lnp_g"], self.stem_w["lnp_b"], out, stream)
+
+
+class DecoderVerifier:
+    """Decoder verification layers with device-resident weights, per-layer cross K/V of one
+    encoder output and a shared workspace (zero-filled once: its leading arrival counters
+    must start at zero). Every step runs in libedda.so."""
+
+    def __init__(self, layer_weights, max_kv: int, n_frames: int = 1500, device="cuda"):
+        import torch
+        self.torch = torch
+        self.device = device
+        self.n_frames = int(n_frames)
+        self._keep, self.structs = [], []
+        for w in layer_weights:
+            t = dict(ln1_gamma=self._dev(w.ln1_g), ln1_beta=self._dev(w.ln1_b),
+                     w_qkv=self._dev(_lib.linear_layout(w.w_qkv)), b_qkv=self._dev(w.b_qkv),
+                     w_o=self._dev(_lib.linear_layout(w.w_o)), b_o=self._dev(w.b_o),
+                     ln2_gamma=self._dev(w.ln2_g), ln2_beta=self._dev(w.ln2_b),
+                     w_q_cross=self._dev(_lib.linear_layout(w.w_qc)), b_q_cross=self._dev(w.b_qc),
+                     w_o_cross=self._dev(_lib.linear_layout(w.w_oc)), b_o_cross=self._dev(w.b_oc),
+                     ln3_gamma=self._dev(w.ln3_g), ln3_beta=self._dev(w.ln3_b),
+                     w_fc1=self._dev(_lib.linear_layout(w.w_fc1)), b_fc1=self._dev(w.b_fc1),
+                     w_fc2=self._dev(_lib.linear_layout(w.w_fc2)), b_fc2=self._dev(w.b_fc2),
+                     w_ck=self._dev(_lib.linear_layout(w.w_ck)), w_cv=self._dev(_lib.linear_layout(w.w_cv)),
+                     b_cv=self._dev(w.b_cv))
+            self._keep.append(t)
+            self.structs.append(_lib.DecoderLayerWeights(
+                **{k: v.data_ptr() for k, v in t.items() if k not in ("w_ck", "w_cv", "b_cv")}))
+        shape = (self.n_frames, _lib.N_HEADS, _lib.HEAD_DIM)
+        self.cross_k = [torch.empty(shape, dtype=torch.float16, device=device) for _ in self._keep]
+        self.cross_v = [torch.empty(shape, dtype=torch.float16, device=device) for _ in self._keep]
+        nb = _lib.decoder_verify_workspace_bytes(_lib.MAX_VERIFY_QUERIES, max_kv, self.n_frames)
+        self.workspace = torch.zeros(max(nb, _lib.VERIFY_COUNTER_BYTES), dtype=torch.uint8, device=device)
+
+    def _dev(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a)).to(self.device)
+
+    @property
+    def layers(self) -> int:
+        return len(self.structs)
+
+    def set_encoder_output(self, enc, stream=None):
+        """Project the encoder output [n_frames, 1280] into every layer's cross K/V."""
+        for l, t in enumerate(self._keep):
+            _lib.edda_cross_kv(enc, t["w_ck"], t["w_cv"], t["b_cv"], self.cross_k[l], self.cross_v[l], stream)
+
+    def layer(self, x, layer: int, slots, k_cache, v_cache, n_kv, mask_rows, y, stream=None):
+        _lib.edda_decoder_verify_layer(x, slots, k_cache, v_cache, n_kv, mask_rows, self.cross_k[layer],
+                                       self.cross_v[layer], self.structs[layer], y, self.workspace, stream)
