@@ -45,6 +45,16 @@ WORKLOADS = {
         "verify_kernelILb0E": ("verify_cross", ["verify_attn.hip"]),
     }),
     # The whole encoder: fc1 is the only 128x256-tile GEMM (N = 5120, GELU, no residual).
+    # The decoder verification pass: block-sized GEMMs by (activation, residual) variant.
+    "decoder": ("decoder verification pass, 32 layers, 16-token block, 360-slot cache, 1500 frames", {
+        "skinny_gemm_kernelILi0ELb0E": ("skinny_gemm_plain", ["skinny.hip"]),
+        "skinny_gemm_kernelILi1ELb0E": ("skinny_gemm_gelu", ["skinny.hip"]),
+        "skinny_gemm_kernelILi0ELb1E": ("skinny_gemm_residual", ["skinny.hip"]),
+        "append_kv_kernel": ("append_kv", ["skinny.hip"]),
+        "layer_norm_kernelILi5E": ("layer_norm_block", ["norm_im2col.hip"]),
+        "verify_kernelILb1E": ("verify_self", ["verify_attn.hip"]),
+        "verify_kernelILb0E": ("verify_cross", ["verify_attn.hip"]),
+    }),
     "encoder": ("whole encoder of one 30 s window (stem, 32 pre-norm layers, final LayerNorm)", {
         "gemm_bias_kernelILi128ELi256E": ("fc1_gemm", ["gemm.hip"]),
         "layer_norm_kernelILi5E": ("layer_norm", ["norm_im2col.hip"]),
@@ -100,6 +110,8 @@ def summarize(trace_dir, fetch_dir, write_dir, out_dir, command, workload="windo
     title, kernels = WORKLOADS[workload]
     extra = {c: counter_values(extra_dir, c) for c in EXTRA_COUNTERS} if extra_dir else {}
     stats = kernel_stats(trace_dir)
+    if fetch_dir is None:  # kernel trace only
+        return trace_only(stats, kernels, title, out_dir, command, workload)
     fetch = counter_values(fetch_dir, "FETCH_SIZE")
     write = counter_values(write_dir, "WRITE_SIZE")
     copy_f, copy_w = _match(fetch, COPY_KERNEL), _match(write, COPY_KERNEL)
@@ -151,18 +163,40 @@ def summarize(trace_dir, fetch_dir, write_dir, out_dir, command, workload="windo
     return traffic
 
 
+def trace_only(stats, kernels, title, out_dir, command, workload):
+    """One summary file for a workload profiled with the kernel trace alone."""
+    os.makedirs(out_dir, exist_ok=True)
+    out = {}
+    with open(os.path.join(out_dir, f"{workload}_kernels.md"), "w") as f:
+        f.write(f"# kernels of the {title}\n\n")
+        f.write("Commands (run from the repository root on one MI355X):\n\n```\n" + command.strip() + "\n```\n\n")
+        f.write("| kernel | symbol fragment | dispatches | mean | min / max |\n|---|---|---|---|---|\n")
+        for frag, (key, _) in kernels.items():
+            st = [v for k, v in stats.items() if frag in k]
+            if not st:
+                continue
+            calls = sum(v["calls"] for v in st)
+            mean = sum(v["avg_ns"] * v["calls"] for v in st) / calls
+            lo, hi = min(v["min_ns"] for v in st), max(v["max_ns"] for v in st)
+            out[key] = {"calls": calls, "mean_us": round(mean / 1e3, 2)}
+            f.write(f"| {key} | `{frag}` | {calls} | {mean / 1e3:.2f} us | {lo / 1e3:.2f} / {hi / 1e3:.2f} us |\n")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("trace_dir")
-    ap.add_argument("fetch_dir")
-    ap.add_argument("write_dir")
+    ap.add_argument("fetch_dir", help="FETCH_SIZE run, or - for a kernel-trace-only summary")
+    ap.add_argument("write_dir", help="WRITE_SIZE run, or -")
     ap.add_argument("out_dir")
     ap.add_argument("--command", required=True)
     ap.add_argument("--workload", default="window", choices=sorted(WORKLOADS))
     ap.add_argument("--extra-pmc", default=None, help="directory of a rocprofv3 --pmc run of EXTRA_COUNTERS")
     a = ap.parse_args()
-    print(json.dumps(summarize(a.trace_dir, a.fetch_dir, a.write_dir, a.out_dir, a.command, a.workload,
-                               a.extra_pmc), indent=1))
+    fetch = None if a.fetch_dir == "-" else a.fetch_dir
+    write = None if a.write_dir == "-" else a.write_dir
+    print(json.dumps(summarize(a.trace_dir, fetch, write, a.out_dir, a.command, a.workload, a.extra_pmc),
+                     indent=1))
 
 
 if __name__ == "__main__":
