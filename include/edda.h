@@ -51,7 +51,9 @@ extern "C" {
 #define EDDA_MAX_VERIFY_QUERIES 16
 #define EDDA_D_FF 5120
 /* Leading bytes of the verification workspace that hold its arrival counters. */
-#define EDDA_VERIFY_COUNTER_BYTES 5120
+#define EDDA_VERIFY_COUNTER_BYTES 16384
+/* Most heads edda_verify_attn_ex handles (head_dim is always 64). */
+#define EDDA_MAX_VERIFY_HEADS 64
 
 typedef enum {
   EDDA_OK = 0,
@@ -161,7 +163,8 @@ edda_status edda_verify_attn(const void* q, int32_t n_q, const void* k, const vo
 /* Bytes of workspace edda_verify_attn needs: 0 for caches of at most 128 keys (one workgroup
  * per head) or an invalid shape; longer caches split the keys into 128-key ranges, one
  * workgroup each, whose fp32 partial results the last workgroup of each head to finish merges
- * in the same launch: EDDA_VERIFY_COUNTER_BYTES + splits * n_q * 20 * 66 * 4 bytes. */
+ * in the same launch: EDDA_VERIFY_COUNTER_BYTES + splits * n_q * 20 * 66 * 4 bytes. (The
+ * counter region serves up to EDDA_MAX_VERIFY_HEADS heads.) */
 size_t edda_verify_workspace_bytes(int32_t n_q, int32_t n_kv);
 
 /* ------------------------------------------------------------------------------------
@@ -344,6 +347,41 @@ size_t edda_decoder_verify_workspace_bytes(int32_t n_q, int32_t n_kv, int32_t n_
  */
 edda_status edda_cross_kv(const void* enc, int32_t n_frames, const void* w_k, const void* w_v, const void* b_v,
                           void* cross_k, void* cross_v, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Attention variants of the drafter (llama.cpp DSpark diff: common/speculative.cpp, a flag
+ * for causal block-internal attention, non-causal by default; src/models/dflash.cpp,
+ * optional per-head attention sinks passed into the attention call).
+ * ------------------------------------------------------------------------------------ */
+
+typedef enum {
+  EDDA_MASK_ROWS = 0,         /* mask_rows given (as for edda_verify_attn)                        */
+  EDDA_MASK_NONE = 1,         /* every slot admitted (cross-attention, non-causal block)          */
+  EDDA_MASK_CAUSAL_BLOCK = 2  /* the block in the last n_q slots: token t admits 0..n_kv-n_q+t    */
+} edda_mask_mode;
+
+/*
+ * Verification attention with a head count, a mask mode and optional attention sinks:
+ *   o[t,h] = sum_j e^(s_j - m) v[j,h] / (e^(sink_h - m) + sum_j e^(s_j - m)), s_j = q[t,h].k[j,h]/8
+ * over the admitted slots j, m = max(sink_h, max_j s_j) (a sink is one extra logit, in
+ * scaled-score units, with a zero value; -inf or NULL sinks = none; a query with neither an
+ * admitted slot nor a sink gets 0).
+ *  q          [n_q, n_heads, 64] fp16; k, v [n_kv, n_heads, 64]; o [n_q, n_heads, 64].
+ *  n_heads    in [1, EDDA_MAX_VERIFY_HEADS].
+ *  mask_mode  edda_mask_mode; mask_rows is required for EDDA_MASK_ROWS and ignored otherwise;
+ *             EDDA_MASK_CAUSAL_BLOCK needs n_q <= n_kv.
+ *  sinks      DEVICE fp32 [n_heads] or NULL.
+ *  workspace  at least edda_verify_workspace_bytes_ex(n_q, n_kv, n_heads) bytes, first
+ *             EDDA_VERIFY_COUNTER_BYTES zero before first use (as for edda_verify_attn).
+ * Errors: EDDA_ERR_INVALID_ARGUMENT, EDDA_ERR_MISALIGNED (sinks 4-byte aligned), EDDA_ERR_WORKSPACE,
+ * EDDA_ERR_HIP.
+ */
+edda_status edda_verify_attn_ex(const void* q, int32_t n_q, const void* k, const void* v, int32_t n_kv,
+                                int32_t n_heads, int32_t mask_mode, const uint32_t* mask_rows, const float* sinks,
+                                void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace edda_verify_attn_ex needs (0 for one 128-key split or an invalid shape). */
+size_t edda_verify_workspace_bytes_ex(int32_t n_q, int32_t n_kv, int32_t n_heads);
 
 /* Text of the calling thread's most recent error ("" after a successful call). */
 const char* edda_last_error(void);

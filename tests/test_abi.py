@@ -51,6 +51,10 @@ def test_header_constants_match_binding():
     consts = dict(re.findall(r"#define (EDDA_\w+) (\d+)", text))
     assert int(consts["EDDA_VERIFY_COUNTER_BYTES"]) == _lib.VERIFY_COUNTER_BYTES
     assert int(consts["EDDA_MAX_VERIFY_QUERIES"]) == _lib.MAX_VERIFY_QUERIES
+    assert int(consts["EDDA_MAX_VERIFY_HEADS"]) == _lib.MAX_VERIFY_HEADS
+    enum = dict(re.findall(r"(EDDA_MASK_\w+) = (\d+)", text))
+    assert {k: int(v) for k, v in enum.items()} == {"EDDA_MASK_ROWS": _lib.MASK_ROWS, "EDDA_MASK_NONE": _lib.MASK_NONE,
+                                                     "EDDA_MASK_CAUSAL_BLOCK": _lib.MASK_CAUSAL_BLOCK}
     assert int(consts["EDDA_D_MODEL"]) == _lib.D_MODEL
 
 
@@ -129,6 +133,31 @@ def ver(lib, q=A, n_q=16, k=A, v=A, n_kv=448, mask=None, o=B, ws=B + (1 << 24), 
 ])
 def test_verify_attn_rejects(lib, kw, status):
     assert ver(lib, **kw) == status
+
+
+def ver_ex(lib, q=A, n_q=16, k=A, v=A, n_kv=448, h=8, mode=1, mask=None, sinks=None, o=B, ws=B + (1 << 24),
+           ws_bytes=1 << 30):
+    return lib.edda_verify_attn_ex(q, n_q, k, v, n_kv, h, mode, mask, sinks, o, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(n_q=0), INVALID), (dict(n_q=17), INVALID),
+    (dict(h=0), INVALID), (dict(h=65), INVALID), (dict(n_kv=0), INVALID), (dict(n_kv=1 << 20, h=64), INVALID),
+    (dict(mode=3), INVALID), (dict(mode=-1), INVALID), (dict(mode=0), INVALID),
+    (dict(mode=2, n_q=16, n_kv=15), INVALID), (dict(q=ODD), MISALIGNED), (dict(sinks=A + 2), MISALIGNED),
+    (dict(mode=0, mask=A + 2), MISALIGNED), (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+])
+def test_verify_attn_ex_rejects(lib, kw, status):
+    assert ver_ex(lib, **kw) == status
+
+
+def test_verify_workspace_bytes_ex(lib):
+    C = _lib.VERIFY_COUNTER_BYTES
+    assert lib.edda_verify_workspace_bytes_ex(16, 128, 64) == 0
+    assert lib.edda_verify_workspace_bytes_ex(16, 129, 64) == C + 2 * 16 * 64 * 66 * 4
+    assert lib.edda_verify_workspace_bytes_ex(4, 1500, 20) == lib.edda_verify_workspace_bytes(4, 1500)
+    assert lib.edda_verify_workspace_bytes_ex(4, 1500, 0) == 0
+    assert lib.edda_verify_workspace_bytes_ex(4, 1500, 65) == 0
 
 
 def test_mask_packing_bit_order():

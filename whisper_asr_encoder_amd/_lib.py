@@ -21,7 +21,7 @@ N_HEADS = 20
 HEAD_DIM = 64
 QKV_COLS = 3 * D_MODEL
 MAX_VERIFY_QUERIES = 16
-VERIFY_COUNTER_BYTES = 5120  # leading workspace bytes of edda_verify_attn: zero before first use
+VERIFY_COUNTER_BYTES = 16384  # leading workspace bytes of edda_verify_attn: zero before first use
 
 STATUS = {0: "EDDA_OK", 1: "EDDA_ERR_INVALID_ARGUMENT", 2: "EDDA_ERR_UNSUPPORTED",
           3: "EDDA_ERR_MISALIGNED", 4: "EDDA_ERR_WORKSPACE", 5: "EDDA_ERR_HIP"}
@@ -31,6 +31,7 @@ EXPORTS = ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_encode
            "edda_verify_workspace_bytes", "edda_linear", "edda_layer_norm", "edda_encoder_layer",
            "edda_encoder_layer_workspace_bytes", "edda_encoder_stem", "edda_encoder_stem_workspace_bytes",
            "edda_decoder_verify_layer", "edda_decoder_verify_workspace_bytes", "edda_cross_kv",
+           "edda_verify_attn_ex", "edda_verify_workspace_bytes_ex",
            "edda_last_error", "edda_version")
 
 D_FF = 5120
@@ -92,11 +93,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edda_decoder_verify_workspace_bytes.argtypes = [i32, i32, i32]
     lib.edda_decoder_verify_workspace_bytes.restype = sz
     lib.edda_cross_kv.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
+    lib.edda_verify_attn_ex.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.edda_verify_workspace_bytes_ex.argtypes = [i32, i32, i32]
+    lib.edda_verify_workspace_bytes_ex.restype = sz
     lib.edda_last_error.restype = ctypes.c_char_p
     lib.edda_version.restype = ctypes.c_char_p
     for name in ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_verify_attn", "edda_linear",
                  "edda_layer_norm", "edda_encoder_layer", "edda_encoder_stem", "edda_decoder_verify_layer",
-                 "edda_cross_kv"):
+                 "edda_cross_kv", "edda_verify_attn_ex"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -360,3 +364,29 @@ def edda_cross_kv(enc, w_k, w_v, b_v, cross_k, cross_v, stream=None):
     _require(cross_v, "cross_v", (n, N_HEADS, HEAD_DIM), torch.float16)
     _check(lib.edda_cross_kv(_ptr(enc), n, _ptr(w_k), _ptr(w_v), _ptr(b_v), _ptr(cross_k), _ptr(cross_v),
                              _stream(stream)))
+
+
+MASK_ROWS, MASK_NONE, MASK_CAUSAL_BLOCK = 0, 1, 2
+MAX_VERIFY_HEADS = 64
+
+
+def verify_workspace_bytes_ex(n_q: int, n_kv: int, n_heads: int) -> int:
+    return int(load().edda_verify_workspace_bytes_ex(n_q, n_kv, n_heads))
+
+
+def edda_verify_attn_ex(q, k, v, o, mask_mode=MASK_NONE, mask_rows=None, sinks=None, workspace=None, stream=None):
+    """Verification attention with n_heads = q.shape[1] (head_dim 64), a mask mode and optional
+    fp32 sinks [n_heads] (device)."""
+    lib = load()
+    torch = _require(q, "q")
+    n_q, n_heads, _ = q.shape
+    n_kv = k.shape[0]
+    _require(q, "q", (n_q, n_heads, HEAD_DIM), torch.float16)
+    _require(k, "k", (n_kv, n_heads, HEAD_DIM), torch.float16)
+    _require(v, "v", (n_kv, n_heads, HEAD_DIM), torch.float16)
+    _require(o, "o", (n_q, n_heads, HEAD_DIM), torch.float16)
+    if sinks is not None:
+        _require(sinks, "sinks", (n_heads,), torch.float32)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.edda_verify_attn_ex(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, n_heads, mask_mode, _ptr(mask_rows),
+                                   _ptr(sinks), _ptr(o), _ptr(workspace), ws_bytes, _stream(stream)))

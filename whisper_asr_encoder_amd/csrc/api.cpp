@@ -123,7 +123,7 @@ edda_status edda_encoder_attn(const void* qkv, int32_t batch, int32_t seq_len, i
 
 size_t edda_verify_workspace_bytes(int32_t n_q, int32_t n_kv) {
   if (n_q < 1 || n_q > EDDA_MAX_VERIFY_QUERIES || n_kv < 1) return 0;
-  return edda::verify_workspace_bytes(n_q, n_kv);
+  return edda::verify_workspace_bytes(n_q, n_kv, EDDA_N_HEADS);
 }
 
 edda_status edda_verify_attn(const void* q, int32_t n_q, const void* k, const void* v, int32_t n_kv,
@@ -138,11 +138,12 @@ edda_status edda_verify_attn(const void* q, int32_t n_q, const void* k, const vo
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       (mask_rows && !aligned(mask_rows, 4)) || (workspace && !aligned(workspace, 16)))
     return fail(EDDA_ERR_MISALIGNED, "edda_verify_attn: q/k/v/o/workspace must be 16-byte and mask_rows 4-byte aligned");
-  const size_t need = edda::verify_workspace_bytes(n_q, n_kv);
+  const size_t need = edda::verify_workspace_bytes(n_q, n_kv, EDDA_N_HEADS);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(EDDA_ERR_WORKSPACE, "edda_verify_attn: workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
-  return from_hip(edda::launch_verify(q, EDDA_D_MODEL, n_q, k, v, n_kv, mask_rows, o, workspace,
+  return from_hip(edda::launch_verify(q, EDDA_D_MODEL, n_q, k, v, n_kv, EDDA_N_HEADS,
+                                      mask_rows ? EDDA_MASK_ROWS : EDDA_MASK_NONE, mask_rows, nullptr, o, workspace,
                                       static_cast<hipStream_t>(stream)),
                   "edda_verify_attn launch");
 }
@@ -317,7 +318,8 @@ struct DecoderWs {
 
 DecoderWs decoder_ws(int32_t n_q, int32_t n_kv, int32_t n_frames) {
   DecoderWs w{};
-  size_t v1 = edda::verify_workspace_bytes(n_q, n_kv), v2 = edda::verify_workspace_bytes(n_q, n_frames);
+  size_t v1 = edda::verify_workspace_bytes(n_q, n_kv, EDDA_N_HEADS);
+  size_t v2 = edda::verify_workspace_bytes(n_q, n_frames, EDDA_N_HEADS);
   size_t off = align256(v1 > v2 ? v1 : v2);
   if (off < EDDA_VERIFY_COUNTER_BYTES) off = EDDA_VERIFY_COUNTER_BYTES;
   w.verify = 0;
@@ -386,11 +388,15 @@ edda_status edda_decoder_verify_layer(const void* x, int32_t n_q, const int32_t*
   EDDA_STEP(edda::launch_layer_norm(x, n_q, D, wt->ln1_gamma, wt->ln1_beta, h, s), "LN1");
   EDDA_STEP(edda::launch_gemm(h, wt->w_qkv, wt->b_qkv, nullptr, 1, EDDA_ACT_NONE, qkv, n_q, EDDA_QKV_COLS, D, s), "QKV");
   EDDA_STEP(edda::launch_append_kv(qkv, n_q, sl, k_cache, v_cache, s), "cache append");
-  EDDA_STEP(edda::launch_verify(qkv, EDDA_QKV_COLS, n_q, k_cache, v_cache, n_kv, mask_rows, o, ws, s), "self-attention");
+  EDDA_STEP(edda::launch_verify(qkv, EDDA_QKV_COLS, n_q, k_cache, v_cache, n_kv, EDDA_N_HEADS,
+                                mask_rows ? EDDA_MASK_ROWS : EDDA_MASK_NONE, mask_rows, nullptr, o, ws, s),
+            "self-attention");
   EDDA_STEP(edda::launch_gemm(o, wt->w_o, wt->b_o, x, n_q, EDDA_ACT_NONE, x1, n_q, D, D, s), "self output projection");
   EDDA_STEP(edda::launch_layer_norm(x1, n_q, D, wt->ln2_gamma, wt->ln2_beta, h, s), "LN2");
   EDDA_STEP(edda::launch_gemm(h, wt->w_q_cross, wt->b_q_cross, nullptr, 1, EDDA_ACT_NONE, o, n_q, D, D, s), "cross query");
-  EDDA_STEP(edda::launch_verify(o, D, n_q, cross_k, cross_v, n_frames, nullptr, h, ws, s), "cross-attention");
+  EDDA_STEP(edda::launch_verify(o, D, n_q, cross_k, cross_v, n_frames, EDDA_N_HEADS, EDDA_MASK_NONE, nullptr,
+                                nullptr, h, ws, s),
+            "cross-attention");
   EDDA_STEP(edda::launch_gemm(h, wt->w_o_cross, wt->b_o_cross, x1, n_q, EDDA_ACT_NONE, x2, n_q, D, D, s),
             "cross output projection");
   EDDA_STEP(edda::launch_layer_norm(x2, n_q, D, wt->ln3_gamma, wt->ln3_beta, h, s), "LN3");
@@ -417,6 +423,45 @@ edda_status edda_cross_kv(const void* enc, int32_t n_frames, const void* w_k, co
   return from_hip(edda::launch_gemm(enc, w_v, b_v, nullptr, 1, EDDA_ACT_NONE, cross_v, n_frames, EDDA_D_MODEL,
                                     EDDA_D_MODEL, s),
                   "edda_cross_kv value projection launch");
+}
+
+
+size_t edda_verify_workspace_bytes_ex(int32_t n_q, int32_t n_kv, int32_t n_heads) {
+  if (n_q < 1 || n_q > EDDA_MAX_VERIFY_QUERIES || n_kv < 1 || n_heads < 1 || n_heads > EDDA_MAX_VERIFY_HEADS)
+    return 0;
+  if ((int64_t)n_kv * n_heads * 64 >= kMaxRows) return 0;
+  return edda::verify_workspace_bytes(n_q, n_kv, n_heads);
+}
+
+edda_status edda_verify_attn_ex(const void* q, int32_t n_q, const void* k, const void* v, int32_t n_kv,
+                                int32_t n_heads, int32_t mask_mode, const uint32_t* mask_rows, const float* sinks,
+                                void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "edda_verify_attn_ex";
+  if (!q || !k || !v || !o) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: q, k, v and o must be non-null", fn);
+  if (n_q < 1 || n_q > EDDA_MAX_VERIFY_QUERIES)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_q = %d outside [1, %d]", fn, n_q, EDDA_MAX_VERIFY_QUERIES);
+  if (n_heads < 1 || n_heads > EDDA_MAX_VERIFY_HEADS)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_heads = %d outside [1, %d]", fn, n_heads, EDDA_MAX_VERIFY_HEADS);
+  if (n_kv < 1 || (int64_t)n_kv * n_heads * 64 >= kMaxRows)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_kv = %d out of range", fn, n_kv);
+  if (mask_mode != EDDA_MASK_ROWS && mask_mode != EDDA_MASK_NONE && mask_mode != EDDA_MASK_CAUSAL_BLOCK)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: unknown mask_mode %d", fn, mask_mode);
+  if (mask_mode == EDDA_MASK_ROWS && !mask_rows)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: EDDA_MASK_ROWS needs mask_rows", fn);
+  if (mask_mode == EDDA_MASK_CAUSAL_BLOCK && n_q > n_kv)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: a causal block needs n_q <= n_kv", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (mask_mode == EDDA_MASK_ROWS && !aligned(mask_rows, 4)) || (sinks && !aligned(sinks, 4)) ||
+      (workspace && !aligned(workspace, 16)))
+    return fail(EDDA_ERR_MISALIGNED, "%s: q/k/v/o/workspace must be 16-byte, mask_rows and sinks 4-byte aligned", fn);
+  const size_t need = edda::verify_workspace_bytes(n_q, n_kv, n_heads);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(EDDA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  return from_hip(edda::launch_verify(q, n_heads * 64, n_q, k, v, n_kv, n_heads, mask_mode,
+                                      mask_mode == EDDA_MASK_ROWS ? mask_rows : nullptr, sinks, o, workspace,
+                                      static_cast<hipStream_t>(stream)),
+                  "edda_verify_attn_ex launch");
 }
 
 }  // extern "C"

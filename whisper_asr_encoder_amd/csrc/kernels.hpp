@@ -48,10 +48,12 @@ hipError_t launch_flash_attn(const void* qkv, void* O, int batch, int seq_len, i
                              const int32_t* valid_host, hipStream_t stream);
 
 // Split-KV verification attention. part_ml / part_o may be null when n_splits == 1.
+// mask_mode: 0 explicit rows (mask), 1 none, 2 causal block; sinks: fp32 [n_heads] or null.
+// q rows are q_stride elements apart (n_heads * 64 for a contiguous [n_q, n_heads, 64] tensor).
 int verify_num_splits(int n_kv);
-size_t verify_workspace_bytes(int n_q, int n_kv);
-// q rows are q_stride elements apart (1280 for a contiguous [n_q, 20, 64] tensor).
-hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, const void* v, int n_kv,
-                         const uint32_t* mask, void* o, void* workspace, hipStream_t stream);
+size_t verify_workspace_bytes(int n_q, int n_kv, int n_heads);
+hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, const void* v, int n_kv, int n_heads,
+                         int mask_mode, const uint32_t* mask, const float* sinks, void* o, void* workspace,
+                         hipStream_t stream);
 
 }  // namespace edda

@@ -16,6 +16,12 @@
 // counter; the last to arrive merges every split of its head:
 //   m = max_s m_s,  l = sum_s l_s 2^(m_s - m),  O = sum_s o_s 2^(m_s - m) / l,
 // and sets the counter back to zero.  A query with no admitted key gets O = 0.
+//
+// Variants for the drafter's attention (llama.cpp DSpark diff): the head count is a runtime
+// value (head_dim 64); the mask is explicit rows, none, or the causal block (query t of the
+// block in the last n_q slots admits slots 0..n_kv-n_q+t) computed in the kernel; optional
+// per-head sinks join the final normalization as one extra logit with a zero value:
+//   M' = max(M, sink), L' = L 2^(M - M') + 2^(sink - M'), O = sum 2^(M - M') / L'.
 #include <math.h>
 
 #include "device.hpp"
@@ -33,8 +39,9 @@ constexpr int kMaxQ = 16;
 constexpr int kVtLd = kWaveKeys + 4;  // V^T row stride (halves): 72 B, 8-byte aligned
 // Per-head arrival counters at the workspace start, one per 256-byte line so that the
 // heads' atomics do not queue on a shared line.
+constexpr int kMaxHeads = 64;
 constexpr int kCounterStride = 64;  // uint32 words
-constexpr size_t kCounterBytes = (size_t)kHeads * kCounterStride * sizeof(uint32_t);
+constexpr size_t kCounterBytes = (size_t)kMaxHeads * kCounterStride * sizeof(uint32_t);
 static_assert(kCounterBytes == EDDA_VERIFY_COUNTER_BYTES, "counter region size in the public header");
 
 // s_waitcnt immediate: vmcnt 0, expcnt and lgkmcnt at their maxima (no wait).
@@ -72,13 +79,25 @@ __device__ __forceinline__ float quad_sum(float x) {
   return as_f32(r[0]) + as_f32(r[1]);
 }
 
-// grid (n_splits, 20 heads), 256 threads.  counters / part_ml / part_o are used only
+// Fold a per-head sink (log2 units) into the running (M, L) and the accumulator scale.
+__device__ __forceinline__ float apply_sink(float& M, float& L, float s2) {
+  if (s2 == -INFINITY) return 1.0f;
+  const float m2 = fmaxf(M, s2);
+  const float a = M == -INFINITY ? 0.0f : exp2_fast(M - m2);
+  L = L * a + exp2_fast(s2 - m2);
+  M = m2;
+  return a;
+}
+
+enum MaskMode { kMaskRows = 0, kMaskNone = 1, kMaskCausal = 2 };
+
+// grid (n_splits, n_heads), 256 threads.  counters / part_ml / part_o are used only
 // when n_splits > 1 (they are written by other workgroups, so not restrict).
-template <bool kMasked>
+template <int kMode>
 __global__ __launch_bounds__(kVThreads) void verify_kernel(
     const f16* __restrict__ q, int q_stride, int n_q, const f16* __restrict__ k, const f16* __restrict__ v,
-    int n_kv, const uint32_t* __restrict__ mask, int mask_words, f16* __restrict__ o,
-    uint32_t* counters, float* part_ml, float* part_o) {
+    int n_kv, int n_heads, const uint32_t* __restrict__ mask, int mask_words, const float* __restrict__ sinks,
+    f16* __restrict__ o, uint32_t* counters, float* part_ml, float* part_o) {
   __shared__ __attribute__((aligned(16))) f16 Vt[kVWaves][kHeadDim * kVtLd];
   __shared__ float mw[kVWaves][kMaxQ], lw[kVWaves][kMaxQ];
   __shared__ __attribute__((aligned(16))) float ow[kVWaves][kMaxQ][kHeadDim + 4];
@@ -88,7 +107,7 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
   const int r16 = lane & 15, G = lane >> 4;
   const int split = blockIdx.x, head = blockIdx.y, n_splits = gridDim.x;
   const int key0 = split * kSplitKeys + wave * kWaveKeys;  // multiple of 32
-  constexpr int kKvStride = kHeads * kHeadDim;
+  const int kKvStride = n_heads * kHeadDim;
   const int last_key = n_kv - 1;
   const f16x8 z8 = {};
 
@@ -97,7 +116,11 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
   const bool q_ok = r16 < n_q;
   const int q_row = min(r16, n_q - 1);
   uint32_t bits = 0xffffffffu;
-  if constexpr (kMasked) bits = mask[(uint32_t)(q_row * mask_words + min(key0 >> 5, mask_words - 1))];
+  if constexpr (kMode == kMaskRows) bits = mask[(uint32_t)(q_row * mask_words + min(key0 >> 5, mask_words - 1))];
+  if constexpr (kMode == kMaskCausal) {
+    const int last = n_kv - n_q + q_row - key0;  // highest admitted key, relative to key0
+    bits = last < 0 ? 0u : last >= 31 ? 0xffffffffu : (uint32_t)((2ull << last) - 1);
+  }
   f16x8 qf[2], kf[2][2], va[2], vb[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) qf[s] = load16(q + (uint32_t)(q_row * q_stride + head * kHeadDim + 32 * s + 8 * G));
@@ -195,9 +218,13 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
     }
   }
   const bool row_ok = mq < n_q;
-  f16* out = o + ((size_t)mq * kHeads + head) * kHeadDim + d0;
+  f16* out = o + ((size_t)mq * n_heads + head) * kHeadDim + d0;
+  const float sink2 = sinks ? sinks[head] * kLog2e : -INFINITY;
   if (n_splits == 1) {
     if (!row_ok) return;
+    const float a = apply_sink(M, L, sink2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] *= a;
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     const f16x2 lo = pack_rne(acc[0] * inv, acc[1] * inv), hi = pack_rne(acc[2] * inv, acc[3] * inv);
     *reinterpret_cast<f16x4*>(out) = (f16x4){lo[0], lo[1], hi[0], hi[1]};
@@ -211,8 +238,8 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
   // before thread 0 counts the workgroup in; the last workgroup's loads are issued
   // after the count returned.
   // Slot (split s, query mq, head): (m, l) at part_ml[2 slot], o at part_o[64 slot + d0];
-  // slot = (s n_q + mq) 20 + head, all offsets below 2^31 for any valid call.
-  const int slot0 = mq * kHeads + head, slot_step = n_q * kHeads;
+  // slot = (s n_q + mq) n_heads + head, all offsets below 2^31 for any valid call.
+  const int slot0 = mq * n_heads + head, slot_step = n_q * n_heads;
   if (row_ok) {
     const int slot = split * slot_step + slot0;
     store_coherent(part_o + (uint32_t)(slot * kHeadDim + d0), acc[0], acc[1]);
@@ -267,6 +294,9 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
     }
     M = mb;
   }
+  const float a = apply_sink(M, L, sink2);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sum[j] *= a;
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   const f16x2 lo = pack_rne(sum[0] * inv, sum[1] * inv), hi = pack_rne(sum[2] * inv, sum[3] * inv);
   *reinterpret_cast<f16x4*>(out) = (f16x4){lo[0], lo[1], hi[0], hi[1]};
@@ -276,14 +306,15 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
 
 int verify_num_splits(int n_kv) { return (n_kv + kSplitKeys - 1) / kSplitKeys; }
 
-size_t verify_workspace_bytes(int n_q, int n_kv) {
+size_t verify_workspace_bytes(int n_q, int n_kv, int n_heads) {
   const int s = verify_num_splits(n_kv);
   if (s <= 1) return 0;
-  return kCounterBytes + (size_t)s * n_q * kHeads * (2 + kHeadDim) * sizeof(float);
+  return kCounterBytes + (size_t)s * n_q * n_heads * (2 + kHeadDim) * sizeof(float);
 }
 
-hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, const void* v, int n_kv,
-                         const uint32_t* mask, void* o, void* workspace, hipStream_t stream) {
+hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, const void* v, int n_kv, int n_heads,
+                         int mask_mode, const uint32_t* mask, const float* sinks, void* o, void* workspace,
+                         hipStream_t stream) {
   const int n_splits = verify_num_splits(n_kv);
   const int mask_words = (n_kv + 31) / 32;
   uint32_t* counters = nullptr;
@@ -292,18 +323,18 @@ hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, co
   if (n_splits > 1) {
     counters = static_cast<uint32_t*>(workspace);
     part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
-    part_o = part_ml + (size_t)n_splits * n_q * kHeads * 2;
+    part_o = part_ml + (size_t)n_splits * n_q * n_heads * 2;
   }
-  const dim3 grid(n_splits, kHeads);
-  if (mask)
-    hipLaunchKernelGGL(verify_kernel<true>, grid, dim3(kVThreads), 0, stream, static_cast<const f16*>(q), q_stride, n_q,
-                       static_cast<const f16*>(k), static_cast<const f16*>(v), n_kv, mask, mask_words,
+  const dim3 grid(n_splits, n_heads);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kVThreads), 0, stream, static_cast<const f16*>(q), q_stride, n_q,
+                       static_cast<const f16*>(k), static_cast<const f16*>(v), n_kv, n_heads, mask, mask_words, sinks,
                        static_cast<f16*>(o), counters, part_ml, part_o);
-  else
-    hipLaunchKernelGGL(verify_kernel<false>, grid, dim3(kVThreads), 0, stream, static_cast<const f16*>(q), q_stride, n_q,
-                       static_cast<const f16*>(k), static_cast<const f16*>(v), n_kv, mask, mask_words,
-                       static_cast<f16*>(o), counters, part_ml, part_o);
-  return hipGetLastError();
+    return hipGetLastError();
+  };
+  if (mask_mode == kMaskRows) return go(verify_kernel<kMaskRows>);
+  if (mask_mode == kMaskCausal) return go(verify_kernel<kMaskCausal>);
+  return go(verify_kernel<kMaskNone>);
 }
 
 }  // namespace edda
