@@ -31,7 +31,11 @@
 //                 is permuted identically on both operands); V^T fragments are read
 //                 with ds_read_b64_tr_b16 from the row-major V tile.
 // K and V tiles reach LDS by direct-to-LDS DMA (natural row layout, 16-byte chunks
-// XOR-swizzled per row) through a 4-stage ring with one barrier per iteration.
+// XOR-swizzled per row) through a 4-stage ring; the workgroup's Q rows arrive the same way
+// once, ahead of the first tiles, instead of each wave loading its rows from memory (four
+// waves share every query row, and the start of the kernel is bound by that first burst).
+// A wave raises its issue priority for its MFMA phase, so its matrix instructions go out
+// ahead of the partner wave's softmax arithmetic on the same SIMD.
 #include <math.h>
 
 #include "device.hpp"
@@ -67,7 +71,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               ::"v"(g), "s"(lds_addr) : "memory", "m0");
+               ::"v"(g), "s"(lds_addr) : "m0");
 }
 // Wait for this wave's DMA down to n outstanding instructions, then the workgroup
 // barrier.  The scheduling barriers keep every instruction (arithmetic included) on its
@@ -116,7 +120,7 @@ __device__ __forceinline__ void divmod_rcp(int u, int h, float rcp, int& q, int&
 
 __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
     const f16* __restrict__ qkv, f16* __restrict__ O, int seq_len, int seg_len_max, int n_segs,
-    int tiles_per_seg, float rcp_segs, float rcp_tiles, int window0, ValidLens valid) {
+    int tiles_per_seg, float rcp_segs, float rcp_tiles, int window0, int uniform_valid, ValidLens valid) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageB];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
   const int q_begin = seg0 + qt * kBMq;
   if (q_begin >= seg_end) return;  // uniform for the workgroup
   const int k_lo = seg0;
-  const int k_hi = max(k_lo, min(seg0 + seg_len_max, (int)valid.v[wloc]));
+  const int k_hi = max(k_lo, min(seg0 + seg_len_max, uniform_valid >= 0 ? uniform_valid : (int)valid.v[wloc]));
 
   const size_t win_row0 = (size_t)window * seq_len;
   const f16* qkv_w = qkv + win_row0 * kQkvCols;
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
     return;
   }
 
-  f16x8 qf[2][4];  // Q^T fragments, filled once the first tiles are in flight
+  f16x8 qf[2][4];  // Q^T fragments, read from LDS once Q has landed
 
   // DMA duties: wave (qg, quarter) loads quarter's K (qg 0) or V (qg 1) tile: 4 x 8 rows.
   const int n_iter = (k_hi - k_lo + kIterKeys - 1) / kIterKeys;
@@ -213,47 +217,63 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
 
   auto k_tile = [&](int it) { return smem + (it % kStages) * kStageB + quarter * 2 * kTileB; };
 
-  // S^T for tile it.  Only the last tile can extend past k_hi, so only it masks.
-  // dma >= 0: also issue the four DMA instructions of tile dma, one per MFMA pair, so
-  // the address unit never sees a burst (used when no PV phase precedes).
-  auto qk = [&](int it, bool last, int dma) {
-    const char* ks = k_tile(it);
-    f16x8 kf[4];
+  // One MFMA phase: S^T for tile qk_it (if >= 0; only the last tile can extend past k_hi,
+  // so only it masks), then O^T += V^T P^T for tile pv_it (if >= 0).  Every LDS fragment
+  // read of the phase is issued first, so the MFMAs wait for the LDS latency once, and the
+  // scores come first so that they are complete before this wave's next softmax while the
+  // PV products finish.  dma >= 0: also issue the four DMA instructions of tile dma, one
+  // per MFMA pair, so the address unit never sees a burst.
+  auto phase = [&](int pv_it, int qk_it, bool last, int dma) {
+    __builtin_amdgcn_s_setprio(1);
+    f16x8 vfr[2][2], kf[4];
+    if (qk_it >= 0) {
+      const char* ks = k_tile(qk_it);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kf[s] = *reinterpret_cast<const f16x8*>(ks + kfrag_off[s]);
+      for (int s = 0; s < 4; ++s) kf[s] = *reinterpret_cast<const f16x8*>(ks + kfrag_off[s]);
+    }
+    if (pv_it >= 0) {
+      const char* vs = k_tile(pv_it) + kTileB;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      sacc[qb] = mfma_32x32x16(kf[0], qf[qb][0], cneg[qb]);
+      for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
-      for (int s = 1; s < 4; ++s) {
-        sacc[qb] = mfma_32x32x16(kf[s], qf[qb][s], sacc[qb]);
-        if (dma >= 0 && (s & 1)) issue_part(dma, 2 * qb + (s >> 1));
+        for (int db = 0; db < 2; ++db) {
+          const f16x4 lo = read_tr(vs + vtr_off[db][sg][0]);
+          const f16x4 hi = read_tr(vs + vtr_off[db][sg][1]);
+          vfr[sg][db] = (f16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (qk_it >= 0) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        sacc[qb] = mfma_32x32x16(kf[0], qf[qb][0], cneg[qb]);
+#pragma unroll
+        for (int s = 1; s < 4; ++s) {
+          sacc[qb] = mfma_32x32x16(kf[s], qf[qb][s], sacc[qb]);
+          if (pv_it < 0 && dma >= 0 && (s & 1)) issue_part(dma, 2 * qb + (s >> 1));
+        }
       }
     }
-    if (last) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (pv_it >= 0) {
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) oacc[qb][db] = mfma_32x32x16(vfr[sg][db], pf[qb][sg], oacc[qb][db]);
+          if (dma >= 0) issue_part(dma, 2 * sg + db);
+        }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (qk_it >= 0 && last) {
       // Admitted keys of this lane's tile rows: key index kt0 + 8(e>>2) + 4g + (e&3) < k_hi.
-      const int lim = k_hi - (k_lo + it * kIterKeys + quarter * kKT) - 4 * g;
+      const int lim = k_hi - (k_lo + qk_it * kIterKeys + quarter * kKT) - 4 * g;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           if (8 * (e >> 2) + (e & 3) >= lim) sacc[qb][e] = -INFINITY;
-    }
-  };
-  // O^T += V^T P^T for tile it; dma >= 0: one DMA instruction of tile dma per MFMA pair.
-  auto pv = [&](int it, int dma) {
-    const char* vs = k_tile(it) + kTileB;
-#pragma unroll
-    for (int sg = 0; sg < 2; ++sg) {
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const f16x4 lo = read_tr(vs + vtr_off[db][sg][0]);
-        const f16x4 hi = read_tr(vs + vtr_off[db][sg][1]);
-        const f16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) oacc[qb][db] = mfma_32x32x16(vf, pf[qb][sg], oacc[qb][db]);
-        if (dma >= 0) issue_part(dma, 2 * sg + db);
-      }
     }
   };
   // Row maximum of the current tile per query block (both lane halves agree).
@@ -328,14 +348,15 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
 
   // Ping-pong schedule over barrier slots b = 0 .. 2 n_iter + 1 (slot b lies between
   // barrier b and the next one).  Query group 0 runs the MFMA phase of iteration i
-  // (PV of tile i-1, QK of tile i) in slot 2i and the softmax of tile i in slot 2i+1;
+  // (QK of tile i, PV of tile i-1) in slot 2i and the softmax of tile i in slot 2i+1;
   // query group 1 runs one slot later, so on every SIMD one wave of each group alternates
   // MFMA and VALU work against the other.  Both groups pass the same 2 n_iter + 2
   // barriers.  Tile t's stage is read from slot 2t to slot 2t+3, so tile t+2 may be
   // loaded from slot 2t on: each wave spreads its share of tile i+2 over its MFMA phase
   // of iteration i (slot 2i or 2i+1) and waits for tile i before barrier 2i.  The odd
   // barriers only order LDS reads and wait for no memory.  The first and last tiles are
-  // peeled so the steady-state body has no conditions.
+  // peeled so the steady-state body has no conditions.  Q's DMA is issued before tile 0's,
+  // so the wait for tile 0 at barrier 0 covers it too.
   auto even_barrier = [&](int j) {  // barrier 2j: tile j has landed in LDS
     if (j + 1 < n_iter) {
       wait_vmcnt_barrier<IPW>();
@@ -345,88 +366,97 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
   };
   auto odd_barrier = [&]() { plain_barrier(); };
   const int nl = n_iter - 1;  // last tile
+  // The workgroup's 128 query rows reach LDS by DMA into stage 3 (first written by tile 3,
+  // after barrier 2; every wave reads its Q fragments before barrier 1), two instructions
+  // of 8 rows per wave, issued before the first tiles.  Rows past the segment load its last
+  // row (finite values whose outputs are never stored).
+  char* const q_lds = smem + 3 * kStageB;
+  {
+    const uint32_t qst = smem_addr + 3 * kStageB;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = 16 * wave + 8 * j + drow;
+      const int q = min(q_begin + row, seg_end - 1);
+      const int lc = (lane & 7) ^ swz(row);
+      dma16(qkv_w + (size_t)q * kQkvCols + head * kHeadDim + 8 * lc, qst + (16 * wave + 8 * j) * kRowB);
+    }
+  }
   issue(0);
   if (n_iter > 1) issue(1);
-
-  // Q^T fragments: lane holds Q[wq0 + 32 qb + l32][16 s + 8 g .. +7] scaled by log2(e)/8.
-  // Loaded after the first tiles' DMA so both latencies overlap; rows past the segment
-  // load its last row instead (finite values whose outputs are never stored).  The scale
-  // is applied as q c_hi + q c_lo with c_hi = fp16(c), so the product is rounded once.
-  {
+  // Q^T fragments from LDS once tile 0 (and Q, issued before it) has landed: lane holds
+  // Q[wq0 + 32 qb + l32][16 s + 8 g .. +7] scaled by log2(e)/8, applied as q c_hi + q c_lo
+  // with c_hi = fp16(c), so the product is rounded once.
+  auto load_q = [&]() {
     const f16x8 chi = (f16x8)(f16)kQScale;
     const f16x8 clo = (f16x8)(f16)(kQScale - (float)(f16)kQScale);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int q = min(wq0 + 32 * qb + l32, seg_end - 1);
-      const f16* qp = qkv_w + (size_t)q * kQkvCols + head * kHeadDim + 8 * g;
+      const int r = qg * kQW + 32 * qb + l32;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const f16x8 v = load16(qp + 16 * s);
+        const f16x8 v = *reinterpret_cast<const f16x8*>(q_lds + tile_off(r, 16 * s + 8 * g));
         qf[qb][s] = __builtin_elementwise_fma(v, chi, v * clo);
       }
     }
-  }
+  };
+
   const int dma0 = n_iter > 2 ? 2 : -1;
   if (qg == 0) {
     even_barrier(0);
-    qk(0, nl == 0, dma0);
+    load_q();
+    phase(-1, 0, nl == 0, dma0);
     odd_barrier();
     softmax(true);
     int i = 1;
     for (; i + 2 < n_iter; ++i) {
       even_barrier(i);
-      pv(i - 1, i + 2);
-      qk(i, false, -1);
+      phase(i - 1, i, false, i + 2);
       odd_barrier();
       softmax(false);
     }
     if (i < nl) {
       even_barrier(i);
-      pv(i - 1, -1);
-      qk(i, false, -1);
+      phase(i - 1, i, false, -1);
       odd_barrier();
       softmax(false);
     }
     if (nl > 0) {
       even_barrier(nl);
-      pv(nl - 1, -1);
-      qk(nl, true, -1);
+      phase(nl - 1, nl, true, -1);
       odd_barrier();
       softmax(false);
     }
     even_barrier(n_iter);
-    pv(nl, -1);
+    phase(nl, -1, false, -1);
     odd_barrier();
   } else {
     even_barrier(0);
+    load_q();
     odd_barrier();
-    qk(0, nl == 0, dma0);
+    phase(-1, 0, nl == 0, dma0);
     even_barrier(1);
     softmax(true);
     int i = 1;
     for (; i + 2 < n_iter; ++i) {
       odd_barrier();
-      pv(i - 1, i + 2);
-      qk(i, false, -1);
+      phase(i - 1, i, false, i + 2);
       even_barrier(i + 1);
       softmax(false);
     }
     if (i < nl) {
       odd_barrier();
-      pv(i - 1, -1);
-      qk(i, false, -1);
+      phase(i - 1, i, false, -1);
       even_barrier(i + 1);
       softmax(false);
     }
     if (nl > 0) {
       odd_barrier();
-      pv(nl - 1, -1);
-      qk(nl, true, -1);
+      phase(nl - 1, nl, true, -1);
       even_barrier(nl + 1);
       softmax(false);
     }
     odd_barrier();
-    pv(nl, -1);
+    phase(nl, -1, false, -1);
   }
 
   // Merge the four key quarters of each query group in one LDS round (the ring is free:
@@ -512,12 +542,15 @@ hipError_t launch_flash_attn(const void* qkv, void* O, int batch, int seq_len, i
     ValidLens vl;
     for (int b = 0; b < nb; ++b) vl.v[b] = valid_host ? valid_host[w0 + b] : seq_len;
     for (int b = nb; b < kMaxBatchPerLaunch; ++b) vl.v[b] = 0;
+    int uniform = vl.v[0];
+    for (int b = 1; b < nb; ++b)
+      if (vl.v[b] != uniform) uniform = -1;
     const long nwg = (long)nb * n_segs * tiles_per_seg * kHeads;
     if (nwg >= (1L << 24)) return hipErrorInvalidValue;  // the decode's division range
     dim3 grid((unsigned)nwg);
     hipLaunchKernelGGL(flash_attn_kernel, grid, dim3(kThreads), 0, stream,
                        static_cast<const f16*>(qkv), static_cast<f16*>(O), seq_len, seg_len_max,
-                       n_segs, tiles_per_seg, 1.0f / (float)n_segs, 1.0f / (float)tiles_per_seg, w0, vl);
+                       n_segs, tiles_per_seg, 1.0f / (float)n_segs, 1.0f / (float)tiles_per_seg, w0, uniform, vl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
