@@ -41,8 +41,9 @@ WORKLOADS = {
     }),
     "verify": ("block verification, 16 queries, 32 layers (causal self-attention over a "
                "360-slot cache, cross-attention over 1500 frames)", {
-        "verify_kernelILb1E": ("verify_causal", ["verify_attn.hip"]),
-        "verify_kernelILb0E": ("verify_cross", ["verify_attn.hip"]),
+        # Mask mode 0 (mask rows: the causal self-attention), mode 1 (none: cross-attention).
+        "verify_kernelILi0E": ("verify_causal", ["verify_attn.hip"]),
+        "verify_kernelILi1E": ("verify_cross", ["verify_attn.hip"]),
     }),
     # The whole encoder: fc1 is the only 128x256-tile GEMM (N = 5120, GELU, no residual).
     # The decoder verification pass: block-sized GEMMs by (activation, residual) variant.
@@ -52,8 +53,8 @@ WORKLOADS = {
         "skinny_gemm_kernelILi0ELb1E": ("skinny_gemm_residual", ["skinny.hip"]),
         "append_kv_kernel": ("append_kv", ["skinny.hip"]),
         "layer_norm_kernelILi5E": ("layer_norm_block", ["norm_im2col.hip"]),
-        "verify_kernelILb1E": ("verify_self", ["verify_attn.hip"]),
-        "verify_kernelILb0E": ("verify_cross", ["verify_attn.hip"]),
+        "verify_kernelILi0E": ("verify_self", ["verify_attn.hip"]),
+        "verify_kernelILi1E": ("verify_cross", ["verify_attn.hip"]),
     }),
     "encoder": ("whole encoder of one 30 s window (stem, 32 pre-norm layers, final LayerNorm)", {
         "gemm_bias_kernelILi128ELi256E": ("fc1_gemm", ["gemm.hip"]),
