@@ -154,3 +154,56 @@ def test_decoder_layer_short_cache_in_place(torch):
     say("decoder layer: cache of 16 slots (the block alone), y = x in place")
     y, _, _, ref, _, _, _ = run_layer(torch, 2, 4, "causal", n_kv=16, in_place=True)
     check(y, ref["y"], "y")
+
+
+@pytest.mark.parametrize("trial,layer,kind", [(0, 3, "causal"), (2, 9, "tree")])
+def test_decoder_layer_matches_composition_of_public_entries(torch, trial, layer, kind):
+    """The layer's fused launches (LayerNorm inside the block GEMMs, the cache append in the
+    QKV epilogue, split K for the 1280-wide outputs) against the public entry points step by
+    step (edda_layer_norm, edda_linear, edda_verify_attn, the append done by indexing): the
+    cache rows bit for bit (LayerNorm and QKV arithmetic are the same code), y to the layer
+    bar (split K groups the fp32 sums differently)."""
+    from whisper_asr_encoder_amd.encoder import DecoderVerifier, VerifyAttention
+    say(f"decoder layer vs composed public entries: trial {trial} layer {layer} {kind}")
+    w = I.decoder_layer_weights(layer)
+    case = I.verify_self_case(trial, layer) if kind == "causal" else I.verify_tree_case(trial, layer)
+    n_q, nk = case.q.shape[0], case.n_kv
+    slots = list(range(nk - n_q, nk)) if kind == "causal" else [int(s) for s in case.query_slots]
+    cap = nk + 4
+    kc = np.zeros((cap, 20, 64), dtype=np.float16)
+    vc = np.zeros((cap, 20, 64), dtype=np.float16)
+    kc[:nk], vc[:nk] = case.k, case.v
+    x = dev(torch, I.decoder_block_input(trial, n_q))
+    dv = DecoderVerifier([w], max_kv=cap)
+    dv.set_encoder_output(dev(torch, I.encoder_workload(1, layers=1).x))
+    mask = None if case.mask is None else VerifyRows(torch, case.mask)
+    # Fused layer.
+    k_f, v_f = dev(torch, kc), dev(torch, vc)
+    y_f = torch.empty((n_q, 1280), dtype=torch.float16, device="cuda")
+    dv.layer(x, 0, slots, k_f, v_f, nk, mask, y_f)
+    # The same layer from public entry points.
+    t = dv._keep[0]
+    k_c, v_c = dev(torch, kc), dev(torch, vc)
+    va = VerifyAttention(max(cap, 1500))
+    e = lambda *shape: torch.empty(shape, dtype=torch.float16, device="cuda")
+    h1, qkv = e(n_q, 1280), e(n_q, 3840)
+    _lib.edda_layer_norm(x, t["ln1_gamma"], t["ln1_beta"], h1)
+    _lib.edda_linear(h1, t["w_qkv"], t["b_qkv"], qkv)
+    idx = torch.tensor(slots, device="cuda")
+    k_c.view(cap, 1280)[idx] = qkv[:, 1280:2560]
+    v_c.view(cap, 1280)[idx] = qkv[:, 2560:]
+    o = e(n_q, 20, 64)
+    va(qkv[:, :1280].contiguous().view(n_q, 20, 64), k_c[:nk], v_c[:nk], mask, o)
+    x1, h2, qc, oc, x2, h3, f, y_c = (e(n_q, 1280), e(n_q, 1280), e(n_q, 1280), e(n_q, 20, 64), e(n_q, 1280),
+                                      e(n_q, 1280), e(n_q, 5120), e(n_q, 1280))
+    _lib.edda_linear(o.view(n_q, 1280), t["w_o"], t["b_o"], x1, residual=x)
+    _lib.edda_layer_norm(x1, t["ln2_gamma"], t["ln2_beta"], h2)
+    _lib.edda_linear(h2, t["w_q_cross"], t["b_q_cross"], qc)
+    va(qc.view(n_q, 20, 64), dv.cross_k[0], dv.cross_v[0], None, oc)
+    _lib.edda_linear(oc.view(n_q, 1280), t["w_o_cross"], t["b_o_cross"], x2, residual=x1)
+    _lib.edda_layer_norm(x2, t["ln3_gamma"], t["ln3_beta"], h3)
+    _lib.edda_linear(h3, t["w_fc1"], t["b_fc1"], f, activation=_lib.ACT_GELU)
+    _lib.edda_linear(f, t["w_fc2"], t["b_fc2"], y_c, residual=x2)
+    torch.cuda.synchronize()
+    assert torch.equal(k_f, k_c) and torch.equal(v_f, v_c), "cache contents differ"
+    check(host(y_f), host(y_c).astype(np.float64), "y, fused vs composed")

@@ -1,6 +1,7 @@
 // C ABI of libedda.so: argument validation, workspace sizing, error text and
 // dispatch of the gfx950 kernels onto the caller's stream.  Every check runs on
 // the host before anything is enqueued; nothing falls back silently.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -312,6 +313,12 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Workspace of the decoder layer: the verification workspace (counters first), then h, qkv,
 // o, x1, x2 and the MLP hidden layer, each 256-byte aligned.
+// Split-K counters of the decoder layer's block GEMMs: after the 20 verification counter
+// lines (256 bytes each) inside the zeroed counter region; 64 bytes per 16-column block.
+constexpr size_t kSplitCounterOffset = (size_t)EDDA_N_HEADS * 256;
+static_assert(kSplitCounterOffset + (EDDA_D_MODEL / 16) * 64 <= EDDA_VERIFY_COUNTER_BYTES,
+              "split-K counters must fit in the counter region");
+
 struct DecoderWs {
   size_t verify, h, qkv, o, x1, x2, f, total;
 };
@@ -320,8 +327,12 @@ DecoderWs decoder_ws(int32_t n_q, int32_t n_kv, int32_t n_frames) {
   DecoderWs w{};
   size_t v1 = edda::verify_workspace_bytes(n_q, n_kv, EDDA_N_HEADS);
   size_t v2 = edda::verify_workspace_bytes(n_q, n_frames, EDDA_N_HEADS);
-  size_t off = align256(v1 > v2 ? v1 : v2);
-  if (off < EDDA_VERIFY_COUNTER_BYTES) off = EDDA_VERIFY_COUNTER_BYTES;
+  // The block GEMMs with 1280 outputs split K; their partials reuse the region after the
+  // counters (launches on one stream never overlap), their counters sit in the counter
+  // lines the 20-head verification leaves unused.
+  const size_t v3 = EDDA_VERIFY_COUNTER_BYTES + std::max(edda::skinny_split_part_bytes(EDDA_D_MODEL, EDDA_D_MODEL),
+                                                         edda::skinny_split_part_bytes(EDDA_D_MODEL, EDDA_D_FF));
+  size_t off = align256(std::max(std::max(v1, v2), v3));
   w.verify = 0;
   const size_t row = (size_t)n_q * 2;
   w.h = off;
@@ -380,28 +391,39 @@ edda_status edda_decoder_verify_layer(const void* x, int32_t n_q, const int32_t*
                 workspace ? workspace_bytes : (size_t)0);
   char* ws = static_cast<char*>(workspace);
   void *h = ws + L.h, *qkv = ws + L.qkv, *o = ws + L.o, *x1 = ws + L.x1, *x2 = ws + L.x2, *f = ws + L.f;
+  void* const sk_counters = ws + kSplitCounterOffset;
+  void* const sk_part = ws + EDDA_VERIFY_COUNTER_BYTES;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int D = EDDA_D_MODEL;
   hipError_t e;
 #define EDDA_STEP(call, what) \
   if ((e = (call)) != hipSuccess) return from_hip(e, "edda_decoder_verify_layer " what " launch")
-  EDDA_STEP(edda::launch_layer_norm(x, n_q, D, wt->ln1_gamma, wt->ln1_beta, h, s), "LN1");
-  EDDA_STEP(edda::launch_gemm(h, wt->w_qkv, wt->b_qkv, nullptr, 1, EDDA_ACT_NONE, qkv, n_q, EDDA_QKV_COLS, D, s), "QKV");
-  EDDA_STEP(edda::launch_append_kv(qkv, n_q, sl, k_cache, v_cache, s), "cache append");
+  // Eight launches: LayerNorms run inside the block GEMMs that consume them, and the QKV
+  // epilogue writes the block's K and V rows into their cache slots.
+  EDDA_STEP(edda::launch_skinny_ln_gemm(x, wt->ln1_gamma, wt->ln1_beta, wt->w_qkv, wt->b_qkv, EDDA_ACT_NONE, qkv, n_q,
+                                        EDDA_QKV_COLS, k_cache, v_cache, &sl, s),
+            "LN1 + QKV + cache append");
   EDDA_STEP(edda::launch_verify(qkv, EDDA_QKV_COLS, n_q, k_cache, v_cache, n_kv, EDDA_N_HEADS,
                                 mask_rows ? EDDA_MASK_ROWS : EDDA_MASK_NONE, mask_rows, nullptr, o, ws, s),
             "self-attention");
-  EDDA_STEP(edda::launch_gemm(o, wt->w_o, wt->b_o, x, n_q, EDDA_ACT_NONE, x1, n_q, D, D, s), "self output projection");
-  EDDA_STEP(edda::launch_layer_norm(x1, n_q, D, wt->ln2_gamma, wt->ln2_beta, h, s), "LN2");
-  EDDA_STEP(edda::launch_gemm(h, wt->w_q_cross, wt->b_q_cross, nullptr, 1, EDDA_ACT_NONE, o, n_q, D, D, s), "cross query");
+  EDDA_STEP(edda::launch_skinny_gemm_split(o, wt->w_o, wt->b_o, x, n_q, EDDA_ACT_NONE, x1, n_q, D, D, sk_counters,
+                                           sk_part, s),
+            "self output projection");
+  EDDA_STEP(edda::launch_skinny_ln_gemm(x1, wt->ln2_gamma, wt->ln2_beta, wt->w_q_cross, wt->b_q_cross, EDDA_ACT_NONE,
+                                        o, n_q, D, nullptr, nullptr, nullptr, s),
+            "LN2 + cross query");
   EDDA_STEP(edda::launch_verify(o, D, n_q, cross_k, cross_v, n_frames, EDDA_N_HEADS, EDDA_MASK_NONE, nullptr,
                                 nullptr, h, ws, s),
             "cross-attention");
-  EDDA_STEP(edda::launch_gemm(h, wt->w_o_cross, wt->b_o_cross, x1, n_q, EDDA_ACT_NONE, x2, n_q, D, D, s),
+  EDDA_STEP(edda::launch_skinny_gemm_split(h, wt->w_o_cross, wt->b_o_cross, x1, n_q, EDDA_ACT_NONE, x2, n_q, D, D,
+                                           sk_counters, sk_part, s),
             "cross output projection");
-  EDDA_STEP(edda::launch_layer_norm(x2, n_q, D, wt->ln3_gamma, wt->ln3_beta, h, s), "LN3");
-  EDDA_STEP(edda::launch_gemm(h, wt->w_fc1, wt->b_fc1, nullptr, 1, EDDA_ACT_GELU, f, n_q, EDDA_D_FF, D, s), "fc1");
-  EDDA_STEP(edda::launch_gemm(f, wt->w_fc2, wt->b_fc2, x2, n_q, EDDA_ACT_NONE, y, n_q, D, EDDA_D_FF, s), "fc2");
+  EDDA_STEP(edda::launch_skinny_ln_gemm(x2, wt->ln3_gamma, wt->ln3_beta, wt->w_fc1, wt->b_fc1, EDDA_ACT_GELU, f, n_q,
+                                        EDDA_D_FF, nullptr, nullptr, nullptr, s),
+            "LN3 + fc1");
+  EDDA_STEP(edda::launch_skinny_gemm_split(f, wt->w_fc2, wt->b_fc2, x2, n_q, EDDA_ACT_NONE, y, n_q, D, EDDA_D_FF,
+                                           sk_counters, sk_part, s),
+            "fc2");
 #undef EDDA_STEP
   return ok();
 }

@@ -38,9 +38,24 @@ struct Slots {
   int32_t s[16];
 };
 
-// k_cache[slots[t]] = K row of qkv[t], v_cache[slots[t]] = its V row (caches [slot][1280]).
-hipError_t launch_append_kv(const void* qkv, int n_q, const Slots& slots, void* k_cache, void* v_cache,
-                            hipStream_t stream);
+// As launch_skinny_gemm (no residual) with A's rows (K = 1280) first normalised by
+// LayerNorm(gamma, beta) inside the kernel.  With k_cache: C is a packed QKV block
+// (N = 3840, act 0) whose K and V columns are also stored into k_cache / v_cache rows
+// slots[m] ([slot][1280]).
+hipError_t launch_skinny_ln_gemm(const void* A, const void* gamma, const void* beta, const void* Bt, const void* bias,
+                                 int act, void* C, int M, int N, void* k_cache, void* v_cache, const Slots* slots,
+                                 hipStream_t stream);
+
+// Split-K form of launch_skinny_gemm (act 0) for narrow outputs: skinny_splits(N, K)
+// workgroups per 16-column block, each over a K range; the last to finish sums their fp32
+// partials (part: skinny_split_part_bytes(N, K) bytes) in split order and applies the
+// epilogue.  counters: N / 16 uint32 counters 64 bytes apart, zero before the call and left
+// zero by it.  One split runs launch_skinny_gemm.
+int skinny_splits(int N, int K);
+size_t skinny_split_part_bytes(int N, int K);
+hipError_t launch_skinny_gemm_split(const void* A, const void* Bt, const void* bias, const void* residual,
+                                    int res_period, int act, void* C, int M, int N, int K, void* counters,
+                                    void* part, hipStream_t stream);
 
 // Flash attention over a packed [batch*seq_len, 3840] QKV buffer into O [batch*seq_len, 1280].
 // chunk_len 0 = whole window; valid[b] = number of admitted key positions of window b.

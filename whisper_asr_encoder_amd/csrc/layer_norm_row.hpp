@@ -1,0 +1,79 @@
+// LayerNorm of one row by one wave, shared by the LayerNorm kernel and the block-row GEMM
+// that normalises its own operand rows: y = (x - mean) / sqrt(var + 1e-5) * gamma + beta,
+// var the biased variance, statistics in fp32 over values held in registers (two passes over
+// the registers, one read of the row), one rounding to fp16.  Each lane holds kGroups groups
+// of 4 consecutive features (feature 4 (c * 64 + lane) + j), so a wave reads 512 contiguous
+// bytes per group; both callers get bit-identical rows.
+#pragma once
+
+#include <math.h>
+
+#include "device.hpp"
+
+namespace edda {
+
+constexpr float kLnEps = 1e-5f;
+
+__device__ __forceinline__ float ln_wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// The row's values and its gamma / beta slices in registers (loaded together, so one memory
+// round trip precedes the arithmetic).
+template <int kGroups>
+struct LnRow {
+  f16x4 v[kGroups], g[kGroups], b[kGroups];
+};
+
+template <int kGroups>
+__device__ __forceinline__ LnRow<kGroups> layer_norm_load(const f16* __restrict__ xr, const f16* __restrict__ gamma,
+                                                          const f16* __restrict__ beta, int lane) {
+  LnRow<kGroups> r;
+#pragma unroll
+  for (int c = 0; c < kGroups; ++c) {
+    const int f = 4 * (c * kWave + lane);
+    r.v[c] = *reinterpret_cast<const f16x4*>(xr + f);
+    r.g[c] = *reinterpret_cast<const f16x4*>(gamma + f);
+    r.b[c] = *reinterpret_cast<const f16x4*>(beta + f);
+  }
+  return r;
+}
+
+// store(f, value) receives the normalised fp16 values of features f .. f + 3.
+template <int kGroups, typename Store>
+__device__ __forceinline__ void layer_norm_finish(const LnRow<kGroups>& r, int lane, Store store) {
+  constexpr int kFeatures = 256 * kGroups;
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kGroups; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += (float)r.v[c][j];
+  const float mean = ln_wave_sum(s) * (1.0f / kFeatures);
+  float q = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kGroups; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float d = (float)r.v[c][j] - mean;
+      q += d * d;
+    }
+  const float rstd = 1.0f / sqrtf(ln_wave_sum(q) * (1.0f / kFeatures) + kLnEps);
+#pragma unroll
+  for (int c = 0; c < kGroups; ++c) {
+    float o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = ((float)r.v[c][j] - mean) * rstd * (float)r.g[c][j] + (float)r.b[c][j];
+    const f16x2 lo = pack_rne(o[0], o[1]), hi = pack_rne(o[2], o[3]);
+    store(4 * (c * kWave + lane), (f16x4){lo[0], lo[1], hi[0], hi[1]});
+  }
+}
+
+template <int kGroups, typename Store>
+__device__ __forceinline__ void layer_norm_row(const f16* __restrict__ xr, const f16* __restrict__ gamma,
+                                               const f16* __restrict__ beta, int lane, Store store) {
+  layer_norm_finish<kGroups>(layer_norm_load<kGroups>(xr, gamma, beta, lane), lane, store);
+}
+
+}  // namespace edda

@@ -1,10 +1,7 @@
 // Kernels 4 and 5: LayerNorm and the column gather of the convolutional stem.
 //
-// LayerNorm: y = (x - mean) / sqrt(var + 1e-5) * gamma + beta per row, var the biased
-// variance, statistics in fp32 over values held in registers (two passes over the
-// registers, one read of the row).  One wave per row, each lane holding features / 256
-// groups of 4 consecutive features (8-byte loads; a wave reads 512 contiguous bytes per
-// step), 4 rows per workgroup.  HBM-bound: 2 bytes read and 2 written per element.
+// LayerNorm: one wave per row (the row arithmetic is layer_norm_row), 4 rows per
+// workgroup.  HBM-bound: 2 bytes read and 2 written per element.
 //
 // Column gather (im2col) of a kernel-3, padding-1 convolution with stride s: output row
 // t of window b holds, for tap = 0, 1, 2, the C input channels of frame s*t + tap - 1
@@ -16,18 +13,12 @@
 
 #include "device.hpp"
 #include "kernels.hpp"
+#include "layer_norm_row.hpp"
 
 namespace edda {
 namespace {
 
-constexpr float kLnEps = 1e-5f;
 constexpr int kLnRowsPerBlock = 4;
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
 
 template <int kGroups>  // 4-feature groups per lane: features = 256 * kGroups
 __global__ __launch_bounds__(kLnRowsPerBlock * kWave) void layer_norm_kernel(
@@ -37,37 +28,9 @@ __global__ __launch_bounds__(kLnRowsPerBlock * kWave) void layer_norm_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int row = blockIdx.x * kLnRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const f16* xr = x + (size_t)row * kFeatures;
-  f16x4 v[kGroups];
-#pragma unroll
-  for (int c = 0; c < kGroups; ++c) v[c] = *reinterpret_cast<const f16x4*>(xr + 4 * (c * kWave + lane));
-  float s = 0.0f;
-#pragma unroll
-  for (int c = 0; c < kGroups; ++c)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s += (float)v[c][j];
-  const float mean = wave_sum(s) * (1.0f / kFeatures);
-  float q = 0.0f;
-#pragma unroll
-  for (int c = 0; c < kGroups; ++c)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float d = (float)v[c][j] - mean;
-      q += d * d;
-    }
-  const float rstd = 1.0f / sqrtf(wave_sum(q) * (1.0f / kFeatures) + kLnEps);
   f16* yr = y + (size_t)row * kFeatures;
-#pragma unroll
-  for (int c = 0; c < kGroups; ++c) {
-    const int f = 4 * (c * kWave + lane);
-    const f16x4 g = *reinterpret_cast<const f16x4*>(gamma + f);
-    const f16x4 b = *reinterpret_cast<const f16x4*>(beta + f);
-    float o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = ((float)v[c][j] - mean) * rstd * (float)g[j] + (float)b[j];
-    const f16x2 lo = pack_rne(o[0], o[1]), hi = pack_rne(o[2], o[3]);
-    *reinterpret_cast<f16x4*>(yr + f) = (f16x4){lo[0], lo[1], hi[0], hi[1]};
-  }
+  layer_norm_row<kGroups>(x + (size_t)row * kFeatures, gamma, beta, lane,
+                          [&](int f, f16x4 v) { *reinterpret_cast<f16x4*>(yr + f) = v; });
 }
 
 template <int kGroups>

@@ -1,4 +1,4 @@
-// Kernels 6 and 7: the decoder's block-sized GEMMs and the KV-cache append.
+// Kernel 6: the decoder's block-sized GEMMs (with the KV-cache append in a fused variant).
 //
 // Skinny GEMM (M <= 16 rows, the verification block): C[M, N] = act(A B^T + bias) +
 // residual, as kernel 1, for the projections of the anchor plus drafted tokens.  The work is
@@ -11,12 +11,14 @@
 // tiles are summed in LDS; the epilogue adds the bias, applies the activation, adds the
 // residual, rounds once to fp16, and each thread stores one element of a 16-column run.
 //
-// KV append: the block's K and V rows (columns 1280..2559 and 2560..3839 of its packed QKV
-// rows) are copied into cache slots given per token, 16-byte chunks per thread.
+// Fused variants for the decoder layer: the operand rows normalised by LayerNorm inside the
+// kernel (no separate LayerNorm launch), and the KV-cache append done by the QKV epilogue.
+
 #include <math.h>
 
 #include "device.hpp"
 #include "kernels.hpp"
+#include "layer_norm_row.hpp"
 
 namespace edda {
 namespace {
@@ -25,76 +27,161 @@ constexpr int kSkWaves = 8;
 constexpr int kSkThreads = kSkWaves * kWave;
 constexpr int kSkCols = 16;
 constexpr int kSkUnroll = 4;
+constexpr int kLnGroups = kDModel / 256;  // rows normalised in the kernel have 1280 features
+constexpr int kALd = kDModel + 8;         // LDS row stride (halves): 16 rows hit 16 bank groups
 
 __device__ __forceinline__ float gelu_exact_sk(float v) {
   return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
 }
 
-template <int ACT, bool RES>
+// LN: A's rows are LayerNorm inputs (K = 1280): every workgroup normalises the block rows
+// into LDS (layer_norm_row, so the rows equal the LayerNorm kernel's bit for bit) while
+// its first weight loads are in flight, and reads its operand rows from there.
+// APPEND: C is a packed QKV block; its K and V columns are also stored into the caches'
+// rows slots[m] (the KV-cache append, done by the epilogue).
+struct SkinnyLn {
+  const f16* gamma;
+  const f16* beta;
+};
+struct SkinnyAppend {
+  f16* k_cache;
+  f16* v_cache;
+  Slots slots;
+};
+// Split K (gridDim.y > 1): workgroup (j, sp) covers steps [sp * per, (sp + 1) * per) of
+// column block j and stores its fp32 partial tile (agent-scope atomic stores, coherent across
+// the XCDs' L2 caches without cache-wide operations); the last of the block's workgroups to
+// count itself in on counters[j * kSplitCounterStride] sums the partials in split order (so the
+// result does not depend on arrival order), applies the epilogue, and resets the counter.
+struct SkinnySplit {
+  uint32_t* counters;
+  float* part;
+};
+constexpr int kSplitCounterStride = 16;  // uint32 words: one counter per 64 bytes
+
+__device__ __forceinline__ void store_coherent_f32(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent_f32(const float* p) {
+  return __builtin_bit_cast(float, __hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)),
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+template <int ACT, bool RES, bool LN, bool APPEND, bool SPLIT>
 __global__ __launch_bounds__(kSkThreads) void skinny_gemm_kernel(const f16* __restrict__ A,
                                                                  const f16* __restrict__ Bt,
                                                                  const f16* __restrict__ bias,
                                                                  const f16* residual, int res_period, f16* C,
-                                                                 int M, int N, int K) {
+                                                                 int M, int N, int K, SkinnyLn ln,
+                                                                 SkinnyAppend ap, SkinnySplit sk) {
+  __shared__ int last_arrival;
   __shared__ float red[kSkWaves][kSkCols][kSkCols + 1];
+  __shared__ __attribute__((aligned(16))) f16 a_lds[LN ? 16 * kALd : 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * kSkCols;
-  const int steps = K / 32;
+  const int per = K / 32 / gridDim.y;  // steps of this workgroup's K range
+  const int steps = (int)(blockIdx.y + 1) * per;
   const f16* wrow = Bt + (size_t)(n0 + r16) * K + 8 * g;
-  const f16* xrow = A + (size_t)min(r16, M - 1) * K + 8 * g;
+  const int arow = min(r16, M - 1);
+  const f16* xrow = A + (size_t)arow * K + 8 * g;
+  auto xload = [&](int st) -> f16x8 {
+    if constexpr (LN) return *reinterpret_cast<const f16x8*>(&a_lds[arow * kALd + 32 * st + 8 * g]);
+    else return load16(xrow + 32 * st);
+  };
   f32x4 acc = {};
-  int s = wave;
-  // Groups of kSkUnroll steps: all loads of a group are issued before its MFMAs.
+  int s = (int)blockIdx.y * per + wave;
+  // Groups of kSkUnroll steps: all loads of a group are issued before its MFMAs.  The first
+  // group's weights are requested before anything else.
+  const bool group0 = s + (kSkUnroll - 1) * kSkWaves < steps;
+  f16x8 wf[kSkUnroll], xf[kSkUnroll];
+  if (group0) {
+#pragma unroll
+    for (int u = 0; u < kSkUnroll; ++u) wf[u] = load16(wrow + 32 * (s + u * kSkWaves));
+  }
+  if constexpr (LN) {
+    // Rows wave and wave + 8 (M <= 16): both rows' loads are issued before either is used.
+    const int r0 = wave, r1 = wave + kSkWaves;
+    const LnRow<kLnGroups> row0 = layer_norm_load<kLnGroups>(A + (size_t)min(r0, M - 1) * kDModel, ln.gamma,
+                                                             ln.beta, lane);
+    const LnRow<kLnGroups> row1 = layer_norm_load<kLnGroups>(A + (size_t)min(r1, M - 1) * kDModel, ln.gamma,
+                                                             ln.beta, lane);
+    if (r0 < M)
+      layer_norm_finish<kLnGroups>(row0, lane, [&](int f, f16x4 v) { *reinterpret_cast<f16x4*>(&a_lds[r0 * kALd + f]) = v; });
+    if (r1 < M)
+      layer_norm_finish<kLnGroups>(row1, lane, [&](int f, f16x4 v) { *reinterpret_cast<f16x4*>(&a_lds[r1 * kALd + f]) = v; });
+    __syncthreads();
+  }
+  if (group0) {
+#pragma unroll
+    for (int u = 0; u < kSkUnroll; ++u) xf[u] = xload(s + u * kSkWaves);
+#pragma unroll
+    for (int u = 0; u < kSkUnroll; ++u) acc = mfma_16x16x32(wf[u], xf[u], acc);
+    s += kSkUnroll * kSkWaves;
+  }
   for (; s + (kSkUnroll - 1) * kSkWaves < steps; s += kSkUnroll * kSkWaves) {
-    f16x8 wf[kSkUnroll], xf[kSkUnroll];
 #pragma unroll
     for (int u = 0; u < kSkUnroll; ++u) {
       wf[u] = load16(wrow + 32 * (s + u * kSkWaves));
-      xf[u] = load16(xrow + 32 * (s + u * kSkWaves));
+      xf[u] = xload(s + u * kSkWaves);
     }
 #pragma unroll
     for (int u = 0; u < kSkUnroll; ++u) acc = mfma_16x16x32(wf[u], xf[u], acc);
   }
-  for (; s < steps; s += kSkWaves) acc = mfma_16x16x32(load16(wrow + 32 * s), load16(xrow + 32 * s), acc);
+  for (; s < steps; s += kSkWaves) acc = mfma_16x16x32(load16(wrow + 32 * s), xload(s), acc);
   // acc[r] = C^T[n = 4 g + r][m = r16] partial over this wave's steps.
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][4 * g + r][r16] = acc[r];
   __syncthreads();
-  if (tid >= kSkCols * kSkCols) return;
   const int m = tid / kSkCols, n = tid % kSkCols;
-  if (m >= M) return;
   float v = 0.0f;
+  if (tid < kSkCols * kSkCols) {
 #pragma unroll
-  for (int w = 0; w < kSkWaves; ++w) v += red[w][n][m];
+    for (int w = 0; w < kSkWaves; ++w) v += red[w][n][m];
+  }
+  if constexpr (SPLIT) {
+    const int nsplit = gridDim.y;
+    float* const part = sk.part + (size_t)blockIdx.x * nsplit * (kSkCols * kSkCols);
+    if (tid < kSkCols * kSkCols) store_coherent_f32(part + blockIdx.y * (kSkCols * kSkCols) + tid, v);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial is acknowledged before the count
+    __syncthreads();
+    uint32_t* const counter = sk.counters + blockIdx.x * kSplitCounterStride;
+    if (tid == 0)
+      last_arrival = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     (uint32_t)(nsplit - 1);
+    __syncthreads();
+    if (!last_arrival) return;
+    if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid >= kSkCols * kSkCols || m >= M) return;
+    v = 0.0f;
+    for (int q = 0; q < nsplit; ++q) v += load_coherent_f32(part + q * (kSkCols * kSkCols) + tid);
+  } else {
+    if (tid >= kSkCols * kSkCols || m >= M) return;
+  }
   if (bias) v += (float)bias[n0 + n];
   if constexpr (ACT == 1) v = gelu_exact_sk(v);
   if constexpr (RES) v += (float)residual[(size_t)(m % res_period) * N + n0 + n];
-  C[(size_t)m * N + n0 + n] = (f16)v;
-}
-
-template <int ACT, bool RES>
-hipError_t launch_sk(const void* A, const void* Bt, const void* bias, const void* residual, int res_period, void* C,
-                     int M, int N, int K, hipStream_t stream) {
-  hipLaunchKernelGGL((skinny_gemm_kernel<ACT, RES>), dim3(N / kSkCols), dim3(kSkThreads), 0, stream,
-                     static_cast<const f16*>(A), static_cast<const f16*>(Bt), static_cast<const f16*>(bias),
-                     static_cast<const f16*>(residual), res_period, static_cast<f16*>(C), M, N, K);
-  return hipGetLastError();
-}
-
-// One workgroup per block token: 2 x 160 chunks of 16 bytes (K row, V row).
-__global__ __launch_bounds__(256) void append_kv_kernel(const f16* __restrict__ qkv, Slots slots,
-                                                        f16* __restrict__ k_cache, f16* __restrict__ v_cache) {
-  const int t = blockIdx.x;
-  const size_t dst = (size_t)slots.s[t] * kHeads * kHeadDim;
-  const f16* src = qkv + (size_t)t * 3 * kHeads * kHeadDim;
-  constexpr int kChunks = kHeads * kHeadDim / 8;  // 160 per row
-  for (int c = threadIdx.x; c < 2 * kChunks; c += 256) {
-    const bool is_v = c >= kChunks;
-    const int cc = is_v ? c - kChunks : c;
-    const f16x8 val = load16(src + (is_v ? 2 : 1) * kHeads * kHeadDim + 8 * cc);
-    store16((is_v ? v_cache : k_cache) + dst + 8 * cc, val);
+  const f16 out = (f16)v;
+  C[(size_t)m * N + n0 + n] = out;
+  if constexpr (APPEND) {
+    const int col = n0 + n - kDModel;  // 0 .. 1279: K, 1280 .. 2559: V
+    if (col >= 0) {
+      const size_t row = (size_t)ap.slots.s[m] * kDModel;
+      if (col < kDModel) ap.k_cache[row + col] = out;
+      else ap.v_cache[row + col - kDModel] = out;
+    }
   }
+}
+
+template <int ACT, bool RES, bool LN, bool APPEND, bool SPLIT = false>
+hipError_t launch_sk(const void* A, const void* Bt, const void* bias, const void* residual, int res_period, void* C,
+                     int M, int N, int K, SkinnyLn ln, const SkinnyAppend& ap, hipStream_t stream,
+                     int nsplit = 1, SkinnySplit sk = {}) {
+  hipLaunchKernelGGL((skinny_gemm_kernel<ACT, RES, LN, APPEND, SPLIT>), dim3(N / kSkCols, nsplit), dim3(kSkThreads),
+                     0, stream, static_cast<const f16*>(A), static_cast<const f16*>(Bt), static_cast<const f16*>(bias),
+                     static_cast<const f16*>(residual), res_period, static_cast<f16*>(C), M, N, K, ln, ap, sk);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -102,18 +189,57 @@ __global__ __launch_bounds__(256) void append_kv_kernel(const f16* __restrict__ 
 hipError_t launch_skinny_gemm(const void* A, const void* Bt, const void* bias, const void* residual, int res_period,
                               int act, void* C, int M, int N, int K, hipStream_t stream) {
   if (M < 1 || M > 16 || N % kSkCols || K % 32) return hipErrorInvalidValue;
+  const SkinnyLn ln{};
+  const SkinnyAppend ap{};
   if (act == 1)
-    return residual ? launch_sk<1, true>(A, Bt, bias, residual, res_period, C, M, N, K, stream)
-                    : launch_sk<1, false>(A, Bt, bias, residual, res_period, C, M, N, K, stream);
-  return residual ? launch_sk<0, true>(A, Bt, bias, residual, res_period, C, M, N, K, stream)
-                  : launch_sk<0, false>(A, Bt, bias, residual, res_period, C, M, N, K, stream);
+    return residual ? launch_sk<1, true, false, false>(A, Bt, bias, residual, res_period, C, M, N, K, ln, ap, stream)
+                    : launch_sk<1, false, false, false>(A, Bt, bias, residual, res_period, C, M, N, K, ln, ap, stream);
+  return residual ? launch_sk<0, true, false, false>(A, Bt, bias, residual, res_period, C, M, N, K, ln, ap, stream)
+                  : launch_sk<0, false, false, false>(A, Bt, bias, residual, res_period, C, M, N, K, ln, ap, stream);
 }
 
-hipError_t launch_append_kv(const void* qkv, int n_q, const Slots& slots, void* k_cache, void* v_cache,
-                            hipStream_t stream) {
-  hipLaunchKernelGGL(append_kv_kernel, dim3(n_q), dim3(256), 0, stream, static_cast<const f16*>(qkv), slots,
-                     static_cast<f16*>(k_cache), static_cast<f16*>(v_cache));
-  return hipGetLastError();
+int skinny_splits(int N, int K) {
+  const int blocks = N / kSkCols, steps = K / 32;
+  int s = 1;
+  while (blocks * s * 2 <= 320 && steps % (2 * s) == 0 && steps / (2 * s) >= kSkWaves) s *= 2;
+  return s;
+}
+
+size_t skinny_split_part_bytes(int N, int K) {
+  const int s = skinny_splits(N, K);
+  return s > 1 ? (size_t)(N / kSkCols) * s * kSkCols * kSkCols * sizeof(float) : 0;
+}
+
+hipError_t launch_skinny_gemm_split(const void* A, const void* Bt, const void* bias, const void* residual,
+                                    int res_period, int act, void* C, int M, int N, int K, void* counters,
+                                    void* part, hipStream_t stream) {
+  if (M < 1 || M > 16 || N % kSkCols || K % 32 || act != 0) return hipErrorInvalidValue;
+  const int ns = skinny_splits(N, K);
+  if (ns == 1) return launch_skinny_gemm(A, Bt, bias, residual, res_period, act, C, M, N, K, stream);
+  if (!counters || !part) return hipErrorInvalidValue;
+  const SkinnySplit sk{static_cast<uint32_t*>(counters), static_cast<float*>(part)};
+  const SkinnyLn ln{};
+  const SkinnyAppend ap{};
+  return residual ? launch_sk<0, true, false, false, true>(A, Bt, bias, residual, res_period, C, M, N, K, ln, ap,
+                                                           stream, ns, sk)
+                  : launch_sk<0, false, false, false, true>(A, Bt, bias, residual, res_period, C, M, N, K, ln, ap,
+                                                            stream, ns, sk);
+}
+
+hipError_t launch_skinny_ln_gemm(const void* A, const void* gamma, const void* beta, const void* Bt, const void* bias,
+                                 int act, void* C, int M, int N, void* k_cache, void* v_cache, const Slots* slots,
+                                 hipStream_t stream) {
+  const int K = kDModel;
+  if (M < 1 || M > 16 || N % kSkCols || !gamma || !beta) return hipErrorInvalidValue;
+  const SkinnyLn ln{static_cast<const f16*>(gamma), static_cast<const f16*>(beta)};
+  if (k_cache) {
+    if (act != 0 || N != kQkvCols || !v_cache || !slots) return hipErrorInvalidValue;
+    const SkinnyAppend ap{static_cast<f16*>(k_cache), static_cast<f16*>(v_cache), *slots};
+    return launch_sk<0, false, true, true>(A, Bt, bias, nullptr, 1, C, M, N, K, ln, ap, stream);
+  }
+  const SkinnyAppend ap{};
+  if (act == 1) return launch_sk<1, false, true, false>(A, Bt, bias, nullptr, 1, C, M, N, K, ln, ap, stream);
+  return launch_sk<0, false, true, false>(A, Bt, bias, nullptr, 1, C, M, N, K, ln, ap, stream);
 }
 
 }  // namespace edda

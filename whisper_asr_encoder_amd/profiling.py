@@ -46,19 +46,20 @@ WORKLOADS = {
         "verify_kernelILi1E": ("verify_cross", ["verify_attn.hip"]),
     }),
     # The whole encoder: fc1 is the only 128x256-tile GEMM (N = 5120, GELU, no residual).
-    # The decoder verification pass: block-sized GEMMs by (activation, residual) variant.
+    # The decoder verification pass: block-sized GEMMs by fused variant (LayerNorm inside the
+    # GEMM, cache append in the QKV epilogue, split K for the 1280-wide residual outputs).
     "decoder": ("decoder verification pass, 32 layers, 16-token block, 360-slot cache, 1500 frames", {
-        "skinny_gemm_kernelILi0ELb0E": ("skinny_gemm_plain", ["skinny.hip"]),
-        "skinny_gemm_kernelILi1ELb0E": ("skinny_gemm_gelu", ["skinny.hip"]),
-        "skinny_gemm_kernelILi0ELb1E": ("skinny_gemm_residual", ["skinny.hip"]),
-        "append_kv_kernel": ("append_kv", ["skinny.hip"]),
-        "layer_norm_kernelILi5E": ("layer_norm_block", ["norm_im2col.hip"]),
+        # skinny_gemm_kernel<act, residual, LayerNorm, append, split K>
+        "skinny_gemm_kernelILi0ELb0ELb1ELb1ELb0E": ("ln_qkv_append", ["skinny.hip", "layer_norm_row.hpp"]),
+        "skinny_gemm_kernelILi0ELb0ELb1ELb0ELb0E": ("ln_cross_query", ["skinny.hip", "layer_norm_row.hpp"]),
+        "skinny_gemm_kernelILi1ELb0ELb1ELb0ELb0E": ("ln_fc1_gelu", ["skinny.hip", "layer_norm_row.hpp"]),
+        "skinny_gemm_kernelILi0ELb1ELb0ELb0ELb1E": ("split_k_residual", ["skinny.hip"]),
         "verify_kernelILi0E": ("verify_self", ["verify_attn.hip"]),
         "verify_kernelILi1E": ("verify_cross", ["verify_attn.hip"]),
     }),
     "encoder": ("whole encoder of one 30 s window (stem, 32 pre-norm layers, final LayerNorm)", {
         "gemm_bias_kernelILi128ELi256E": ("fc1_gemm", ["gemm.hip"]),
-        "layer_norm_kernelILi5E": ("layer_norm", ["norm_im2col.hip"]),
+        "layer_norm_kernelILi5E": ("layer_norm", ["norm_im2col.hip", "layer_norm_row.hpp"]),
         "im2col3_kernel": ("im2col3", ["norm_im2col.hip"]),
     }),
 }
