@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the Whisper-large-v3 encoder attention path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload window|chunked|batched|small|verify]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload window|chunked|batched|small|verify|encoder|decoder|decoder_q8]
 
 A step is one pass of the hot path over one batch of synthetic input. The
 default workload is one 30 s window (1500 frames x 1280, 20 heads of 64) through
@@ -369,7 +369,8 @@ def decoder_bench(args, torch):
     layers, n_q, trial = I.ENCODER_LAYERS, I.VERIFY_BLOCK, 0
     L = I.cache_length(trial)
     weights = [I.decoder_layer_weights(l) for l in range(layers)]
-    dv = DecoderVerifier(weights, max_kv=L)
+    q8 = args.workload == "decoder_q8"
+    dv = DecoderVerifier(weights, max_kv=L, q8=q8)
     enc = torch.from_numpy(I.encoder_workload(1, layers=1).x).cuda()
     dv.set_encoder_output(enc)
     caches = []
@@ -405,7 +406,9 @@ def decoder_bench(args, torch):
     # K/V rows written, activations and the mask (small).
     # Matrices: W_qkv (3 D^2), self output, cross query and output (3 D^2), fc1 and fc2;
     # biases: qkv, self output, cross query and output, fc1, fc2; three LayerNorms.
-    w_bytes = 2 * (6 * D * D + 2 * D * I.D_FF) + 2 * (3 * D + 3 * D + I.D_FF + D) + 2 * 6 * D
+    # Q8_0 matrices: one code byte per weight plus an fp16 scale per 32 (1.0625 bytes).
+    mat_bytes = (6 * D * D + 2 * D * I.D_FF) * (1.0625 if q8 else 2)
+    w_bytes = int(mat_bytes) + 2 * (3 * D + 3 * D + I.D_FF + D) + 2 * 6 * D
     kv_bytes = 2 * 2 * D * (L + I.FRAMES_PER_WINDOW) + 2 * 2 * D * n_q
     act_bytes = 2 * n_q * D * 4 + n_q * ((L + 31) // 32) * 4
     per_layer = w_bytes + kv_bytes + act_bytes
@@ -413,10 +416,12 @@ def decoder_bench(args, torch):
     flops = layers * (gemm_flops(n_q, QKV, D) + 2 * gemm_flops(n_q, D, D) + gemm_flops(n_q, D, D)
                       + 2 * gemm_flops(n_q, I.D_FF, D) + attn_flops(n_q * L) + attn_flops(n_q * I.FRAMES_PER_WINDOW))
     return {
-        "metric": "decoder verification pass (32 decoder layers, 16-token block) on 1 MI355X",
+        "metric": ("decoder verification pass (32 decoder layers, 16-token block"
+                   + (", Q8_0 projection weights" if q8 else "") + ") on 1 MI355X"),
         "value": round(ms * 1e3, 2), "unit": "us per pass", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp16", "data": "synthetic (seeded weights, caches and block rows)",
+        "vs_baseline": None, "dtype": "fp16 activations, q8_0 weights" if q8 else "fp16",
+        "data": "synthetic (seeded weights, caches and block rows)",
         "launch": "hip graph of the pass", "eager_ms_per_step": round(eager_ms, 4),
         "us_per_layer": round(ms * 1e3 / layers, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
         "config": {"workload": f"Whisper-large-v3 decoder verification layers: 16 block tokens, causal self-attention "
@@ -504,7 +509,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="window", choices=["small", "window", "chunked", "batched", "verify", "encoder", "decoder"])
+    ap.add_argument("--workload", default="window", choices=["small", "window", "chunked", "batched", "verify", "encoder", "decoder",
+                                                             "decoder_q8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -532,7 +538,7 @@ def main():
         res = verify_bench(args, torch)
     elif args.workload == "encoder":
         res = full_encoder_bench(args, torch)
-    elif args.workload == "decoder":
+    elif args.workload in ("decoder", "decoder_q8"):
         res = decoder_bench(args, torch)
     else:
         cfg = {"small": 0, "window": 1, "chunked": 2, "batched": 3}[args.workload]

@@ -337,6 +337,76 @@ edda_status edda_decoder_verify_layer(const void* x, int32_t n_q, const int32_t*
 /* Bytes of workspace edda_decoder_verify_layer needs (0 if the shape is invalid). */
 size_t edda_decoder_verify_workspace_bytes(int32_t n_q, int32_t n_kv, int32_t n_frames);
 
+/* ------------------------------------------------------------------------------------
+ * Q8_0 decoder weights ("audio.cpp PR #1223", PR description and results table: the decoder
+ * runs with Q8_0 weights beside an F16 encoder). The pages name the format only; it is read
+ * as GGML's Q8_0: each weight row (an output feature's inputs, in order) is cut into blocks
+ * of 32 values; a block stores d = max|x| / 127 (computed in fp32, stored as fp16) and 32
+ * int8 codes q = round(x / d) (x * (1/d) in fp32, rounded half away from zero); the weight
+ * is d * q. Codes are kept row-major like the fp16 weights; scales step-major:
+ * scales[k / 32][n] belongs to codes[n][k .. k+31].
+ * ------------------------------------------------------------------------------------ */
+
+/* One weight matrix in Q8_0 form: codes int8 [out, in], scales fp16 [in / 32, out]. */
+typedef struct {
+  const void* codes;
+  const void* scales;
+} edda_q8_matrix;
+
+/*
+ * Q8_0 codes and scales of fp16 weights w [rows, cols] (Linear layout, one row per output
+ * feature): codes int8 [rows, cols], scales fp16 [cols / 32, rows]. cols must be a
+ * multiple of 32. Device pointers; w and codes 16-byte aligned, scales 2-byte aligned.
+ * Errors: EDDA_ERR_INVALID_ARGUMENT, EDDA_ERR_UNSUPPORTED (cols), EDDA_ERR_MISALIGNED,
+ * EDDA_ERR_HIP.
+ */
+edda_status edda_quantize_q8_0(const void* w, int32_t rows, int32_t cols, void* codes, void* scales, void* stream);
+
+/*
+ * edda_linear with Q8_0 weights, for block-sized inputs: rows in [1, 16]; in_features a
+ * multiple of 32, out_features a multiple of 16; codes / scales as edda_quantize_q8_0
+ * writes them for the [out_features, in_features] weight. Each 32-deep block's dot product
+ * is taken on the codes and scaled in fp32, so the result is that of the dequantized
+ * weights up to fp32 summation order. Errors as edda_linear; EDDA_ERR_UNSUPPORTED for rows
+ * above 16 or the feature counts.
+ */
+edda_status edda_linear_q8(const void* x, int64_t rows, int32_t in_features, const void* codes, const void* scales,
+                           int32_t out_features, const void* bias, int32_t activation, const void* residual,
+                           int64_t residual_rows, void* y, void* stream);
+
+/* edda_decoder_layer_weights with every projection matrix in Q8_0 form. */
+typedef struct {
+  const void* ln1_gamma;
+  const void* ln1_beta;
+  edda_q8_matrix w_qkv;
+  const void* b_qkv;
+  edda_q8_matrix w_o;
+  const void* b_o;
+  const void* ln2_gamma;
+  const void* ln2_beta;
+  edda_q8_matrix w_q_cross;
+  const void* b_q_cross;
+  edda_q8_matrix w_o_cross;
+  const void* b_o_cross;
+  const void* ln3_gamma;
+  const void* ln3_beta;
+  edda_q8_matrix w_fc1;
+  const void* b_fc1;
+  edda_q8_matrix w_fc2;
+  const void* b_fc2;
+} edda_decoder_layer_weights_q8;
+
+/*
+ * edda_decoder_verify_layer with Q8_0 projection weights (LayerNorm parameters and biases
+ * fp16; codes and scales 16-byte aligned). Same arguments, workspace
+ * (edda_decoder_verify_workspace_bytes) and errors.
+ */
+edda_status edda_decoder_verify_layer_q8(const void* x, int32_t n_q, const int32_t* slots, void* k_cache,
+                                         void* v_cache, int32_t cache_slots, int32_t n_kv,
+                                         const uint32_t* mask_rows, const void* cross_k, const void* cross_v,
+                                         int32_t n_frames, const edda_decoder_layer_weights_q8* weights, void* y,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Cross-attention keys and values of the encoder output, once per utterance and layer:
  * cross_k = enc W_k (no bias), cross_v = enc W_v + b_v.

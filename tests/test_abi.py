@@ -292,3 +292,77 @@ def test_decoder_workspace_sizes(lib):
     assert n >= verify + 16 * (4 * 1280 + 3840 + 5120) * 2  # h, o, x1, x2, qkv, MLP hidden
     assert lib.edda_decoder_verify_workspace_bytes(17, 360, 1500) == 0
     assert lib.edda_decoder_verify_workspace_bytes(1, 0, 1500) == 0
+
+
+def q8(lib, w=A, rows=64, cols=128, codes=B, scales=B + 4096):
+    return lib.edda_quantize_q8_0(w, rows, cols, codes, scales, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), INVALID), (dict(codes=None), INVALID), (dict(scales=None), INVALID), (dict(rows=0), INVALID),
+    (dict(cols=16), INVALID), (dict(cols=48), UNSUPPORTED), (dict(rows=1 << 20, cols=4096), INVALID),
+    (dict(w=ODD), MISALIGNED), (dict(codes=B + 8), MISALIGNED), (dict(scales=B + 1), MISALIGNED),
+])
+def test_quantize_q8_0_rejects(lib, kw, status):
+    assert q8(lib, **kw) == status
+
+
+def lin_q8(lib, x=A, rows=16, k=1280, codes=B, scales=B + 65536, n=1280, bias=None, act=0, res=None, res_rows=0, y=A + 65536):
+    return lib.edda_linear_q8(x, rows, k, codes, scales, n, bias, act, res, res_rows, y, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(codes=None), INVALID), (dict(scales=None), INVALID), (dict(y=None), INVALID),
+    (dict(rows=0), INVALID), (dict(act=2), INVALID), (dict(res=A, res_rows=0), INVALID),
+    (dict(rows=17), UNSUPPORTED), (dict(k=48), UNSUPPORTED), (dict(n=24), UNSUPPORTED),
+    (dict(x=ODD), MISALIGNED), (dict(scales=B + 8), MISALIGNED), (dict(codes=B + 8), MISALIGNED),
+])
+def test_linear_q8_rejects(lib, kw, status):
+    assert lin_q8(lib, **kw) == status
+
+
+def test_decoder_layer_q8_rejects_missing_scales(lib):
+    w = _lib.DecoderLayerWeightsQ8()
+    for name, _ in w._fields_:
+        if name.startswith("w_"):
+            setattr(w, name, _lib.Q8Matrix(A, A + 4096))
+        elif not name.startswith("b_"):
+            setattr(w, name, A)
+    slots = (ctypes.c_int32 * 1)(0)
+    args = lambda: (A, 1, ctypes.cast(slots, ctypes.POINTER(ctypes.c_int32)), A, A, 64, 8, None, A, A, 1500,
+                    ctypes.byref(w), A, B, 1 << 30, None)
+    w.w_fc2 = _lib.Q8Matrix(A, None)
+    assert lib.edda_decoder_verify_layer_q8(*args()) == INVALID
+    w.w_fc2 = _lib.Q8Matrix(A, A + 8)
+    assert lib.edda_decoder_verify_layer_q8(*args()) == MISALIGNED
+    assert lib.edda_decoder_verify_layer_q8(A, 17, ctypes.cast(slots, ctypes.POINTER(ctypes.c_int32)), A, A, 64, 8,
+                                            None, A, A, 1500, ctypes.byref(w), A, B, 1 << 30, None) == INVALID
+
+
+def test_weight_structs_match_the_c_layout(tmp_path):
+    """sizeof / offsetof of the header's weight structs, compiled with the host C compiler,
+    equal the binding's ctypes layouts."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    structs = {"edda_decoder_layer_weights": _lib.DecoderLayerWeights,
+               "edda_decoder_layer_weights_q8": _lib.DecoderLayerWeightsQ8,
+               "edda_q8_matrix": _lib.Q8Matrix}
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "edda.h"', 'int main(void) {']
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for field, _ in py._fields_:
+            lines.append(f'  printf("{cname} {field} %zu\\n", offsetof({cname}, {field}));')
+    lines += ['  return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {(l.split()[0], l.split()[1]): int(l.split()[2]) for l in out if l}
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for field, _ in py._fields_:
+            assert got[(cname, field)] == getattr(py, field).offset, (cname, field)

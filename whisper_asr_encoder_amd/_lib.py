@@ -32,6 +32,7 @@ EXPORTS = ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_encode
            "edda_encoder_layer_workspace_bytes", "edda_encoder_stem", "edda_encoder_stem_workspace_bytes",
            "edda_decoder_verify_layer", "edda_decoder_verify_workspace_bytes", "edda_cross_kv",
            "edda_verify_attn_ex", "edda_verify_workspace_bytes_ex",
+           "edda_quantize_q8_0", "edda_linear_q8", "edda_decoder_verify_layer_q8",
            "edda_last_error", "edda_version")
 
 D_FF = 5120
@@ -48,6 +49,18 @@ class LayerWeights(ctypes.Structure):
 class DecoderLayerWeights(ctypes.Structure):
     """edda_decoder_layer_weights: device pointers (Linear layout)."""
     _fields_ = [(name, ctypes.c_void_p) for name in (
+        "ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_gamma", "ln2_beta", "w_q_cross",
+        "b_q_cross", "w_o_cross", "b_o_cross", "ln3_gamma", "ln3_beta", "w_fc1", "b_fc1", "w_fc2", "b_fc2")]
+
+
+class Q8Matrix(ctypes.Structure):
+    """edda_q8_matrix: Q8_0 codes int8 [out, in] and scales fp16 [in / 32, out] (device)."""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class DecoderLayerWeightsQ8(ctypes.Structure):
+    """edda_decoder_layer_weights_q8: projection matrices as Q8Matrix, the rest fp16 pointers."""
+    _fields_ = [(name, Q8Matrix if name.startswith("w_") else ctypes.c_void_p) for name in (
         "ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_gamma", "ln2_beta", "w_q_cross",
         "b_q_cross", "w_o_cross", "b_o_cross", "ln3_gamma", "ln3_beta", "w_fc1", "b_fc1", "w_fc2", "b_fc2")]
 
@@ -90,6 +103,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edda_encoder_stem_workspace_bytes.restype = sz
     lib.edda_decoder_verify_layer.argtypes = [vp, i32, ctypes.POINTER(i32), vp, vp, i32, i32, vp, vp, vp, i32,
                                               ctypes.POINTER(DecoderLayerWeights), vp, vp, sz, vp]
+    lib.edda_decoder_verify_layer_q8.argtypes = [vp, i32, ctypes.POINTER(i32), vp, vp, i32, i32, vp, vp, vp, i32,
+                                                 ctypes.POINTER(DecoderLayerWeightsQ8), vp, vp, sz, vp]
+    lib.edda_quantize_q8_0.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.edda_linear_q8.argtypes = [vp, ctypes.c_int64, i32, vp, vp, i32, vp, i32, vp, ctypes.c_int64, vp, vp]
     lib.edda_decoder_verify_workspace_bytes.argtypes = [i32, i32, i32]
     lib.edda_decoder_verify_workspace_bytes.restype = sz
     lib.edda_cross_kv.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
@@ -100,7 +117,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edda_version.restype = ctypes.c_char_p
     for name in ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_verify_attn", "edda_linear",
                  "edda_layer_norm", "edda_encoder_layer", "edda_encoder_stem", "edda_decoder_verify_layer",
-                 "edda_cross_kv", "edda_verify_attn_ex"):
+                 "edda_cross_kv", "edda_verify_attn_ex", "edda_quantize_q8_0", "edda_linear_q8",
+                 "edda_decoder_verify_layer_q8"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -328,9 +346,10 @@ def decoder_verify_workspace_bytes(n_q: int, n_kv: int, n_frames: int) -> int:
 
 
 def edda_decoder_verify_layer(x, slots, k_cache, v_cache, n_kv, mask_rows, cross_k, cross_v,
-                              weights: "DecoderLayerWeights", y, workspace, stream=None):
+                              weights, y, workspace, stream=None):
     """One decoder layer over the block rows x [n_q, 1280]; slots: host ints; caches
-    [cache_slots, 20, 64] updated in place; mask_rows as for edda_verify_attn (or None)."""
+    [cache_slots, 20, 64] updated in place; mask_rows as for edda_verify_attn (or None).
+    weights: DecoderLayerWeights (fp16) or DecoderLayerWeightsQ8 (Q8_0 projections)."""
     lib = load()
     torch = _require(x, "x")
     n_q = x.shape[0]
@@ -346,10 +365,10 @@ def edda_decoder_verify_layer(x, slots, k_cache, v_cache, n_kv, mask_rows, cross
         _require(mask_rows, "mask_rows", (n_q, (n_kv + 31) // 32))
     arr = (ctypes.c_int32 * n_q)(*[int(v) for v in slots])
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib.edda_decoder_verify_layer(_ptr(x), n_q, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)),
-                                         _ptr(k_cache), _ptr(v_cache), cache_slots, n_kv, _ptr(mask_rows),
-                                         _ptr(cross_k), _ptr(cross_v), n_frames, ctypes.byref(weights), _ptr(y),
-                                         _ptr(workspace), ws_bytes, _stream(stream)))
+    fn = lib.edda_decoder_verify_layer_q8 if isinstance(weights, DecoderLayerWeightsQ8) else lib.edda_decoder_verify_layer
+    _check(fn(_ptr(x), n_q, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), _ptr(k_cache), _ptr(v_cache),
+              cache_slots, n_kv, _ptr(mask_rows), _ptr(cross_k), _ptr(cross_v), n_frames, ctypes.byref(weights),
+              _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def edda_cross_kv(enc, w_k, w_v, b_v, cross_k, cross_v, stream=None):
@@ -390,3 +409,33 @@ def edda_verify_attn_ex(q, k, v, o, mask_mode=MASK_NONE, mask_rows=None, sinks=N
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.edda_verify_attn_ex(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, n_heads, mask_mode, _ptr(mask_rows),
                                    _ptr(sinks), _ptr(o), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def edda_quantize_q8_0(w, codes, scales, stream=None):
+    """Q8_0 codes int8 [rows, cols] and scales fp16 [cols / 32, rows] of fp16 w [rows, cols]."""
+    lib = load()
+    torch = _require(w, "w")
+    rows, cols = w.shape
+    _require(w, "w", (rows, cols), torch.float16)
+    _require(codes, "codes", (rows, cols), torch.int8)
+    _require(scales, "scales", (cols // 32, rows), torch.float16)
+    _check(lib.edda_quantize_q8_0(_ptr(w), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def edda_linear_q8(x, codes, scales, bias, y, activation=ACT_NONE, residual=None, residual_rows=None, stream=None):
+    """edda_linear with Q8_0 weights (codes [out, in], scales [in / 32, out]); rows <= 16."""
+    lib = load()
+    torch = _require(x, "x")
+    rows, k = x.shape
+    n = codes.shape[0]
+    _require(x, "x", (rows, k), torch.float16)
+    _require(codes, "codes", (n, k), torch.int8)
+    _require(scales, "scales", (k // 32, n), torch.float16)
+    if bias is not None:
+        _require(bias, "bias", (n,), torch.float16)
+    _require(y, "y", (rows, n), torch.float16)
+    if residual is not None:
+        residual_rows = residual.shape[0] if residual_rows is None else residual_rows
+        _require(residual, "residual", (residual.shape[0], n), torch.float16)
+    _check(lib.edda_linear_q8(_ptr(x), rows, k, _ptr(codes), _ptr(scales), n, _ptr(bias), activation,
+                              _ptr(residual), residual_rows or 0, _ptr(y), _stream(stream)))

@@ -352,18 +352,43 @@ size_t edda_decoder_verify_workspace_bytes(int32_t n_q, int32_t n_kv, int32_t n_
   return decoder_ws(n_q, n_kv, n_frames).total;
 }
 
-edda_status edda_decoder_verify_layer(const void* x, int32_t n_q, const int32_t* slots, void* k_cache,
-                                      void* v_cache, int32_t cache_slots, int32_t n_kv,
-                                      const uint32_t* mask_rows, const void* cross_k, const void* cross_v,
-                                      int32_t n_frames, const edda_decoder_layer_weights* wt, void* y,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "edda_decoder_verify_layer";
+namespace {
+// One projection matrix: fp16 [out, in] (scales null) or Q8_0 codes with their scales.
+struct Mat {
+  const void* w;
+  const void* scales;
+};
+struct DecoderMats {
+  const void *ln1_gamma, *ln1_beta;
+  Mat qkv;
+  const void* b_qkv;
+  Mat o;
+  const void* b_o;
+  const void *ln2_gamma, *ln2_beta;
+  Mat q_cross;
+  const void* b_q_cross;
+  Mat o_cross;
+  const void* b_o_cross;
+  const void *ln3_gamma, *ln3_beta;
+  Mat fc1;
+  const void* b_fc1;
+  Mat fc2;
+  const void* b_fc2;
+};
+
+edda_status decoder_layer(const char* fn, const void* x, int32_t n_q, const int32_t* slots, void* k_cache,
+                          void* v_cache, int32_t cache_slots, int32_t n_kv, const uint32_t* mask_rows,
+                          const void* cross_k, const void* cross_v, int32_t n_frames, const DecoderMats* wt, void* y,
+                          void* workspace, size_t workspace_bytes, void* stream, bool q8) {
   if (!x || !slots || !k_cache || !v_cache || !cross_k || !cross_v || !wt || !y)
     return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: x, slots, caches, cross K/V, weights and y must be non-null", fn);
-  const void* required[] = {wt->ln1_gamma, wt->ln1_beta, wt->w_qkv, wt->w_o, wt->ln2_gamma, wt->ln2_beta,
-                            wt->w_q_cross, wt->w_o_cross, wt->ln3_gamma, wt->ln3_beta, wt->w_fc1, wt->w_fc2};
+  const Mat mats[] = {wt->qkv, wt->o, wt->q_cross, wt->o_cross, wt->fc1, wt->fc2};
+  const void* required[] = {wt->ln1_gamma, wt->ln1_beta, wt->ln2_gamma, wt->ln2_beta, wt->ln3_gamma, wt->ln3_beta};
   for (const void* p : required)
     if (!p) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: every LayerNorm and weight-matrix pointer is required", fn);
+  for (const Mat& m : mats)
+    if (!m.w || (q8 && !m.scales))
+      return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: every LayerNorm and weight-matrix pointer is required", fn);
   if (n_q < 1 || n_q > EDDA_MAX_VERIFY_QUERIES)
     return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_q = %d outside [1, %d]", fn, n_q, EDDA_MAX_VERIFY_QUERIES);
   if (cache_slots < 1 || n_kv < 1 || n_kv > cache_slots || (int64_t)cache_slots * EDDA_D_MODEL >= kMaxRows)
@@ -378,12 +403,14 @@ edda_status edda_decoder_verify_layer(const void* x, int32_t n_q, const int32_t*
       if (slots[u] == slots[t]) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: slot %d repeated", fn, slots[t]);
     sl.s[t] = slots[t];
   }
-  const void* all[] = {x, y, k_cache, v_cache, cross_k, cross_v, workspace, wt->ln1_gamma, wt->ln1_beta, wt->w_qkv,
-                       wt->b_qkv, wt->w_o, wt->b_o, wt->ln2_gamma, wt->ln2_beta, wt->w_q_cross, wt->b_q_cross,
-                       wt->w_o_cross, wt->b_o_cross, wt->ln3_gamma, wt->ln3_beta, wt->w_fc1, wt->b_fc1, wt->w_fc2,
-                       wt->b_fc2};
+  const void* all[] = {x, y, k_cache, v_cache, cross_k, cross_v, workspace, wt->ln1_gamma, wt->ln1_beta, wt->b_qkv,
+                       wt->b_o, wt->ln2_gamma, wt->ln2_beta, wt->b_q_cross, wt->b_o_cross, wt->ln3_gamma,
+                       wt->ln3_beta, wt->b_fc1, wt->b_fc2};
   for (const void* p : all)
     if (p && !aligned(p, 16)) return fail(EDDA_ERR_MISALIGNED, "%s: pointers must be 16-byte aligned", fn);
+  for (const Mat& m : mats)
+    if (!aligned(m.w, 16) || (m.scales && !aligned(m.scales, 16)))
+      return fail(EDDA_ERR_MISALIGNED, "%s: pointers must be 16-byte aligned", fn);
   if (mask_rows && !aligned(mask_rows, 4)) return fail(EDDA_ERR_MISALIGNED, "%s: mask_rows must be 4-byte aligned", fn);
   const DecoderWs L = decoder_ws(n_q, n_kv, n_frames);
   if (!workspace || workspace_bytes < L.total)
@@ -396,36 +423,108 @@ edda_status edda_decoder_verify_layer(const void* x, int32_t n_q, const int32_t*
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int D = EDDA_D_MODEL;
   hipError_t e;
-#define EDDA_STEP(call, what) \
-  if ((e = (call)) != hipSuccess) return from_hip(e, "edda_decoder_verify_layer " what " launch")
+#define EDDA_STEP(call, what)             \
+  if ((e = (call)) != hipSuccess) {       \
+    char msg[96];                         \
+    snprintf(msg, sizeof msg, "%s " what " launch", fn); \
+    return from_hip(e, msg);              \
+  }
   // Eight launches: LayerNorms run inside the block GEMMs that consume them, and the QKV
   // epilogue writes the block's K and V rows into their cache slots.
-  EDDA_STEP(edda::launch_skinny_ln_gemm(x, wt->ln1_gamma, wt->ln1_beta, wt->w_qkv, wt->b_qkv, EDDA_ACT_NONE, qkv, n_q,
-                                        EDDA_QKV_COLS, k_cache, v_cache, &sl, s),
+  EDDA_STEP(edda::launch_skinny_ln_gemm(x, wt->ln1_gamma, wt->ln1_beta, wt->qkv.w, wt->b_qkv, EDDA_ACT_NONE, qkv, n_q,
+                                        EDDA_QKV_COLS, k_cache, v_cache, &sl, s, wt->qkv.scales),
             "LN1 + QKV + cache append");
   EDDA_STEP(edda::launch_verify(qkv, EDDA_QKV_COLS, n_q, k_cache, v_cache, n_kv, EDDA_N_HEADS,
                                 mask_rows ? EDDA_MASK_ROWS : EDDA_MASK_NONE, mask_rows, nullptr, o, ws, s),
             "self-attention");
-  EDDA_STEP(edda::launch_skinny_gemm_split(o, wt->w_o, wt->b_o, x, n_q, EDDA_ACT_NONE, x1, n_q, D, D, sk_counters,
-                                           sk_part, s),
+  EDDA_STEP(edda::launch_skinny_gemm_split(o, wt->o.w, wt->b_o, x, n_q, EDDA_ACT_NONE, x1, n_q, D, D, sk_counters,
+                                           sk_part, s, wt->o.scales),
             "self output projection");
-  EDDA_STEP(edda::launch_skinny_ln_gemm(x1, wt->ln2_gamma, wt->ln2_beta, wt->w_q_cross, wt->b_q_cross, EDDA_ACT_NONE,
-                                        o, n_q, D, nullptr, nullptr, nullptr, s),
+  EDDA_STEP(edda::launch_skinny_ln_gemm(x1, wt->ln2_gamma, wt->ln2_beta, wt->q_cross.w, wt->b_q_cross, EDDA_ACT_NONE,
+                                        o, n_q, D, nullptr, nullptr, nullptr, s, wt->q_cross.scales),
             "LN2 + cross query");
   EDDA_STEP(edda::launch_verify(o, D, n_q, cross_k, cross_v, n_frames, EDDA_N_HEADS, EDDA_MASK_NONE, nullptr,
                                 nullptr, h, ws, s),
             "cross-attention");
-  EDDA_STEP(edda::launch_skinny_gemm_split(h, wt->w_o_cross, wt->b_o_cross, x1, n_q, EDDA_ACT_NONE, x2, n_q, D, D,
-                                           sk_counters, sk_part, s),
+  EDDA_STEP(edda::launch_skinny_gemm_split(h, wt->o_cross.w, wt->b_o_cross, x1, n_q, EDDA_ACT_NONE, x2, n_q, D, D,
+                                           sk_counters, sk_part, s, wt->o_cross.scales),
             "cross output projection");
-  EDDA_STEP(edda::launch_skinny_ln_gemm(x2, wt->ln3_gamma, wt->ln3_beta, wt->w_fc1, wt->b_fc1, EDDA_ACT_GELU, f, n_q,
-                                        EDDA_D_FF, nullptr, nullptr, nullptr, s),
+  EDDA_STEP(edda::launch_skinny_ln_gemm(x2, wt->ln3_gamma, wt->ln3_beta, wt->fc1.w, wt->b_fc1, EDDA_ACT_GELU, f, n_q,
+                                        EDDA_D_FF, nullptr, nullptr, nullptr, s, wt->fc1.scales),
             "LN3 + fc1");
-  EDDA_STEP(edda::launch_skinny_gemm_split(f, wt->w_fc2, wt->b_fc2, x2, n_q, EDDA_ACT_NONE, y, n_q, D, EDDA_D_FF,
-                                           sk_counters, sk_part, s),
+  EDDA_STEP(edda::launch_skinny_gemm_split(f, wt->fc2.w, wt->b_fc2, x2, n_q, EDDA_ACT_NONE, y, n_q, D, EDDA_D_FF,
+                                           sk_counters, sk_part, s, wt->fc2.scales),
             "fc2");
 #undef EDDA_STEP
   return ok();
+}
+}  // namespace
+
+edda_status edda_decoder_verify_layer(const void* x, int32_t n_q, const int32_t* slots, void* k_cache,
+                                      void* v_cache, int32_t cache_slots, int32_t n_kv,
+                                      const uint32_t* mask_rows, const void* cross_k, const void* cross_v,
+                                      int32_t n_frames, const edda_decoder_layer_weights* wt, void* y,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "edda_decoder_verify_layer";
+  if (!wt) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: x, slots, caches, cross K/V, weights and y must be non-null", fn);
+  const DecoderMats m{wt->ln1_gamma, wt->ln1_beta, {wt->w_qkv, nullptr}, wt->b_qkv, {wt->w_o, nullptr}, wt->b_o,
+                      wt->ln2_gamma, wt->ln2_beta, {wt->w_q_cross, nullptr}, wt->b_q_cross, {wt->w_o_cross, nullptr},
+                      wt->b_o_cross, wt->ln3_gamma, wt->ln3_beta, {wt->w_fc1, nullptr}, wt->b_fc1,
+                      {wt->w_fc2, nullptr}, wt->b_fc2};
+  return decoder_layer(fn, x, n_q, slots, k_cache, v_cache, cache_slots, n_kv, mask_rows, cross_k, cross_v, n_frames,
+                       &m, y, workspace, workspace_bytes, stream, false);
+}
+
+edda_status edda_decoder_verify_layer_q8(const void* x, int32_t n_q, const int32_t* slots, void* k_cache,
+                                         void* v_cache, int32_t cache_slots, int32_t n_kv,
+                                         const uint32_t* mask_rows, const void* cross_k, const void* cross_v,
+                                         int32_t n_frames, const edda_decoder_layer_weights_q8* wt, void* y,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "edda_decoder_verify_layer_q8";
+  if (!wt) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: x, slots, caches, cross K/V, weights and y must be non-null", fn);
+  auto M = [](const edda_q8_matrix& q) { return Mat{q.codes, q.scales}; };
+  const DecoderMats m{wt->ln1_gamma, wt->ln1_beta, M(wt->w_qkv), wt->b_qkv, M(wt->w_o), wt->b_o,
+                      wt->ln2_gamma, wt->ln2_beta, M(wt->w_q_cross), wt->b_q_cross, M(wt->w_o_cross),
+                      wt->b_o_cross, wt->ln3_gamma, wt->ln3_beta, M(wt->w_fc1), wt->b_fc1, M(wt->w_fc2), wt->b_fc2};
+  return decoder_layer(fn, x, n_q, slots, k_cache, v_cache, cache_slots, n_kv, mask_rows, cross_k, cross_v, n_frames,
+                       &m, y, workspace, workspace_bytes, stream, true);
+}
+
+edda_status edda_quantize_q8_0(const void* w, int32_t rows, int32_t cols, void* codes, void* scales, void* stream) {
+  const char* fn = "edda_quantize_q8_0";
+  if (!w || !codes || !scales) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: w, codes and scales must be non-null", fn);
+  if (rows < 1 || cols < 32 || (int64_t)rows * cols >= kMaxRows)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: rows = %d, cols = %d out of range", fn, rows, cols);
+  if (cols % 32) return fail(EDDA_ERR_UNSUPPORTED, "%s: cols = %d must be a multiple of 32", fn, cols);
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 2))
+    return fail(EDDA_ERR_MISALIGNED, "%s: w and codes must be 16-byte, scales 2-byte aligned", fn);
+  return from_hip(edda::launch_quantize_q8_0(w, rows, cols, codes, scales, static_cast<hipStream_t>(stream)),
+                  "edda_quantize_q8_0 launch");
+}
+
+edda_status edda_linear_q8(const void* x, int64_t rows, int32_t in_features, const void* codes, const void* scales,
+                           int32_t out_features, const void* bias, int32_t activation, const void* residual,
+                           int64_t residual_rows, void* y, void* stream) {
+  const char* fn = "edda_linear_q8";
+  if (!x || !codes || !scales || !y) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: x, codes, scales and y must be non-null", fn);
+  if (rows < 1 || in_features < 1 || out_features < 1)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: rows, in_features and out_features must be >= 1", fn);
+  if (activation != EDDA_ACT_NONE && activation != EDDA_ACT_GELU)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: unknown activation %d", fn, activation);
+  if (residual && residual_rows < 1)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: residual_rows = %lld must be >= 1", fn, (long long)residual_rows);
+  if ((int64_t)in_features * out_features >= kMaxRows)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: weight matrix too large", fn);
+  if (rows > EDDA_MAX_VERIFY_QUERIES || in_features % 32 || out_features % 16)
+    return fail(EDDA_ERR_UNSUPPORTED, "%s: rows = %lld (at most 16), in_features = %d (multiple of 32), "
+                "out_features = %d (multiple of 16)", fn, (long long)rows, in_features, out_features);
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 16) || !aligned(y, 16) || (bias && !aligned(bias, 16)) ||
+      (residual && !aligned(residual, 16)))
+    return fail(EDDA_ERR_MISALIGNED, "%s: pointers must be 16-byte aligned", fn);
+  return from_hip(edda::launch_skinny_gemm(x, codes, bias, residual, residual ? (int)residual_rows : 1, activation, y,
+                                           (int)rows, out_features, in_features, static_cast<hipStream_t>(stream),
+                                           scales),
+                  "edda_linear_q8 launch");
 }
 
 edda_status edda_cross_kv(const void* enc, int32_t n_frames, const void* w_k, const void* w_v, const void* b_v,

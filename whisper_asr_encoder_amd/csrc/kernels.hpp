@@ -30,8 +30,14 @@ hipError_t launch_im2col3(const void* x, int batch, long x_batch, int t_in, int 
 
 // C = act(A * Bt^T + bias) + residual for M <= 16 rows (N % 16 == 0, K % 32 == 0):
 // weights streamed straight into registers, 8-way K split inside a workgroup.
+// scales != null: Bt holds Q8_0 int8 codes [N][K] and scales fp16 [K / 32][N] (the weight
+// of (n, k) is scales[k / 32][n] * codes[n][k]); every skinny launcher takes them the same way.
 hipError_t launch_skinny_gemm(const void* A, const void* Bt, const void* bias, const void* residual, int res_period,
-                              int act, void* C, int M, int N, int K, hipStream_t stream);
+                              int act, void* C, int M, int N, int K, hipStream_t stream,
+                              const void* scales = nullptr);
+
+// Q8_0 codes [rows][cols] and scales [cols / 32][rows] of fp16 weights [rows][cols].
+hipError_t launch_quantize_q8_0(const void* w, int rows, int cols, void* codes, void* scales, hipStream_t stream);
 
 // Cache slots of the (at most 16) block tokens, passed by value.
 struct Slots {
@@ -44,7 +50,7 @@ struct Slots {
 // slots[m] ([slot][1280]).
 hipError_t launch_skinny_ln_gemm(const void* A, const void* gamma, const void* beta, const void* Bt, const void* bias,
                                  int act, void* C, int M, int N, void* k_cache, void* v_cache, const Slots* slots,
-                                 hipStream_t stream);
+                                 hipStream_t stream, const void* scales = nullptr);
 
 // Split-K form of launch_skinny_gemm (act 0) for narrow outputs: skinny_splits(N, K)
 // workgroups per 16-column block, each over a K range; the last to finish sums their fp32
@@ -55,7 +61,7 @@ int skinny_splits(int N, int K);
 size_t skinny_split_part_bytes(int N, int K);
 hipError_t launch_skinny_gemm_split(const void* A, const void* Bt, const void* bias, const void* residual,
                                     int res_period, int act, void* C, int M, int N, int K, void* counters,
-                                    void* part, hipStream_t stream);
+                                    void* part, hipStream_t stream, const void* scales = nullptr);
 
 // Flash attention over a packed [batch*seq_len, 3840] QKV buffer into O [batch*seq_len, 1280].
 // chunk_len 0 = whole window; valid[b] = number of admitted key positions of window b.

@@ -141,12 +141,17 @@ class DecoderVerifier:
     encoder output and a shared workspace (zero-filled once: its leading arrival counters
     must start at zero). Every step runs in libedda.so."""
 
-    def __init__(self, layer_weights, max_kv: int, n_frames: int = 1500, device="cuda"):
+    MATRICES = ("w_qkv", "w_o", "w_q_cross", "w_o_cross", "w_fc1", "w_fc2")
+
+    def __init__(self, layer_weights, max_kv: int, n_frames: int = 1500, device="cuda", q8: bool = False):
+        """q8: the six projection matrices of every layer are quantized to Q8_0 on the device
+        (edda_quantize_q8_0) and the layers run edda_decoder_verify_layer_q8."""
         import torch
         self.torch = torch
         self.device = device
+        self.q8 = bool(q8)
         self.n_frames = int(n_frames)
-        self._keep, self.structs = [], []
+        self._keep, self.structs, self.codes = [], [], []
         for w in layer_weights:
             t = dict(ln1_gamma=self._dev(w.ln1_g), ln1_beta=self._dev(w.ln1_b),
                      w_qkv=self._dev(_lib.linear_layout(w.w_qkv)), b_qkv=self._dev(w.b_qkv),
@@ -160,8 +165,20 @@ class DecoderVerifier:
                      w_ck=self._dev(_lib.linear_layout(w.w_ck)), w_cv=self._dev(_lib.linear_layout(w.w_cv)),
                      b_cv=self._dev(w.b_cv))
             self._keep.append(t)
-            self.structs.append(_lib.DecoderLayerWeights(
-                **{k: v.data_ptr() for k, v in t.items() if k not in ("w_ck", "w_cv", "b_cv")}))
+            fields = {k: v.data_ptr() for k, v in t.items() if k not in ("w_ck", "w_cv", "b_cv")}
+            if not self.q8:
+                self.structs.append(_lib.DecoderLayerWeights(**fields))
+                continue
+            codes = {}
+            for name in self.MATRICES:
+                w = t[name]
+                c = torch.empty(w.shape, dtype=torch.int8, device=device)
+                d = torch.empty((w.shape[1] // 32, w.shape[0]), dtype=torch.float16, device=device)
+                _lib.edda_quantize_q8_0(w, c, d)
+                codes[name] = (c, d)
+                fields[name] = _lib.Q8Matrix(c.data_ptr(), d.data_ptr())
+            self.codes.append(codes)
+            self.structs.append(_lib.DecoderLayerWeightsQ8(**fields))
         shape = (self.n_frames, _lib.N_HEADS, _lib.HEAD_DIM)
         self.cross_k = [torch.empty(shape, dtype=torch.float16, device=device) for _ in self._keep]
         self.cross_v = [torch.empty(shape, dtype=torch.float16, device=device) for _ in self._keep]

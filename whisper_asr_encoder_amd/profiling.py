@@ -49,11 +49,22 @@ WORKLOADS = {
     # The decoder verification pass: block-sized GEMMs by fused variant (LayerNorm inside the
     # GEMM, cache append in the QKV epilogue, split K for the 1280-wide residual outputs).
     "decoder": ("decoder verification pass, 32 layers, 16-token block, 360-slot cache, 1500 frames", {
-        # skinny_gemm_kernel<act, residual, LayerNorm, append, split K>
-        "skinny_gemm_kernelILi0ELb0ELb1ELb1ELb0E": ("ln_qkv_append", ["skinny.hip", "layer_norm_row.hpp"]),
-        "skinny_gemm_kernelILi0ELb0ELb1ELb0ELb0E": ("ln_cross_query", ["skinny.hip", "layer_norm_row.hpp"]),
-        "skinny_gemm_kernelILi1ELb0ELb1ELb0ELb0E": ("ln_fc1_gelu", ["skinny.hip", "layer_norm_row.hpp"]),
-        "skinny_gemm_kernelILi0ELb1ELb0ELb0ELb1E": ("split_k_residual", ["skinny.hip"]),
+        # skinny_gemm_kernel<act, residual, LayerNorm, append, split K, Q8_0 weights>
+        "skinny_gemm_kernelILi0ELb0ELb1ELb1ELb0ELb0E": ("ln_qkv_append", ["skinny.hip", "layer_norm_row.hpp"]),
+        "skinny_gemm_kernelILi0ELb0ELb1ELb0ELb0ELb0E": ("ln_cross_query", ["skinny.hip", "layer_norm_row.hpp"]),
+        "skinny_gemm_kernelILi1ELb0ELb1ELb0ELb0ELb0E": ("ln_fc1_gelu", ["skinny.hip", "layer_norm_row.hpp"]),
+        "skinny_gemm_kernelILi0ELb1ELb0ELb0ELb1ELb0E": ("split_k_residual", ["skinny.hip"]),
+        "verify_kernelILi0E": ("verify_self", ["verify_attn.hip"]),
+        "verify_kernelILi1E": ("verify_cross", ["verify_attn.hip"]),
+    }),
+    # The same pass with Q8_0 projection weights (last template flag of the block GEMMs).
+    "decoder_q8": ("decoder verification pass with Q8_0 projection weights, 32 layers, 16-token block, "
+                   "360-slot cache, 1500 frames", {
+        "skinny_gemm_kernelILi0ELb0ELb1ELb1ELb0ELb1E": ("q8_ln_qkv_append", ["skinny.hip", "layer_norm_row.hpp"]),
+        "skinny_gemm_kernelILi0ELb0ELb1ELb0ELb0ELb1E": ("q8_ln_cross_query", ["skinny.hip", "layer_norm_row.hpp"]),
+        "skinny_gemm_kernelILi1ELb0ELb1ELb0ELb0ELb1E": ("q8_ln_fc1_gelu", ["skinny.hip", "layer_norm_row.hpp"]),
+        "skinny_gemm_kernelILi0ELb1ELb0ELb0ELb1ELb1E": ("q8_split_k_residual", ["skinny.hip"]),
+        "quantize_q8_0_kernel": ("quantize_q8_0 (setup, once per matrix)", ["skinny.hip"]),
         "verify_kernelILi0E": ("verify_self", ["verify_attn.hip"]),
         "verify_kernelILi1E": ("verify_cross", ["verify_attn.hip"]),
     }),
