@@ -295,3 +295,43 @@ def test_verify_graph_replay(torch):
         assert not va.workspace[:_lib.VERIFY_COUNTER_BYTES].any().item(), f"replay {rep}: arrival counters not zero"
         run()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_encoder_graph_replay(torch, cfg):
+    """Sublayers captured in a HIP graph (as the benchmark replays them) give the eager
+    results bit for bit on every replay, with eager work and synchronisations in between."""
+    from whisper_asr_encoder_amd.encoder import EncoderAttention
+    say(f"encoder graph replay, workload {cfg}, 2 sublayers")
+    wl = I.encoder_workload(cfg, layers=2)
+    weights = [wl.weights(l) for l in range(2)]
+    enc = EncoderAttention(weights, wl.batch, wl.seq_len, wl.chunk_len, None if cfg == 1 else wl.valid_len)
+    x = dev(torch, wl.x)
+    ys = [torch.empty((wl.rows, I.D_MODEL), dtype=torch.float16, device="cuda") for _ in range(2)]
+
+    def step():
+        for l in range(2):
+            enc.sublayer(x, l, ys[l])
+
+    step()
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in ys]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        enc.qkv.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for l in range(2):
+            assert torch.equal(ys[l], eager[l]), f"replay {rep}, layer {l} differs from eager"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
