@@ -160,7 +160,7 @@ edda_status edda_verify_attn(const void* q, int32_t n_q, const void* k, const vo
                              const uint32_t* mask_rows, void* o, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace edda_verify_attn needs: 0 for caches of at most 128 keys (one workgroup
+/* Bytes of workspace edda_verify_attn needs: 0 for caches of at most 512 keys (one workgroup
  * per head) or an invalid shape; longer caches split the keys into 128-key ranges, one
  * workgroup each, whose fp32 partial results the last workgroup of each head to finish merges
  * in the same launch: EDDA_VERIFY_COUNTER_BYTES + splits * n_q * 20 * 66 * 4 bytes. (The
@@ -450,7 +450,7 @@ edda_status edda_verify_attn_ex(const void* q, int32_t n_q, const void* k, const
                                 int32_t n_heads, int32_t mask_mode, const uint32_t* mask_rows, const float* sinks,
                                 void* o, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace edda_verify_attn_ex needs (0 for one 128-key split or an invalid shape). */
+/* Bytes of workspace edda_verify_attn_ex needs (0 for caches of at most 512 keys or an invalid shape). */
 size_t edda_verify_workspace_bytes_ex(int32_t n_q, int32_t n_kv, int32_t n_heads);
 
 /* Text of the calling thread's most recent error ("" after a successful call). */

@@ -65,8 +65,9 @@ def test_workspace_sizes(lib):
     assert lib.edda_encoder_workspace_bytes(1, -3) == 0
     assert lib.edda_verify_workspace_bytes(16, 100) == 0      # one split: no workspace
     assert lib.edda_verify_workspace_bytes(16, 128) == 0
+    assert lib.edda_verify_workspace_bytes(16, 512) == 0      # still one workgroup per head
     C = _lib.VERIFY_COUNTER_BYTES
-    assert lib.edda_verify_workspace_bytes(16, 129) == C + 2 * 16 * 20 * 66 * 4  # counters + partials
+    assert lib.edda_verify_workspace_bytes(16, 513) == C + 5 * 16 * 20 * 66 * 4  # counters + partials
     assert lib.edda_verify_workspace_bytes(3, 1500) == C + 12 * 3 * 20 * 66 * 4
     assert lib.edda_verify_workspace_bytes(17, 1500) == 0      # invalid n_q
     assert lib.edda_verify_workspace_bytes(1, 0) == 0
@@ -129,7 +130,7 @@ def ver(lib, q=A, n_q=16, k=A, v=A, n_kv=448, mask=None, o=B, ws=B + (1 << 24), 
     (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(o=None), INVALID),
     (dict(n_q=0), INVALID), (dict(n_q=17), INVALID), (dict(n_kv=0), INVALID), (dict(n_kv=-5), INVALID),
     (dict(q=ODD), MISALIGNED), (dict(o=ODD), MISALIGNED), (dict(mask=A + 2), MISALIGNED),
-    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+    (dict(ws=None, n_kv=1500), WORKSPACE), (dict(ws_bytes=16, n_kv=513), WORKSPACE),
 ])
 def test_verify_attn_rejects(lib, kw, status):
     assert ver(lib, **kw) == status
@@ -145,7 +146,8 @@ def ver_ex(lib, q=A, n_q=16, k=A, v=A, n_kv=448, h=8, mode=1, mask=None, sinks=N
     (dict(h=0), INVALID), (dict(h=65), INVALID), (dict(n_kv=0), INVALID), (dict(n_kv=1 << 20, h=64), INVALID),
     (dict(mode=3), INVALID), (dict(mode=-1), INVALID), (dict(mode=0), INVALID),
     (dict(mode=2, n_q=16, n_kv=15), INVALID), (dict(q=ODD), MISALIGNED), (dict(sinks=A + 2), MISALIGNED),
-    (dict(mode=0, mask=A + 2), MISALIGNED), (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+    (dict(mode=0, mask=A + 2), MISALIGNED), (dict(ws=None, n_kv=1500), WORKSPACE),
+    (dict(ws_bytes=16, n_kv=513), WORKSPACE),
 ])
 def test_verify_attn_ex_rejects(lib, kw, status):
     assert ver_ex(lib, **kw) == status
@@ -153,8 +155,8 @@ def test_verify_attn_ex_rejects(lib, kw, status):
 
 def test_verify_workspace_bytes_ex(lib):
     C = _lib.VERIFY_COUNTER_BYTES
-    assert lib.edda_verify_workspace_bytes_ex(16, 128, 64) == 0
-    assert lib.edda_verify_workspace_bytes_ex(16, 129, 64) == C + 2 * 16 * 64 * 66 * 4
+    assert lib.edda_verify_workspace_bytes_ex(16, 512, 64) == 0
+    assert lib.edda_verify_workspace_bytes_ex(16, 513, 64) == C + 5 * 16 * 64 * 66 * 4
     assert lib.edda_verify_workspace_bytes_ex(4, 1500, 20) == lib.edda_verify_workspace_bytes(4, 1500)
     assert lib.edda_verify_workspace_bytes_ex(4, 1500, 0) == 0
     assert lib.edda_verify_workspace_bytes_ex(4, 1500, 65) == 0

@@ -85,7 +85,8 @@ CASES = [
     (5, 100, 32, "causal", "mixed"), (16, 128, 64, "none", "mixed"), (16, 129, 20, "causal", "random"),
     (16, 360, 20, "causal", None), (16, 360, 20, "none", None), (9, 1500, 12, "none", "random"),
     (16, 1500, 20, "rows", "mixed"), (3, 2200, 40, "causal", "random"), (16, 4097, 64, "causal", "mixed"),
-    (16, 2100, 4, "rows", "random"), (7, 33, 2, "causal", "mixed"),
+    (16, 2100, 4, "rows", "random"), (7, 33, 2, "causal", "mixed"), (16, 300, 64, "rows", "mixed"),
+    (11, 512, 20, "causal", "random"), (16, 513, 6, "none", "mixed"),
 ]
 
 

@@ -6,11 +6,13 @@
 // The work is memory bound (each K/V byte is used by at most 16 queries) and small
 // (a few MB per call), so the time is latency: the key sequence is split across
 // many workgroups, one launch covers the call, and every load a wave needs is
-// issued at kernel start.  Workgroup (split, head) covers kSplitKeys keys, each of
-// its 4 waves 32 of them.  Per wave, on 16x16x32 MFMAs: S^T = K Q^T (lane l holds 8
-// scores of query l % 16), masked softmax statistics via cross-lane max/sum (lane
-// swaps between 16- and 32-lane halves), then O^T = V^T P^T with P kept in
-// registers as the B operand and V^T staged through a wave-private LDS tile.  The 4
+// issued at kernel start.  A cache of at most 512 keys takes one workgroup per head,
+// each of its 4 waves up to four 32-key chunks; a longer one is split into 128-key
+// ranges, one workgroup (split, head) each, 32 keys per wave.  Per wave and chunk, on
+// 16x16x32 MFMAs: S^T = K Q^T (lane l holds 8 scores of query l % 16); masked softmax
+// statistics over the wave's chunks via cross-lane max/sum (lane swaps between 16- and
+// 32-lane halves); then O^T = V^T P^T, summed over the chunks, with P kept in
+// registers as the B operand and V^T staged through wave-private LDS tiles.  The 4
 // waves merge in LDS.  With more than one split, each workgroup writes fp32 partials
 // (m, l, unnormalized o) to the workspace and counts itself in on a per-head arrival
 // counter; the last to arrive merges every split of its head:
@@ -23,6 +25,8 @@
 // per-head sinks join the final normalization as one extra logit with a zero value:
 //   M' = max(M, sink), L' = L 2^(M - M') + 2^(sink - M'), O = sum 2^(M - M') / L'.
 #include <math.h>
+
+#include <type_traits>
 
 #include "device.hpp"
 #include "kernels.hpp"
@@ -93,12 +97,14 @@ enum MaskMode { kMaskRows = 0, kMaskNone = 1, kMaskCausal = 2 };
 
 // grid (n_splits, n_heads), 256 threads.  counters / part_ml / part_o are used only
 // when n_splits > 1 (they are written by other workgroups, so not restrict).
-template <int kMode>
+// CPW: 32-key chunks per wave.  A workgroup covers kVWaves * 32 * CPW keys, wave w chunk c
+// the 32 keys from (c kVWaves + w) 32 on: CPW = ceil(n_kv / 128) with one split, else 1.
+template <int kMode, int CPW>
 __global__ __launch_bounds__(kVThreads) void verify_kernel(
     const f16* __restrict__ q, int q_stride, int n_q, const f16* __restrict__ k, const f16* __restrict__ v,
     int n_kv, int n_heads, const uint32_t* __restrict__ mask, int mask_words, const float* __restrict__ sinks,
     f16* __restrict__ o, uint32_t* counters, float* part_ml, float* part_o) {
-  __shared__ __attribute__((aligned(16))) f16 Vt[kVWaves][kHeadDim * kVtLd];
+  __shared__ __attribute__((aligned(16))) f16 Vt[kVWaves][CPW][kHeadDim * kVtLd];
   __shared__ float mw[kVWaves][kMaxQ], lw[kVWaves][kMaxQ];
   __shared__ __attribute__((aligned(16))) float ow[kVWaves][kMaxQ][kHeadDim + 4];
   __shared__ int last_arrival;
@@ -106,7 +112,8 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, G = lane >> 4;
   const int split = blockIdx.x, head = blockIdx.y, n_splits = gridDim.x;
-  const int key0 = split * kSplitKeys + wave * kWaveKeys;  // multiple of 32
+  const int wg_key0 = split * kSplitKeys * CPW;
+  auto chunk_key0 = [&](int c) { return wg_key0 + (c * kVWaves + wave) * kWaveKeys; };  // multiple of 32
   const int kKvStride = n_heads * kHeadDim;
   const int last_key = n_kv - 1;
   const f16x8 z8 = {};
@@ -115,83 +122,109 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
   // its last row and masked out below; element offsets fit 32 bits for any valid n_kv).
   const bool q_ok = r16 < n_q;
   const int q_row = min(r16, n_q - 1);
-  uint32_t bits = 0xffffffffu;
-  if constexpr (kMode == kMaskRows) bits = mask[(uint32_t)(q_row * mask_words + min(key0 >> 5, mask_words - 1))];
-  if constexpr (kMode == kMaskCausal) {
-    const int last = n_kv - n_q + q_row - key0;  // highest admitted key, relative to key0
-    bits = last < 0 ? 0u : last >= 31 ? 0xffffffffu : (uint32_t)((2ull << last) - 1);
+  uint32_t bits[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    const int key0 = chunk_key0(c);
+    bits[c] = 0xffffffffu;
+    if constexpr (kMode == kMaskRows)
+      bits[c] = mask[(uint32_t)(q_row * mask_words + min(key0 >> 5, mask_words - 1))];
+    if constexpr (kMode == kMaskCausal) {
+      const int last = n_kv - n_q + q_row - key0;  // highest admitted key, relative to key0
+      bits[c] = last < 0 ? 0u : last >= 31 ? 0xffffffffu : (uint32_t)((2ull << last) - 1);
+    }
   }
-  f16x8 qf[2], kf[2][2], va[2], vb[2];
+  f16x8 qf[2], kf[CPW][2][2], va[CPW][2], vb[CPW][2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) qf[s] = load16(q + (uint32_t)(q_row * q_stride + head * kHeadDim + 32 * s + 8 * G));
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    const int key = min(key0 + 16 * blk + r16, last_key);
-    const uint32_t off = (uint32_t)(key * kKvStride + head * kHeadDim + 8 * G);
-    kf[blk][0] = load16(k + off);
-    kf[blk][1] = load16(k + (off + 32));
-  }
-  // V rows as two keys per 16-byte group, for the transposed LDS staging.
+  for (int c = 0; c < CPW; ++c) {
+    const int key0 = chunk_key0(c);
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int u = lane + kWave * r;
-    const int kp = u >> 3, c8 = u & 7;
-    const int key = key0 + 2 * kp;
-    va[r] = load16(v + (uint32_t)(min(key, last_key) * kKvStride + head * kHeadDim + 8 * c8));
-    vb[r] = load16(v + (uint32_t)(min(key + 1, last_key) * kKvStride + head * kHeadDim + 8 * c8));
+    for (int blk = 0; blk < 2; ++blk) {
+      const int key = min(key0 + 16 * blk + r16, last_key);
+      const uint32_t off = (uint32_t)(key * kKvStride + head * kHeadDim + 8 * G);
+      kf[c][blk][0] = load16(k + off);
+      kf[c][blk][1] = load16(k + (off + 32));
+    }
+    // V rows as two keys per 16-byte group, for the transposed LDS staging.
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int u = lane + kWave * r;
+      const int kp = u >> 3, c8 = u & 7;
+      const int key = key0 + 2 * kp;
+      va[c][r] = load16(v + (uint32_t)(min(key, last_key) * kKvStride + head * kHeadDim + 8 * c8));
+      vb[c][r] = load16(v + (uint32_t)(min(key + 1, last_key) * kKvStride + head * kHeadDim + 8 * c8));
+    }
   }
   if (!q_ok) qf[0] = qf[1] = z8;
 
-  // Stage this wave's V tile transposed: Vt[d][key - key0]; key pairs share a 32-bit word.
+  // Stage this wave's V tiles transposed: Vt[d][key - key0]; key pairs share a 32-bit word.
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int u = lane + kWave * r;
-    const int kp = u >> 3, c8 = u & 7;
+  for (int c = 0; c < CPW; ++c)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<f16x2*>(&Vt[wave][(8 * c8 + e) * kVtLd + 2 * kp]) = (f16x2){va[r][e], vb[r][e]};
-  }
+    for (int r = 0; r < 2; ++r) {
+      const int u = lane + kWave * r;
+      const int kp = u >> 3, c8 = u & 7;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<f16x2*>(&Vt[wave][c][(8 * c8 + e) * kVtLd + 2 * kp]) = (f16x2){va[c][r][e], vb[c][r][e]};
+    }
 
-  // S^T for keys key0 + 16 blk + 4 G + r, query r16.
-  f32x4 sacc[2];
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    sacc[blk] = mfma_16x16x32(kf[blk][0], qf[0], (f32x4){});
-    sacc[blk] = mfma_16x16x32(kf[blk][1], qf[1], sacc[blk]);
-  }
-  if (!q_ok) bits = 0;
+  // S^T for keys key0 + 16 blk + 4 G + r of each chunk, query r16; one softmax over the
+  // wave's chunks.
   const float c_scale = kLog2e / 8.0f;
-  float sc[8];
+  float sc[CPW][8];
   float m = -INFINITY;
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
+  for (int c = 0; c < CPW; ++c) {
+    f32x4 sacc[2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int kk = 16 * blk + 4 * G + r;
-      const bool ok = ((bits >> kk) & 1u) && (key0 + kk < n_kv);
-      const float s = ok ? sacc[blk][r] * c_scale : -INFINITY;
-      sc[4 * blk + r] = s;
-      m = fmaxf(m, s);
+    for (int blk = 0; blk < 2; ++blk) {
+      sacc[blk] = mfma_16x16x32(kf[c][blk][0], qf[0], (f32x4){});
+      sacc[blk] = mfma_16x16x32(kf[c][blk][1], qf[1], sacc[blk]);
     }
+    const uint32_t b = q_ok ? bits[c] : 0u;
+    const int key0 = chunk_key0(c);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = 16 * blk + 4 * G + r;
+        const bool ok = ((b >> kk) & 1u) && (key0 + kk < n_kv);
+        const float sv = ok ? sacc[blk][r] * c_scale : -INFINITY;
+        sc[c][4 * blk + r] = sv;
+        m = fmaxf(m, sv);
+      }
+  }
   m = quad_max(m);
   float l = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float p = (m == -INFINITY) ? 0.0f : exp2_fast(sc[i] - m);
-    sc[i] = p;
-    l += p;
-  }
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = (m == -INFINITY) ? 0.0f : exp2_fast(sc[c][i] - m);
+      sc[c][i] = p;
+      l += p;
+    }
   l = quad_sum(l);
 
   __syncthreads();  // V^T tiles visible to every lane
-  const f16x8 pf = pack8(sc[0], sc[1], sc[2], sc[3], sc[4], sc[5], sc[6], sc[7]);
+  f16x8 pf[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+    pf[c] = pack8(sc[c][0], sc[c][1], sc[c][2], sc[c][3], sc[c][4], sc[c][5], sc[c][6], sc[c][7]);
 #pragma unroll
   for (int dd = 0; dd < 4; ++dd) {
-    const f16* row = &Vt[wave][(16 * dd + r16) * kVtLd];
-    const f16x4 lo = *reinterpret_cast<const f16x4*>(row + 4 * G);
-    const f16x4 hi = *reinterpret_cast<const f16x4*>(row + 16 + 4 * G);
-    const f16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    const f32x4 oa = mfma_16x16x32(vf, pf, (f32x4){});
+    f32x4 oa = {};
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const f16* row = &Vt[wave][c][(16 * dd + r16) * kVtLd];
+      const f16x4 lo = *reinterpret_cast<const f16x4*>(row + 4 * G);
+      const f16x4 hi = *reinterpret_cast<const f16x4*>(row + 16 + 4 * G);
+      const f16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      oa = mfma_16x16x32(vf, pf[c], oa);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) ow[wave][r16][16 * dd + 4 * G + r] = oa[r];
   }
@@ -304,7 +337,13 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
 
 }  // namespace
 
-int verify_num_splits(int n_kv) { return (n_kv + kSplitKeys - 1) / kSplitKeys; }
+namespace {
+constexpr int kOneWorkgroupKeys = 4 * kSplitKeys;  // up to 512 keys: one workgroup per head
+
+int chunks_per_wave(int n_kv) { return n_kv <= kOneWorkgroupKeys ? (n_kv + kSplitKeys - 1) / kSplitKeys : 1; }
+}  // namespace
+
+int verify_num_splits(int n_kv) { return n_kv <= kOneWorkgroupKeys ? 1 : (n_kv + kSplitKeys - 1) / kSplitKeys; }
 
 size_t verify_workspace_bytes(int n_q, int n_kv, int n_heads) {
   const int s = verify_num_splits(n_kv);
@@ -332,9 +371,18 @@ hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, co
                        static_cast<f16*>(o), counters, part_ml, part_o);
     return hipGetLastError();
   };
-  if (mask_mode == kMaskRows) return go(verify_kernel<kMaskRows>);
-  if (mask_mode == kMaskCausal) return go(verify_kernel<kMaskCausal>);
-  return go(verify_kernel<kMaskNone>);
+  auto by_chunks = [&](auto mode_c) {
+    constexpr int M = decltype(mode_c)::value;
+    switch (chunks_per_wave(n_kv)) {
+      case 4: return go(verify_kernel<M, 4>);
+      case 3: return go(verify_kernel<M, 3>);
+      case 2: return go(verify_kernel<M, 2>);
+      default: return go(verify_kernel<M, 1>);
+    }
+  };
+  if (mask_mode == kMaskRows) return by_chunks(std::integral_constant<int, kMaskRows>());
+  if (mask_mode == kMaskCausal) return by_chunks(std::integral_constant<int, kMaskCausal>());
+  return by_chunks(std::integral_constant<int, kMaskNone>());
 }
 
 }  // namespace edda
