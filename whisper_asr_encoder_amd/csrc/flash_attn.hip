@@ -82,12 +82,6 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(n) : "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
-// Workgroup barrier with no memory wait: orders LDS reads against later DMA writes only.
-__device__ __forceinline__ void plain_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
 // 16-byte chunk swizzle of a 128-byte row: h = (row >> 1) & 7 rotated right by one bit.
 // Rows 2m and 2m+1 fall in opposite bank halves, so K fragment reads (one row per lane)
 // need h bijective over 8 rows; transposed V reads touch rows 4m..4m+3 at once, so rows
@@ -350,11 +344,13 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
   // barrier b and the next one).  Query group 0 runs the MFMA phase of iteration i
   // (QK of tile i, PV of tile i-1) in slot 2i and the softmax of tile i in slot 2i+1;
   // query group 1 runs one slot later, so on every SIMD one wave of each group alternates
-  // MFMA and VALU work against the other.  Both groups pass the same 2 n_iter + 2
-  // barriers.  Tile t's stage is read from slot 2t to slot 2t+3, so tile t+2 may be
-  // loaded from slot 2t on: each wave spreads its share of tile i+2 over its MFMA phase
-  // of iteration i (slot 2i or 2i+1) and waits for tile i before barrier 2i.  The odd
-  // barriers only order LDS reads and wait for no memory.  The first and last tiles are
+  // MFMA and VALU work against the other.  Only the even barriers are workgroup barriers
+  // (both groups pass the same n_iter + 1 of them); an odd slot boundary is a scheduling
+  // fence alone, since no LDS hazard crosses it: tile t's stage is read from slot 2t to
+  // slot 2t+3 and reloaded with tile t+4 after barrier 2t+4, each wave spreading its share
+  // of tile i+2 over its MFMA phase of iteration i (slot 2i or 2i+1) and waiting for tile i
+  // before barrier 2i.  (A workgroup barrier at the odd boundaries too, forcing the two
+  // groups to swap roles in step, measured 3 % slower.)  The first and last tiles are
   // peeled so the steady-state body has no conditions.  Q's DMA is issued before tile 0's,
   // so the wait for tile 0 at barrier 0 covers it too.
   auto even_barrier = [&](int j) {  // barrier 2j: tile j has landed in LDS
@@ -364,11 +360,12 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
       wait_vmcnt_barrier<0>();
     }
   };
-  auto odd_barrier = [&]() { plain_barrier(); };
+  auto odd_barrier = [&]() { __builtin_amdgcn_sched_barrier(0); };  // slot boundary: no s_barrier
   const int nl = n_iter - 1;  // last tile
-  // The workgroup's 128 query rows reach LDS by DMA into stage 3 (first written by tile 3,
-  // after barrier 2; every wave reads its Q fragments before barrier 1), two instructions
-  // of 8 rows per wave, issued before the first tiles.  Rows past the segment load its last
+  // The workgroup's 128 query rows reach LDS by DMA into stage 3 (whose first tile, tile 3,
+  // is copied after slot boundary 2, the second workgroup barrier; every wave reads its Q
+  // fragments before that barrier), two instructions of 8 rows per wave, issued before the
+  // first tiles.  Rows past the segment load its last
   // row (finite values whose outputs are never stored).
   char* const q_lds = smem + 3 * kStageB;
   {
