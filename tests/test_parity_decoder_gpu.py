@@ -98,8 +98,9 @@ def test_cross_kv(torch):
     check(host(dv.cross_v[0]), v, "cross V")
 
 
-def run_layer(torch, layer, trial, kind, n_kv=None, in_place=False):
-    """One decoder layer on GPU and oracle; kind = 'causal' (chain of 16) or 'tree' (5 beams)."""
+def run_layer(torch, layer, trial, kind, n_kv=None, in_place=False, frames=1500):
+    """One decoder layer on GPU and oracle; kind = 'causal' (chain of 16) or 'tree' (5 beams);
+    `frames` rows of the encoder output feed the cross-attention."""
     from whisper_asr_encoder_amd.encoder import DecoderVerifier
     w = I.decoder_layer_weights(layer)
     if kind == "causal":
@@ -117,8 +118,8 @@ def run_layer(torch, layer, trial, kind, n_kv=None, in_place=False):
     kc[:nk], vc[:nk] = case.k, case.v
     kc[nk:] = r.standard_normal((cap - nk, 20, 64)).astype(np.float16)   # beyond n_kv: must stay
     x = I.decoder_block_input(trial, n_q)
-    enc = I.encoder_workload(1, layers=1).x
-    dv = DecoderVerifier([w], max_kv=cap)
+    enc = np.ascontiguousarray(I.encoder_workload(1, layers=1).x[:frames])
+    dv = DecoderVerifier([w], max_kv=cap, n_frames=frames)
     dv.set_encoder_output(dev(torch, enc))
     ck, cv = DL.cross_kv(enc, w.w_ck, w.w_cv, w.b_cv)
     ck16, cv16 = host(dv.cross_k[0]).astype(np.float16), host(dv.cross_v[0]).astype(np.float16)
@@ -148,6 +149,16 @@ def test_decoder_layer(torch, trial, layer, kind):
     assert np.array_equal(vd[others], vc[others].astype(np.float32)), "cache rows outside the block changed"
     check(kd[slots], ref["k_cache"][slots], "appended K rows")
     check(vd[slots], ref["v_cache"][slots], "appended V rows")
+
+
+@pytest.mark.parametrize("frames", [300, 100])
+def test_decoder_layer_short_encoder_output(torch, frames):
+    """Cross-attention over fewer frames: one workgroup per head (the 1500-frame layers split
+    the frames over twelve workgroups per head)."""
+    say(f"decoder layer: {frames} encoder frames")
+    y, kd, _, ref, _, _, slots = run_layer(torch, 7, 5, "causal", frames=frames)
+    check(y, ref["y"], "y")
+    check(kd[slots], ref["k_cache"][slots], "appended K rows")
 
 
 def test_decoder_layer_short_cache_in_place(torch):

@@ -112,7 +112,7 @@ def test_linear_q8(torch, rows, k, n, act, res):
     check(y.float().cpu().numpy(), ref, "y")
 
 
-def run_layer(torch, layer, trial, kind, q8):
+def run_layer(torch, layer, trial, kind, q8, frames=1500):
     from whisper_asr_encoder_amd.encoder import DecoderVerifier
     w = I.decoder_layer_weights(layer)
     case = I.verify_self_case(trial, layer) if kind == "causal" else I.verify_tree_case(trial, layer)
@@ -123,8 +123,8 @@ def run_layer(torch, layer, trial, kind, q8):
     vc = np.zeros((cap, 20, 64), dtype=np.float16)
     kc[:nk], vc[:nk] = case.k, case.v
     x = I.decoder_block_input(trial, n_q)
-    dv = DecoderVerifier([w], max_kv=cap, q8=q8)
-    dv.set_encoder_output(dev(torch, I.encoder_workload(1, layers=1).x))
+    dv = DecoderVerifier([w], max_kv=cap, q8=q8, n_frames=frames)
+    dv.set_encoder_output(dev(torch, np.ascontiguousarray(I.encoder_workload(1, layers=1).x[:frames])))
     k_d, v_d = dev(torch, kc), dev(torch, vc)
     y = torch.full((n_q, 1280), float("nan"), dtype=torch.float16, device="cuda")
     mask = None if case.mask is None else torch.from_numpy(_lib.pack_mask_rows(case.mask).view(np.int32)).cuda()
@@ -135,15 +135,16 @@ def run_layer(torch, layer, trial, kind, q8):
     return w, x, slots, kc, vc, nk, case.mask, ck16, cv16, y.float().cpu().numpy(), k_d.float().cpu().numpy()
 
 
-@pytest.mark.parametrize("trial,layer,kind", [(0, 0, "causal"), (3, 31, "causal"), (1, 5, "tree")])
-def test_decoder_layer_q8(torch, trial, layer, kind):
-    say(f"Q8 decoder verification layer trial {trial} layer {layer} {kind}")
-    w, x, slots, kc, vc, nk, mask, ck16, cv16, y, kd = run_layer(torch, layer, trial, kind, q8=True)
+@pytest.mark.parametrize("trial,layer,kind,frames", [(0, 0, "causal", 1500), (3, 31, "causal", 1500),
+                                                    (1, 5, "tree", 1500), (2, 11, "causal", 300)])
+def test_decoder_layer_q8(torch, trial, layer, kind, frames):
+    say(f"Q8 decoder verification layer trial {trial} layer {layer} {kind}, {frames} frames")
+    w, x, slots, kc, vc, nk, mask, ck16, cv16, y, kd = run_layer(torch, layer, trial, kind, q8=True, frames=frames)
     wq = Q.DequantizedDecoderWeights(w, Q.quantize_decoder_weights(w))
     ref = DL.decoder_verify_layer(x, wq, slots, kc, vc, nk, mask, ck16, cv16)
     check(y, ref["y"], "y")
     check(kd[slots], ref["k_cache"][slots], "appended K rows")
-    y16 = run_layer(torch, layer, trial, kind, q8=False)[9]
+    y16 = run_layer(torch, layer, trial, kind, q8=False, frames=frames)[9]
     rel = np.linalg.norm(y - y16) / np.linalg.norm(y16)
     say(f"  Q8 vs fp16 weights: y relative Frobenius distance {rel:.3e} (weight quantization)")
     assert rel < 2e-2
