@@ -540,8 +540,8 @@ def main():
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is a design note only)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "edda runs on one GPU: --gpus must be 1 (sharding across GPUs is "
+                                   "described in the design notes, not implemented)", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

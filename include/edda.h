@@ -58,7 +58,7 @@ extern "C" {
 typedef enum {
   EDDA_OK = 0,
   EDDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, size out of range            */
-  EDDA_ERR_UNSUPPORTED = 2,      /* valid request this build does not handle  */
+  EDDA_ERR_UNSUPPORTED = 2,      /* valid request the library does not handle */
   EDDA_ERR_MISALIGNED = 3,       /* a pointer is not 16-byte aligned           */
   EDDA_ERR_WORKSPACE = 4,        /* workspace missing or too small             */
   EDDA_ERR_HIP = 5               /* the HIP runtime reported a launch error    */

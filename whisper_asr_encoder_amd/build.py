@@ -3,8 +3,8 @@
     python -m whisper_asr_encoder_amd.build        # or: python whisper_asr_encoder_amd/build.py
 
 Each source compiles to an object in parallel, then one hipcc link produces
-whisper_asr_encoder_amd/libedda.so. Always recompiles (the build check must
-prove the sources compile).
+whisper_asr_encoder_amd/libedda.so. Always recompiles, so a successful run
+shows that the current sources compile.
 """
 from __future__ import annotations
 
