@@ -98,9 +98,13 @@ def oracle_layer(x, w, batch, seq_len, chunk_len, valid_len, rows=None):
     (1, 130, 1, None),          # chunk of one frame: O = V row
     (1, 200, 65, [199]),        # chunk just above a key tile
     (3, 96, 32, [96, 40, 33]),  # several windows, chunked and padded
+    # More windows than one launch takes (256): the second launch's windows and their valid
+    # lengths are indexed from its first window.
+    (300, 8, 0, [1 + b % 8 for b in range(300)]),
+    (260, 24, 8, [24 - b % 24 for b in range(260)]),
 ])
 def test_encoder_small(torch, batch, seq_len, chunk_len, valid):
-    say(f"encoder small batch={batch} seq={seq_len} chunk={chunk_len} valid={valid}")
+    say(f"encoder small batch={batch} seq={seq_len} chunk={chunk_len} valid={valid if batch <= 16 else '...'}")
     wl = I.encoder_workload(0, batch=batch, seq_len=seq_len, chunk_len=chunk_len, layers=1, valid_len=valid)
     w = wl.weights(0)
     ys, qkvs = run_encoder(torch, wl.x, [w], batch, seq_len, chunk_len, wl.valid_len)
