@@ -99,11 +99,16 @@ def test_cross_kv(torch):
 
 
 def run_layer(torch, layer, trial, kind, n_kv=None, in_place=False, frames=1500):
-    """One decoder layer on GPU and oracle; kind = 'causal' (chain of 16) or 'tree' (5 beams);
-    `frames` rows of the encoder output feed the cross-attention."""
+    """One decoder layer on GPU and oracle; kind = 'causal' (chain of 16), 'tree' (5 beams) or
+    'single' (one token: a plain decoding step); `frames` rows of the encoder output feed the
+    cross-attention."""
     from whisper_asr_encoder_amd.encoder import DecoderVerifier
     w = I.decoder_layer_weights(layer)
-    if kind == "causal":
+    if kind == "single":
+        case = I.verify_self_case(trial, layer, n_kv=n_kv, n_q=1)
+        n_q, nk = 1, case.n_kv
+        slots = [nk - 1]
+    elif kind == "causal":
         case = I.verify_self_case(trial, layer, n_kv=n_kv)
         n_q, nk = 16, case.n_kv
         slots = list(range(nk - n_q, nk))
@@ -139,7 +144,8 @@ def VerifyRows(torch, mask):
     return torch.from_numpy(_lib.pack_mask_rows(mask).view(np.int32)).cuda()
 
 
-@pytest.mark.parametrize("trial,layer,kind", [(0, 0, "causal"), (3, 31, "causal"), (1, 5, "tree"), (6, 17, "tree")])
+@pytest.mark.parametrize("trial,layer,kind", [(0, 0, "causal"), (3, 31, "causal"), (1, 5, "tree"), (6, 17, "tree"),
+                                             (4, 12, "single")])
 def test_decoder_layer(torch, trial, layer, kind):
     say(f"decoder verification layer trial {trial} layer {layer} {kind}")
     y, kd, vd, ref, kc, vc, slots = run_layer(torch, layer, trial, kind)
