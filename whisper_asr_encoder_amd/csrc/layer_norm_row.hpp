@@ -14,10 +14,26 @@ namespace edda {
 
 constexpr float kLnEps = 1e-5f;
 
+// Sum over the 64 lanes, in registers.  Within each 16-lane row a lane adds its partner's value
+// with a symmetric partner relation (quad neighbours at distances 1 and 2, then mirrored lanes
+// within 8 and 16: DPP), so every lane of a row holds the same row sum; the DPP row broadcasts
+// then add row 0 into row 1 and row 2 into row 3 (from lane 15 of the row below), and rows 0-1
+// into rows 2-3 (from lane 31), so lane 63 holds the total, which v_readlane hands to every
+// lane.  (The gfx950 lane-swap builtins are avoided here: combined in one commutative operation,
+// their two results have been compiled as if they were the same value.)
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float ln_dpp_add(float v) {
+  const int p = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask, 0xF, false);
+  return v + __builtin_bit_cast(float, p);
+}
 __device__ __forceinline__ float ln_wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v = ln_dpp_add<0xB1, 0xF>(v);   // quad_perm [1, 0, 3, 2]
+  v = ln_dpp_add<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
+  v = ln_dpp_add<0x141, 0xF>(v);  // row_half_mirror
+  v = ln_dpp_add<0x140, 0xF>(v);  // row_mirror
+  v = ln_dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = ln_dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // The row's values and its gamma / beta slices in registers (loaded together, so one memory
@@ -38,6 +54,9 @@ __device__ __forceinline__ LnRow<kGroups> layer_norm_load(const f16* __restrict_
     r.g[c] = *reinterpret_cast<const f16x4*>(gamma + f);
     r.b[c] = *reinterpret_cast<const f16x4*>(beta + f);
   }
+  // Keep every load of the row here, ahead of the reductions (left to itself the scheduler
+  // issues gamma and beta after them: a second memory round trip).
+  __builtin_amdgcn_sched_barrier(0);
   return r;
 }
 
