@@ -187,6 +187,25 @@ def test_encoder_layer_full_window_sampled_rows(torch):
     check(got[rows], ref["y"], "sampled rows")
 
 
+def test_encoder_layer_four_windows_sampled_rows(torch):
+    """Four padded 30 s windows in one call (6000 rows: every GEMM takes more than one round of
+    tiles over the CUs); rows sampled in every window, around tile and valid-length edges."""
+    valid = [1500, 900, 1200, 300]
+    say(f"encoder layer, 4 windows of 1500 rows, valid {valid}, sampled rows")
+    w = I.full_layer_weights(1, 17)
+    enc = make_encoder(torch, [w], 4, 1500, 0, valid)
+    x = I.encoder_workload(1, batch=4, seq_len=1500, layers=1).x
+    y = nan_like(torch, x.shape)
+    enc.layer(dev(torch, x), 0, y)
+    torch.cuda.synchronize()
+    got = host(y)
+    assert np.isfinite(got).all()
+    local = np.unique(np.concatenate([np.arange(0, 1500, 97), [1, 127, 128, 299, 300, 899, 900, 1199, 1200, 1499]]))
+    rows = np.concatenate([b * 1500 + local for b in range(4)])
+    ref = L.encoder_layer(x, w, 4, 1500, 0, valid, 20, rows=rows)
+    check(got[rows], ref["y"], "sampled rows")
+
+
 def test_encoder_layer_in_place_matches(torch):
     say("encoder layer in place (y = x) equals out of place")
     w = I.full_layer_weights(1, 5)
