@@ -6,13 +6,13 @@
 // The work is memory bound (each K/V byte is used by at most 16 queries) and small
 // (a few MB per call), so the time is latency: the key sequence is split across
 // many workgroups, one launch covers the call, and every load a wave needs is
-// issued at kernel start.  A cache of at most 512 keys takes one workgroup per head,
-// each of its 4 waves up to four 32-key chunks; a longer one is split into 128-key
-// ranges, one workgroup (split, head) each, 32 keys per wave.  Per wave and chunk, on
+// issued at kernel start.  A cache of at most 512 keys takes one workgroup per head: 4
+// waves of up to three 32-key chunks (384 keys), else 8 waves of two; a longer one is split
+// into 128-key ranges, one workgroup (split, head) each, 32 keys per wave.  Per wave and chunk, on
 // 16x16x32 MFMAs: S^T = K Q^T (lane l holds 8 scores of query l % 16); masked softmax
 // statistics over the wave's chunks via cross-lane max/sum (lane swaps between 16- and
 // 32-lane halves); then O^T = V^T P^T, summed over the chunks, with P kept in
-// registers as the B operand and V^T staged through wave-private LDS tiles.  The 4
+// registers as the B operand and V^T staged through wave-private LDS tiles.  The
 // waves merge in LDS.  With more than one split, each workgroup writes fp32 partials
 // (m, l, unnormalized o) to the workspace and counts itself in on a per-head arrival
 // counter; the last to arrive merges every split of its head:
@@ -97,23 +97,24 @@ enum MaskMode { kMaskRows = 0, kMaskNone = 1, kMaskCausal = 2 };
 
 // grid (n_splits, n_heads), 256 threads.  counters / part_ml / part_o are used only
 // when n_splits > 1 (they are written by other workgroups, so not restrict).
-// CPW: 32-key chunks per wave.  A workgroup covers kVWaves * 32 * CPW keys, wave w chunk c
-// the 32 keys from (c kVWaves + w) 32 on: CPW = ceil(n_kv / 128) with one split, else 1.
-template <int kMode, int CPW>
-__global__ __launch_bounds__(kVThreads) void verify_kernel(
+// NW waves (4 or 8) of CPW 32-key chunks each.  A workgroup covers NW * 32 * CPW keys, wave w
+// chunk c the 32 keys from (c NW + w) 32 on: one split of up to 512 keys (4 waves of up to 3
+// chunks up to 384 keys, else 8 waves of 2 chunks), or 128-key splits of 4 waves of one chunk.
+template <int kMode, int CPW, int NW>
+__global__ __launch_bounds__(NW * kWave) void verify_kernel(
     const f16* __restrict__ q, int q_stride, int n_q, const f16* __restrict__ k, const f16* __restrict__ v,
     int n_kv, int n_heads, const uint32_t* __restrict__ mask, int mask_words, const float* __restrict__ sinks,
     f16* __restrict__ o, uint32_t* counters, float* part_ml, float* part_o) {
-  __shared__ __attribute__((aligned(16))) f16 Vt[kVWaves][CPW][kHeadDim * kVtLd];
-  __shared__ float mw[kVWaves][kMaxQ], lw[kVWaves][kMaxQ];
-  __shared__ __attribute__((aligned(16))) float ow[kVWaves][kMaxQ][kHeadDim + 4];
+  __shared__ __attribute__((aligned(16))) f16 Vt[NW][CPW][kHeadDim * kVtLd];
+  __shared__ float mw[NW][kMaxQ], lw[NW][kMaxQ];
+  __shared__ __attribute__((aligned(16))) float ow[NW][kMaxQ][kHeadDim + 4];
   __shared__ int last_arrival;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, G = lane >> 4;
   const int split = blockIdx.x, head = blockIdx.y, n_splits = gridDim.x;
-  const int wg_key0 = split * kSplitKeys * CPW;
-  auto chunk_key0 = [&](int c) { return wg_key0 + (c * kVWaves + wave) * kWaveKeys; };  // multiple of 32
+  const int wg_key0 = split * NW * kWaveKeys * CPW;
+  auto chunk_key0 = [&](int c) { return wg_key0 + (c * NW + wave) * kWaveKeys; };  // multiple of 32
   const int kKvStride = n_heads * kHeadDim;
   const int last_key = n_kv - 1;
   const f16x8 z8 = {};
@@ -234,15 +235,16 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
   }
   __syncthreads();
 
-  // Merge the 4 waves: thread -> (query mq, dims d0 .. d0 + 3).
-  const int mq = tid >> 4, d0 = (tid & 15) * 4;
+  // Merge the NW waves: thread -> (query mq, dims d0 .. d0 + 3); with 8 waves the threads past
+  // the 16th query read query 15's values and store nothing.
+  const int mq_t = tid >> 4, mq = min(mq_t, kMaxQ - 1), d0 = (tid & 15) * 4;
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kVWaves; ++w) M = fmaxf(M, mw[w][mq]);
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w][mq]);
   float L = 0.0f, acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (M != -INFINITY) {
 #pragma unroll
-    for (int w = 0; w < kVWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float wt = exp2_fast(mw[w][mq] - M);
       L += lw[w][mq] * wt;
       const f32x4 ov = *reinterpret_cast<const f32x4*>(&ow[w][mq][d0]);
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
       for (int j = 0; j < 4; ++j) acc[j] += ov[j] * wt;
     }
   }
-  const bool row_ok = mq < n_q;
+  const bool row_ok = mq_t < n_q;
   f16* out = o + ((size_t)mq * n_heads + head) * kHeadDim + d0;
   const float sink2 = sinks ? sinks[head] * kLog2e : -INFINITY;
   if (n_splits == 1) {
@@ -339,8 +341,6 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(
 
 namespace {
 constexpr int kOneWorkgroupKeys = 4 * kSplitKeys;  // up to 512 keys: one workgroup per head
-
-int chunks_per_wave(int n_kv) { return n_kv <= kOneWorkgroupKeys ? (n_kv + kSplitKeys - 1) / kSplitKeys : 1; }
 }  // namespace
 
 int verify_num_splits(int n_kv) { return n_kv <= kOneWorkgroupKeys ? 1 : (n_kv + kSplitKeys - 1) / kSplitKeys; }
@@ -365,20 +365,24 @@ hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, co
     part_o = part_ml + (size_t)n_splits * n_q * n_heads * 2;
   }
   const dim3 grid(n_splits, n_heads);
+  int threads = kVThreads;
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, dim3(kVThreads), 0, stream, static_cast<const f16*>(q), q_stride, n_q,
+    hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, stream, static_cast<const f16*>(q), q_stride, n_q,
                        static_cast<const f16*>(k), static_cast<const f16*>(v), n_kv, n_heads, mask, mask_words, sinks,
                        static_cast<f16*>(o), counters, part_ml, part_o);
     return hipGetLastError();
   };
+  // One split: 4 waves of 1-3 chunks up to 384 keys, else 8 waves of 2 (measured: at 360
+  // keys 4 waves of 3 chunks beat 8 of 2 by 7 %, at 448 keys 8 of 2 beat 4 of 4 by 12 %).
   auto by_chunks = [&](auto mode_c) {
     constexpr int M = decltype(mode_c)::value;
-    switch (chunks_per_wave(n_kv)) {
-      case 4: return go(verify_kernel<M, 4>);
-      case 3: return go(verify_kernel<M, 3>);
-      case 2: return go(verify_kernel<M, 2>);
-      default: return go(verify_kernel<M, 1>);
+    if (n_splits == 1 && n_kv > 3 * kSplitKeys) {
+      threads = 8 * kWave;
+      return go(verify_kernel<M, 2, 8>);
     }
+    if (n_splits == 1 && n_kv > 2 * kSplitKeys) return go(verify_kernel<M, 3, kVWaves>);
+    if (n_splits == 1 && n_kv > kSplitKeys) return go(verify_kernel<M, 2, kVWaves>);
+    return go(verify_kernel<M, 1, kVWaves>);
   };
   if (mask_mode == kMaskRows) return by_chunks(std::integral_constant<int, kMaskRows>());
   if (mask_mode == kMaskCausal) return by_chunks(std::integral_constant<int, kMaskCausal>());
