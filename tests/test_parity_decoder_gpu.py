@@ -125,16 +125,18 @@ def run_layer(torch, layer, trial, kind, n_kv=None, in_place=False, frames=1500)
     x = I.decoder_block_input(trial, n_q)
     enc = np.ascontiguousarray(I.encoder_workload(1, layers=1).x[:frames])
     dv = DecoderVerifier([w], max_kv=cap, n_frames=frames)
-    dv.set_encoder_output(dev(torch, enc))
+    # The oracle's own cross K/V, rounded once to fp16 on the host, feed both sides (the
+    # projection on the device, edda_cross_kv, is checked on its own in test_cross_kv).
     ck, cv = DL.cross_kv(enc, w.w_ck, w.w_cv, w.b_cv)
-    ck16, cv16 = host(dv.cross_k[0]).astype(np.float16), host(dv.cross_v[0]).astype(np.float16)
+    ck16, cv16 = ck.astype(np.float16), cv.astype(np.float16)
+    dv.cross_k[0].copy_(dev(torch, ck16))
+    dv.cross_v[0].copy_(dev(torch, cv16))
     k_d, v_d = dev(torch, kc), dev(torch, vc)
     xd = dev(torch, x)
     y = xd if in_place else torch.full((n_q, 1280), float("nan"), dtype=torch.float16, device="cuda")
     mask = case.mask
     dv.layer(xd, 0, slots, k_d, v_d, nk, None if mask is None else VerifyRows(torch, mask), y)
     torch.cuda.synchronize()
-    # The oracle reads the GPU's own cross K/V (fp16, checked separately above).
     ref = DL.decoder_verify_layer(x, w, slots, kc, vc, nk, mask, ck16, cv16)
     assert not dv.workspace[:_lib.VERIFY_COUNTER_BYTES].any().item(), "arrival counters not returned to zero"
     return host(y), host(k_d), host(v_d), ref, kc, vc, slots

@@ -174,20 +174,27 @@ def test_config_chunked_45s(torch):
 
 
 def test_config_batched_windows(torch):
-    say("workload: 16 windows with padded key tails, 32 sublayers (sampled)")
+    """All 16 windows at layer 0 (each with its own drawn valid length, so its own masked tail
+    tile), rows around every valid length; layers 17 and 31 on a spread of windows."""
+    say("workload: 16 windows with padded key tails, 32 sublayers (sampled rows of every window)")
     wl = I.encoder_workload(3)
     weights = [wl.weights(l) for l in range(wl.layers)]
     ys, _ = run_encoder(torch, wl.x, weights, wl.batch, wl.seq_len, 0, wl.valid_len, keep=(0, 17, 31))
     order = np.argsort(wl.valid_len)
-    picks = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
     rng = np.random.default_rng(11)
-    for l, wins in ((0, picks), (31, picks[:1]), (17, picks[1:2])):
+    S = wl.seq_len
+    plan = ((0, list(range(wl.batch))),
+            (17, [int(order[0]), int(order[5]), int(order[10]), int(order[-1])]),
+            (31, [int(order[2]), int(order[8]), int(order[13])]))
+    for l, wins in plan:
         for b in wins:
-            rows = b * wl.seq_len + np.sort(rng.choice(wl.seq_len, size=96, replace=False))
-            rows = np.unique(np.concatenate([rows, [b * wl.seq_len, b * wl.seq_len + wl.seq_len - 1,
-                                                    b * wl.seq_len + int(wl.valid_len[b]) - 1]]))
-            ref = oracle_layer(wl.x, weights[l], wl.batch, wl.seq_len, 0, wl.valid_len, rows=rows)
-            check(ys[l][rows], ref["y"], f"layer {l} window {b} (valid {wl.valid_len[b]}) y")
+            v = int(wl.valid_len[b])
+            near = [r for r in range(v - 3, v + 3) if 0 <= r < S]  # both sides of the valid length
+            tile = [r for r in (128 * (v // 128), 128 * (v // 128) + 127) if r < S]  # its query tile
+            local = np.unique(np.concatenate([rng.choice(S, size=48, replace=False), [0, S - 1], near, tile]))
+            rows = b * S + local
+            ref = oracle_layer(wl.x, weights[l], wl.batch, S, 0, wl.valid_len, rows=rows)
+            check(ys[l][rows], ref["y"], f"layer {l} window {b} (valid {v}) y")
 
 
 # ---------------------------------------------------------------------------

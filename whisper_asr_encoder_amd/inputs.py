@@ -390,3 +390,48 @@ def decoder_layer_weights(layer: int, seed: int = 0, cfg: int = 4) -> DecoderLay
 def decoder_block_input(trial: int = 0, n_q: int = VERIFY_BLOCK, seed: int = 0, cfg: int = 4) -> np.ndarray:
     """Residual-stream rows of the n_q block tokens [n_q, 1280] ~ N(0, 1)."""
     return normal_f16(rng_for(seed, cfg, 0, T_DX, trial), (n_q, D_MODEL), 1.0)
+
+
+# --------------------------------------------------------------------------------------
+# Packed QKV buffers with planted scores (online-softmax edge cases).
+# --------------------------------------------------------------------------------------
+
+PLANT_KEY_VALUE = 4.0   # the one non-zero coordinate of a planted key
+PLANT_COORDS = 8        # coordinates 0..7 of every head are reserved for planting
+
+
+@dataclass
+class Plant:
+    """Query rows `rows` (window-local) of window `window` hold a * e_c in every head and the
+    key at window-local position `key` holds PLANT_KEY_VALUE * e_c; c = `coord` (< 8).  With
+    the reserved coordinates of every other key zero, these rows score 0 against every other
+    key and a * PLANT_KEY_VALUE / 8 against the planted one."""
+    coord: int
+    a: float
+    key: int
+    rows: list
+    window: int = 0
+
+
+def plant_scale(excess_log2: float) -> float:
+    """Query amplitude a whose score against a planted key is `excess_log2` in log2 units
+    (a * PLANT_KEY_VALUE / 8 * log2(e) = excess)."""
+    return float(excess_log2) * 8.0 / (PLANT_KEY_VALUE * math.log2(math.e))
+
+
+def planted_qkv(batch: int, seq_len: int, plants, seed: int = 0) -> np.ndarray:
+    """fp16 [batch*seq_len, 3840] packed Q | K | V drawn N(0, 1), with the reserved key
+    coordinates zeroed and the plants written in (all 20 heads alike)."""
+    r = rng_for(seed, 90, 0, T_X)
+    qkv = r.standard_normal((batch * seq_len, QKV_COLS)).astype(np.float16)
+    q = qkv[:, :D_MODEL].reshape(-1, N_HEADS, HEAD_DIM)
+    k = qkv[:, D_MODEL:2 * D_MODEL].reshape(-1, N_HEADS, HEAD_DIM)
+    k[:, :, :PLANT_COORDS] = 0
+    for p in plants:
+        base = p.window * seq_len
+        for row in p.rows:
+            q[base + row] = 0
+            q[base + row, :, p.coord] = np.float16(p.a)
+        k[base + p.key] = 0
+        k[base + p.key, :, p.coord] = np.float16(PLANT_KEY_VALUE)
+    return qkv
