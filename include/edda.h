@@ -29,6 +29,16 @@
  *  - Arguments are validated on the host before anything is enqueued; an
  *    invalid call returns a non-zero status, enqueues nothing and sets the text
  *    returned by edda_last_error(). Nothing falls back silently.
+ *  - WEIGHT LAYOUT. Every weight matrix argument is output-feature major
+ *    ("Linear" layout, [out_features, in_features], row n = the inputs of
+ *    output feature n), the layout Whisper checkpoints store q/k/v/out
+ *    projections in; both GEMM operands are then K-contiguous. This replaces
+ *    the math layout y = x * W with W [in, out]: the packed QKV weight is
+ *    passed as w_qkv [3840, 1280] = W_qkv^T, NOT as the [1280, 3840] matrix
+ *    whose column blocks are Q | K | V, and the output projection as
+ *    w_o [1280, 1280] = W_o^T. A math-layout matrix must be transposed once
+ *    at load time. The two layouts have the same element count, so passing
+ *    the untransposed matrix is not detected and gives wrong results.
  *  - Arithmetic: fp16 operands, fp32 accumulation and fp32 softmax, fp16
  *    results rounded to nearest even. The score scale is 1/sqrt(64) = 1/8.
  *  - Calls on different streams may run concurrently when their output and

@@ -10,17 +10,18 @@ of intermediates and no blocking, fusion or reordering.
 What it computes, and the passages it follows:
 
 * Packed QKV projection, then attention, then the output projection:
-  "audio.cpp PR #1223, Add Edda ASR" — PR description ("it packs QKV and uses
-  flash attention over F16 K/V") and the encoder commit message (the shared
-  encoder materializes F32 scores for all 1500 frames; packing QKV and flash
-  attention give the same transcripts faster). Flash attention is an exact
+  "audio.cpp PR #1223, Add Edda ASR" — PR description (the encoder projects
+  Q, K and V in one packed GEMM and runs flash attention with fp16 keys and
+  values) and the encoder commit message (the shared encoder materializes F32
+  scores for all 1500 frames; packing QKV and flash attention give the same
+  transcripts faster). Flash attention is an exact
   reordering of softmax attention, so the oracle is softmax attention written
   out: full score matrix, masked softmax, P·V, output projection. The attention
   call taking the output projection and the score scale together follows the
   llama.cpp DSpark diff, src/models/dflash.cpp ("cache-aware, non-causal
   attention" hunk).
 * Bidirectional encoder (no causal mask): "BuzzASR/danish discussion #1",
-  first reply ("Whisper's encoder is also fully bidirectional").
+  first reply (every encoder position attends to every other one).
 * Chunk-local attention: "higgs-audio-v3-stt-GGUF" model card, "Architecture
   note (chunked encoder)": 4 s chunks encoded independently with within-chunk
   attention; a valid frame must not attend to padding.
