@@ -170,6 +170,27 @@ edda_status edda_verify_attn(const void* q, int32_t n_q, const void* k, const vo
                              const uint32_t* mask_rows, void* o, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/*
+ * edda_verify_attn without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It allocates nothing (no hipMalloc, hipFree or allocating library call); the
+ * split results of caches above 512 keys go to a static device array of
+ * EDDA_NOALLOC_SCRATCH_BYTES bytes inside the library (one copy per GPU, held until the
+ * process ends), whose device address is looked up on the first call on each device; that
+ * first call also clears the array's arrival counters with a kernel on its stream, and every
+ * call leaves them zero again.
+ *  Arguments and result as for edda_verify_attn; n_kv at most EDDA_NOALLOC_MAX_KV.
+ *  Every call on one GPU shares that GPU's array: calls that overlap on one GPU (different
+ *  streams, or graphs replayed concurrently) race and give wrong results; order them. The first
+ *  call on a device must also complete or be ordered before calls on other streams.
+ * Errors: as edda_verify_attn; EDDA_ERR_UNSUPPORTED for n_kv > EDDA_NOALLOC_MAX_KV;
+ * EDDA_ERR_HIP if the array's address cannot be obtained.
+ */
+#define EDDA_NOALLOC_MAX_KV 8192
+#define EDDA_NOALLOC_SCRATCH_BYTES (EDDA_VERIFY_COUNTER_BYTES + 64 * 16 * 20 * 66 * 4)
+edda_status edda_verify_attn_noalloc(const void* q, int32_t n_q, const void* k, const void* v, int32_t n_kv,
+                                     const uint32_t* mask_rows, void* o, void* stream);
+
 /* Bytes of workspace edda_verify_attn needs: 0 for caches of at most 512 keys (one workgroup
  * per head) or an invalid shape; longer caches split the keys into 128-key ranges, one
  * workgroup each, whose fp32 partial results the last workgroup of each head to finish merges

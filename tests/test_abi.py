@@ -368,3 +368,27 @@ def test_weight_structs_match_the_c_layout(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for field, _ in py._fields_:
             assert got[(cname, field)] == getattr(py, field).offset, (cname, field)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 16, A, A, 100, None, B, None), INVALID),
+    ((A, 0, A, A, 100, None, B, None), INVALID),
+    ((A, 17, A, A, 100, None, B, None), INVALID),
+    ((A, 16, A, A, 0, None, B, None), INVALID),
+    ((A, 16, A, A, 8193, None, B, None), UNSUPPORTED),   # beyond the static scratch
+    ((A, 16, A, A, 1 << 30, None, B, None), UNSUPPORTED),
+    ((ODD, 16, A, A, 100, None, B, None), MISALIGNED),
+    ((A, 16, A, A, 100, A + 1, B, None), MISALIGNED),
+])
+def test_verify_noalloc_rejects(lib, args, status):
+    assert lib.edda_verify_attn_noalloc(*args) == status
+    if status == UNSUPPORTED:
+        assert b"8192" in lib.edda_last_error()
+
+
+def test_noalloc_limits_match_header():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (EDDA_\w+) (\d+)", text))
+    assert int(consts["EDDA_NOALLOC_MAX_KV"]) == _lib.NOALLOC_MAX_KV
+    # The scratch holds the counters and the partials of 16 queries x 20 heads x 64 splits.
+    assert _lib.load().edda_verify_workspace_bytes(16, _lib.NOALLOC_MAX_KV) == 16384 + 64 * 16 * 20 * 66 * 4

@@ -21,6 +21,7 @@ N_HEADS = 20
 HEAD_DIM = 64
 QKV_COLS = 3 * D_MODEL
 MAX_VERIFY_QUERIES = 16
+NOALLOC_MAX_KV = 8192  # most keys edda_verify_attn_noalloc takes (its static scratch)
 VERIFY_COUNTER_BYTES = 16384  # leading workspace bytes of edda_verify_attn: zero before first use
 
 STATUS = {0: "EDDA_OK", 1: "EDDA_ERR_INVALID_ARGUMENT", 2: "EDDA_ERR_UNSUPPORTED",
@@ -28,6 +29,7 @@ STATUS = {0: "EDDA_OK", 1: "EDDA_ERR_INVALID_ARGUMENT", 2: "EDDA_ERR_UNSUPPORTED
 
 # Every symbol include/edda.h declares.
 EXPORTS = ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_encoder_workspace_bytes", "edda_verify_attn",
+           "edda_verify_attn_noalloc",
            "edda_verify_workspace_bytes", "edda_linear", "edda_layer_norm", "edda_encoder_layer",
            "edda_encoder_layer_workspace_bytes", "edda_encoder_stem", "edda_encoder_stem_workspace_bytes",
            "edda_decoder_verify_layer", "edda_decoder_verify_workspace_bytes", "edda_cross_kv",
@@ -90,6 +92,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edda_encoder_workspace_bytes.argtypes = [i32, i32]
     lib.edda_encoder_workspace_bytes.restype = sz
     lib.edda_verify_attn.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.edda_verify_attn_noalloc.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp]
     lib.edda_verify_workspace_bytes.argtypes = [i32, i32]
     lib.edda_verify_workspace_bytes.restype = sz
     lib.edda_linear.argtypes = [vp, i64, i32, vp, i32, vp, i32, vp, i64, vp, vp]
@@ -115,7 +118,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.edda_verify_workspace_bytes_ex.restype = sz
     lib.edda_last_error.restype = ctypes.c_char_p
     lib.edda_version.restype = ctypes.c_char_p
-    for name in ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_verify_attn", "edda_linear",
+    for name in ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_verify_attn", "edda_verify_attn_noalloc",
+                 "edda_linear",
                  "edda_layer_norm", "edda_encoder_layer", "edda_encoder_stem", "edda_decoder_verify_layer",
                  "edda_cross_kv", "edda_verify_attn_ex", "edda_quantize_q8_0", "edda_linear_q8",
                  "edda_decoder_verify_layer_q8"):
@@ -266,6 +270,24 @@ def edda_verify_attn(q, k, v, mask_rows, o, workspace=None, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.edda_verify_attn(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, _ptr(mask_rows), _ptr(o),
                                 _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def edda_verify_attn_noalloc(q, k, v, mask_rows, o, stream=None):
+    """edda_verify_attn with the library's static scratch instead of a workspace (n_kv up to
+    NOALLOC_MAX_KV; calls on one GPU must not overlap)."""
+    lib = load()
+    torch = _require(q, "q")
+    n_q, n_kv = q.shape[0], k.shape[0]
+    _require(q, "q", (n_q, N_HEADS, HEAD_DIM), torch.float16)
+    _require(k, "k", (n_kv, N_HEADS, HEAD_DIM), torch.float16)
+    _require(v, "v", (n_kv, N_HEADS, HEAD_DIM), torch.float16)
+    _require(o, "o", (n_q, N_HEADS, HEAD_DIM), torch.float16)
+    if mask_rows is not None:
+        _require(mask_rows, "mask_rows", (n_q, (n_kv + 31) // 32))
+        if mask_rows.dtype not in (torch.int32, torch.uint32):
+            raise ValueError("mask_rows must hold 32-bit words")
+    _check(lib.edda_verify_attn_noalloc(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, _ptr(mask_rows), _ptr(o),
+                                        _stream(stream)))
 
 
 def edda_linear(x, w, bias, y, activation=ACT_NONE, residual=None, residual_rows=None, stream=None):

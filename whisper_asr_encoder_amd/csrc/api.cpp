@@ -6,6 +6,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/edda.h"
@@ -41,6 +42,43 @@ constexpr int64_t kMaxRows = (int64_t)1 << 31;
 
 // The GEMM's tile map handles fewer than 65536 tiles (128 rows by at least 64 columns).
 bool gemm_tiles_ok(int64_t rows, int64_t n) { return ((rows + 127) / 128) * (n / 64) < 65536; }
+
+// Scratch of edda_verify_attn_noalloc: the verification workspace (arrival counters, then the
+// fp32 partial results of the key splits) for up to EDDA_NOALLOC_MAX_KV keys, 16 queries and 20
+// heads, as a device array of this library (one copy per GPU, held until the process ends).
+// Host code never passes `scratch` itself to a kernel: its name is only a host-side stand-in;
+// the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocSplits = (EDDA_NOALLOC_MAX_KV + 127) / 128;
+constexpr size_t kNoAllocScratchBytes =
+    EDDA_VERIFY_COUNTER_BYTES + kNoAllocSplits * EDDA_MAX_VERIFY_QUERIES * EDDA_N_HEADS * (2 + EDDA_HEAD_DIM) * 4;
+static_assert(EDDA_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "scratch size in the public header");
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's `scratch`, looked up on the first call on the device; that
+// call also clears the arrival counters with a kernel on its stream (every later call leaves
+// them zero, as the verification kernels reset their counters).
+edda_status noalloc_scratch(const char* fn, hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(EDDA_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(EDDA_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(EDDA_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    e = edda::launch_zero_words(p, EDDA_VERIFY_COUNTER_BYTES / 4, stream);
+    if (e != hipSuccess) return fail(EDDA_ERR_HIP, "%s: clearing the counters: %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return EDDA_OK;
+}
 
 }  // namespace
 
@@ -120,6 +158,32 @@ edda_status edda_encoder_attn(const void* qkv, int32_t batch, int32_t seq_len, i
   if (e != hipSuccess) return from_hip(e, "edda_encoder_attn flash-attention launch");
   return from_hip(edda::launch_gemm_bias(workspace, w_o, b_o, y, (int)rows, EDDA_D_MODEL, EDDA_D_MODEL, s),
                   "edda_encoder_attn output-projection launch");
+}
+
+edda_status edda_verify_attn_noalloc(const void* q, int32_t n_q, const void* k, const void* v, int32_t n_kv,
+                                     const uint32_t* mask_rows, void* o, void* stream) {
+  const char* fn = "edda_verify_attn_noalloc";
+  if (!q || !k || !v || !o) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: q, k, v and o must be non-null", fn);
+  if (n_q < 1 || n_q > EDDA_MAX_VERIFY_QUERIES)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_q = %d outside [1, %d]", fn, n_q, EDDA_MAX_VERIFY_QUERIES);
+  if (n_kv < 1) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_kv = %d out of range", fn, n_kv);
+  if (n_kv > EDDA_NOALLOC_MAX_KV)
+    return fail(EDDA_ERR_UNSUPPORTED, "%s: n_kv = %d beyond the static scratch's limit of %d keys "
+                "(use edda_verify_attn with a workspace)", fn, n_kv, EDDA_NOALLOC_MAX_KV);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || (mask_rows && !aligned(mask_rows, 4)))
+    return fail(EDDA_ERR_MISALIGNED, "%s: q/k/v/o must be 16-byte and mask_rows 4-byte aligned", fn);
+  const size_t need = edda::verify_workspace_bytes(n_q, n_kv, EDDA_N_HEADS);
+  if (need > kNoAllocScratchBytes)
+    return fail(EDDA_ERR_UNSUPPORTED, "%s: %zu bytes of scratch needed, %zu held", fn, need, kNoAllocScratchBytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (need > 0) {
+    const edda_status st = noalloc_scratch(fn, s, &ws);
+    if (st != EDDA_OK) return st;
+  }
+  return from_hip(edda::launch_verify(q, EDDA_D_MODEL, n_q, k, v, n_kv, EDDA_N_HEADS,
+                                      mask_rows ? EDDA_MASK_ROWS : EDDA_MASK_NONE, mask_rows, nullptr, o, ws, s),
+                  "edda_verify_attn_noalloc launch");
 }
 
 size_t edda_verify_workspace_bytes(int32_t n_q, int32_t n_kv) {

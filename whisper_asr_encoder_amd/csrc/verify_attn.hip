@@ -341,7 +341,18 @@ __global__ __launch_bounds__(NW * kWave) void verify_kernel(
 
 namespace {
 constexpr int kOneWorkgroupKeys = 4 * kSplitKeys;  // up to 512 keys: one workgroup per head
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
 }  // namespace
+
+hipError_t launch_zero_words(void* p, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, static_cast<uint32_t*>(p), n);
+  return hipGetLastError();
+}
 
 int verify_num_splits(int n_kv) { return n_kv <= kOneWorkgroupKeys ? 1 : (n_kv + kSplitKeys - 1) / kSplitKeys; }
 
