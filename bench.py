@@ -432,7 +432,7 @@ def decoder_bench(args, torch):
     gbs = per_layer * layers / (ms * 1e-3) / 1e9
     flops = layers * (gemm_flops(n_q, QKV, D) + 2 * gemm_flops(n_q, D, D) + gemm_flops(n_q, D, D)
                       + 2 * gemm_flops(n_q, I.D_FF, D) + attn_flops(n_q * L) + attn_flops(n_q * I.FRAMES_PER_WINDOW))
-    return {
+    res = {
         "metric": ("decoder verification pass (32 decoder layers, 16-token block"
                    + (", Q8_0 projection weights" if q8 else "") + ") on 1 MI355X"),
         "value": round(ms * 1e3, 2), "unit": "us per pass", "n_gpus": 1, "steps": args.steps,
@@ -447,6 +447,37 @@ def decoder_bench(args, torch):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_layer": per_layer, "traffic": None},
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decoder(weights, trial, L, n_q, slots, q8, dv, args.cpu_seconds)
+    return res
+
+
+def cpu_baseline_decoder(weights, trial, L, n_q, slots, q8, dv, budget_s):
+    """The oracle's decoder layers (fp64) on the same block, caches and cross K/V until the time
+    budget is used; microseconds per 32-layer pass, extrapolated."""
+    import oracle.decoder_layer as DL
+    import oracle.quant as Q
+    from whisper_asr_encoder_amd import inputs as I
+    threads = blas_threads()
+    x = I.decoder_block_input(trial)
+    enc = I.encoder_workload(1, layers=1).x
+    mask = I.causal_block_mask(n_q, L)
+    done, el = 0, 0.0
+    while done < len(weights) and (done == 0 or el < budget_s):
+        w = weights[done]
+        if q8:  # quantized once at load time on both sides: not timed
+            w = Q.DequantizedDecoderWeights(w, Q.quantize_decoder_weights(w))
+        c = I.verify_self_case(trial, done)
+        # Cross K/V are projected once per utterance on both sides: not timed.
+        ck, cv = DL.cross_kv(enc, weights[done].w_ck, weights[done].w_cv, weights[done].b_cv)
+        t0 = time.perf_counter()
+        DL.decoder_verify_layer(x, w, slots, c.k, c.v, L, mask, ck, cv)
+        el += time.perf_counter() - t0
+        done += 1
+    return {"value": round(el / done * len(weights) * 1e6, 1), "unit": "us per pass", "cores": threads,
+            "kind": "oracle", "sample": f"{done} of {len(weights)} decoder layers (cross K/V and Q8_0 weights "
+                                        f"prepared untimed, as on the GPU), fp64 NumPy, {el:.1f} s",
+            "cpu": cpu_model()}
 
 
 # ---------------------------------------------------------------------------
@@ -454,76 +485,142 @@ def decoder_bench(args, torch):
 # ---------------------------------------------------------------------------
 
 def verify_bench(args, torch):
+    """All 8 drawn cache lengths of the verification workload: per trial, 32 layers of causal
+    self-attention (16 queries over L_t slots) and cross-attention (16 queries over 1500 encoder
+    frames), and the beam variant (5 queries on the token tree of L_t slots)."""
     from whisper_asr_encoder_amd import inputs as I
     from whisper_asr_encoder_amd.encoder import VerifyAttention
 
-    trial = 0
-    layers = 32
+    layers, trials = 32, 8
     va = VerifyAttention(1500)
-    # Two copies of the pass's 32 layers of K/V (2 x 305 MB, more than twice the 256 MB
-    # Infinity Cache) are used in turn, so every pass reads its caches from HBM.
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    # Cross K/V: one set per layer (the encoder output of one utterance; drawn as trial 0's),
+    # reused by every trial. Two copies of every layer's K/V are used in turn (2 x 32 x 7.7 MB of
+    # cross K/V alone, more than the 256 MB Infinity Cache), so every pass reads HBM.
     copies = 2
-    sets = [[] for _ in range(copies)]
-    bytes_alg = 0
-    flops = 0
+    cross = [[] for _ in range(copies)]
+    cross_cases = []
     for l in range(layers):
-        s = I.verify_self_case(trial, l)
-        c = I.verify_cross_case(trial, l)
-        d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-        for copy in sets:
-            copy.append((d(s.q), d(s.k), d(s.v), va.mask_rows(s.mask), d(c.k), d(c.v)))
-        bytes_alg += (s.k.nbytes + s.v.nbytes + s.q.nbytes * 2 + s.mask.shape[0] * ((s.n_kv + 31) // 32) * 4)
-        bytes_alg += (c.k.nbytes + c.v.nbytes + c.q.nbytes * 2)
-        flops += attn_flops(int(s.mask.sum())) + attn_flops(16 * 1500)
-    o = torch.empty((16, H, DH), dtype=torch.float16, device="cuda")
-
-    def step():  # one pass over each copy
-        for copy in sets:
-            for q, k, v, m, ck, cv in copy:
-                va(q, k, v, m, o)
-                va(q, ck, cv, None, o)
-
-    for _ in range(args.warmup):
-        step()
+        c = I.verify_cross_case(0, l)
+        cross_cases.append(c)
+        for cp in cross:
+            cp.append((d(c.k), d(c.v)))
+    per_trial = []
+    tot = {"bytes": 0.0, "us": 0.0, "beam_bytes": 0.0, "beam_us": 0.0, "flops": 0.0}
     timer = Timer(torch)
-    # Each call is a few microseconds of GPU work, less than the Python binding takes to
-    # marshal it, so eager issue leaves the GPU idle between launches.  A decoder that
-    # verifies draft blocks replays its per-token launches from a HIP graph; the pass is
-    # timed that way (the graph holds each copy's 64 launches), and the eager rate is
-    # reported beside it.  Times are per pass.
-    eager_ms = timer(step, args.steps) / copies
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step()
-    torch.cuda.current_stream().wait_stream(side)
-    with torch.cuda.graph(graph):
-        step()
-    for _ in range(args.warmup):
-        graph.replay()
-    ms = timer(graph.replay, args.steps) / copies
-    L = I.cache_length(trial)
+    o = torch.empty((16, H, DH), dtype=torch.float16, device="cuda")
+    ob = torch.empty((I.BEAMS, H, DH), dtype=torch.float16, device="cuda")
+
+    def capture(step):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(max(1, args.warmup)):
+            g.replay()
+        return g
+
+    for t in range(trials):
+        L = I.cache_length(t)
+        sets = [[] for _ in range(copies)]
+        beams = [[] for _ in range(copies)]
+        b_self = b_cross = b_beam = 0
+        f = 0.0
+        for l in range(layers):
+            sc = I.verify_self_case(t, l)
+            tc = I.verify_tree_case(t, l)
+            cc = cross_cases[l]
+            for i in range(copies):
+                q = d(sc.q)  # the block's queries serve the self and the cross call
+                sets[i].append((q, d(sc.k), d(sc.v), va.mask_rows(sc.mask), q))
+                beams[i].append((d(tc.q), d(tc.k), d(tc.v), va.mask_rows(tc.mask)))
+            words = (L + 31) // 32
+            b_self += sc.k.nbytes + sc.v.nbytes + 2 * sc.q.nbytes + 16 * words * 4
+            b_cross += cc.k.nbytes + cc.v.nbytes + 2 * sc.q.nbytes
+            # Beam: K/V rows of the union of the five ancestor sets (the algorithmic bytes),
+            # queries, outputs and mask words.
+            used = int(tc.mask.any(axis=0).sum())
+            b_beam += used * H * DH * 2 * 2 + 2 * tc.q.nbytes + I.BEAMS * words * 4
+            f += attn_flops(int(sc.mask.sum())) + attn_flops(16 * 1500)
+
+        def step():
+            for i in range(copies):
+                for (q, k, v, m, qx), (ck, cv) in zip(sets[i], cross[i]):
+                    va(q, k, v, m, o)
+                    va(qx, ck, cv, None, o)
+
+        def beam_step():
+            for i in range(copies):
+                for q, k, v, m in beams[i]:
+                    va(q, k, v, m, ob)
+
+        g, gb = capture(step), capture(beam_step)
+        ms = timer(g.replay, args.steps) / copies
+        ms_b = timer(gb.replay, args.steps) / copies
+        per_trial.append({"L": L, "us_per_pass": round(ms * 1e3, 2), "us_per_call": round(ms * 1e3 / (2 * layers), 3),
+                          "gbs": round((b_self + b_cross) / (ms * 1e-3) / 1e9, 1),
+                          "beam_us_per_call": round(ms_b * 1e3 / layers, 3),
+                          "beam_gbs": round(b_beam / (ms_b * 1e-3) / 1e9, 1)})
+        tot["bytes"] += b_self + b_cross
+        tot["us"] += ms * 1e3
+        tot["beam_bytes"] += b_beam
+        tot["beam_us"] += ms_b * 1e3
+        tot["flops"] += f
+        del g, gb, sets, beams
+    gbs = tot["bytes"] / (tot["us"] * 1e-6) / 1e9
     dig = source_digest(["verify_attn.hip"])
     t_causal, t_cross = measured_traffic("verify_causal", dig), measured_traffic("verify_cross", dig)
     traffic = round((t_causal + t_cross) / 2) if t_causal and t_cross else None
-    return {
-        "metric": "verification attention pass (32 layers x causal self + cross attention) on 1 MI355X",
-        "value": round(bytes_alg / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+    res = {
+        "metric": "verification attention (8 drawn cache lengths x 32 layers x causal self + cross attention) "
+                  "on 1 MI355X, HBM GB/s of algorithmic bytes",
+        "value": round(gbs, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(tot["us"] / 1e3 / trials, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
-        "data": "synthetic", "us_per_call": round(ms * 1e3 / (2 * layers), 3),
-        "launch": "hip graph of the pass", "eager_ms_per_step": round(eager_ms, 4),
-        "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
-        "config": {"workload": f"speculative block verification: 16 queries, self cache L={L}, "
-                               f"cross 1500 encoder frames, 32 layers", "parallelism": "single GPU"},
+        "data": "synthetic", "us_per_call": round(tot["us"] / (trials * 2 * layers), 3),
+        "launch": "hip graph of each trial's pass (64 launches per copy of the K/V)",
+        "tflops": round(tot["flops"] / (tot["us"] * 1e-6) / 1e12, 3),
+        "per_trial": per_trial,
+        "beam": {"value": round(tot["beam_bytes"] / (tot["beam_us"] * 1e-6) / 1e9, 2), "unit": "GB/s",
+                 "us_per_call": round(tot["beam_us"] / (trials * layers), 3),
+                 "bytes": "K/V rows of the union of the 5 ancestor sets + queries, outputs, mask words"},
+        "config": {"workload": "speculative block verification: 16 queries, self caches L in "
+                               f"{sorted(p['L'] for p in per_trial)}, cross 1500 encoder frames, 32 layers; "
+                               "beam variant 5 queries on a token tree", "parallelism": "single GPU"},
         # Per launch on average (32 causal + 32 cross launches per pass); traffic is the
         # mean of the two kernels' measured HBM bytes per launch.
-        "roofline": {"bound": "hbm", "achieved": round(bytes_alg / (ms * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(bytes_alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                     "bytes_per_launch": round(bytes_alg / (2 * layers)), "traffic": traffic},
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "bytes_per_launch": round(tot["bytes"] / (trials * 2 * layers)), "traffic": traffic},
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_verify(cross_cases, args.cpu_seconds)
+    return res
+
+
+def cpu_baseline_verify(cross_cases, budget_s):
+    """The oracle on trial 0's layers (causal self-attention + cross-attention per layer) until
+    the time budget is used; GB/s of the same algorithmic bytes."""
+    import oracle
+    from whisper_asr_encoder_amd import inputs as I
+    threads = blas_threads()
+    done, nbytes, t0 = 0, 0, time.perf_counter()
+    while done < len(cross_cases) and (done == 0 or time.perf_counter() - t0 < budget_s):
+        sc = I.verify_self_case(0, done)
+        oracle.verify_attention(sc.q, sc.k, sc.v, sc.mask)
+        cc = cross_cases[done]
+        oracle.verify_attention(sc.q, cc.k, cc.v, None)
+        nbytes += sc.k.nbytes + sc.v.nbytes + cc.k.nbytes + cc.v.nbytes + 4 * sc.q.nbytes
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of 32 layers of trial 0 (causal self over L={I.cache_length(0)} + cross over 1500), "
+                      f"fp64 NumPy, {el:.1f} s", "us_per_call": round(el / (2 * done) * 1e6, 1), "cpu": cpu_model()}
 
 
 def main():

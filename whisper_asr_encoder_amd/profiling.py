@@ -6,7 +6,15 @@ passes (FETCH_SIZE, then WRITE_SIZE) write, and produces
 * per-kernel launch statistics (calls, mean / min / max duration),
 * HBM traffic per launch: the median counter value per dispatch (KiB) scaled by the
   factor that makes the same counter read the true byte count of a plain device copy
-  of known size in the same run (bench.py --calibrate-copy issues that copy).
+  of known size in the same run (bench.py --calibrate-copy issues that copy),
+* the median per dispatch of every counter in further --pmc runs, with derived figures:
+  MFMA utilisation (SQ_VALU_MFMA_BUSY_CYCLES is the busy cycles of the 1024 SIMDs summed,
+  one busy cycle per 1024 dense fp16 FLOP) against the nominal 2.4 GHz clock over the
+  trace's mean duration, and rocprof's own MfmaUtil formula; the share of L2 read / write
+  requests that go to DRAM (TCC_EA0_RDREQ_DRAM / TCC_EA0_RDREQ and the write pair) and the
+  DRAM bytes they imply,
+* beside the trace's mean, the per-launch time bench.py measured with HIP events in the
+  same traced run (--bench-json).
 
     python -m whisper_asr_encoder_amd.profiling TRACE_DIR FETCH_DIR WRITE_DIR OUT_DIR \
         --workload window|verify --command "<the rocprofv3 command lines>"
@@ -75,10 +83,45 @@ WORKLOADS = {
     }),
 }
 
-# Optional extra counter pass (one rocprofv3 --pmc run): median per dispatch.
-EXTRA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_F16",
-                  "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_VALU_TRANS_F32")
+# Optional extra counter passes (rocprofv3 --pmc runs): every counter they hold is reported as
+# its median per dispatch, and these combinations are derived when their counters are present.
 COPY_KERNEL = "copyBuffer"
+SIMDS = 1024            # 256 CUs x 4 SIMDs
+FLOP_PER_BUSY = 1024    # fp16 dense MFMA FLOP per busy cycle of one SIMD
+NOMINAL_GHZ = 2.4
+XCDS = 8
+
+
+def derived_lines(med, mean_ns):
+    """Figures derived from the median counter values `med` of one kernel (see module doc)."""
+    out = []
+    busy = med.get("SQ_VALU_MFMA_BUSY_CYCLES")
+    if busy is not None and mean_ns:
+        util = busy / (SIMDS * NOMINAL_GHZ * mean_ns)
+        out.append(("MFMA work executed (busy cycles x 1024 FLOP)", f"{busy * FLOP_PER_BUSY / 1e9:.3f} GFLOP"))
+        out.append(("MfmaUtil at the nominal 2.4 GHz over the trace's mean duration "
+                    "(busy / (1024 SIMDs x 2.4 GHz x duration))", f"{100 * util:.1f} %"))
+        gui = med.get("GRBM_GUI_ACTIVE")
+        if gui:
+            out.append(("rocprof's MfmaUtil formula, busy / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) "
+                        "(its counting window also holds the profiler's per-dispatch overhead)",
+                        f"{100 * busy / (gui / XCDS * SIMDS):.1f} %"))
+    rd, rq = med.get("TCC_EA0_RDREQ_DRAM"), med.get("TCC_EA0_RDREQ")
+    if rd is not None and rq:
+        n32, n128 = med.get("TCC_EA0_RDREQ_32B", 0.0), med.get("TCC_EA0_RDREQ_128B", 0.0)
+        n64 = max(rq - n32 - n128, 0.0)
+        avg = (32 * n32 + 64 * n64 + 128 * n128) / rq
+        out.append(("L2 read requests to DRAM / all L2-to-fabric read requests", f"{rd:.0f} / {rq:.0f} "
+                    f"({100 * rd / rq:.1f} %)"))
+        out.append(("DRAM read bytes (DRAM requests x mean request size)", f"{rd * avg / 1e6:.2f} MB "
+                    f"(mean request {avg:.0f} B)"))
+    wd, wq = med.get("TCC_EA0_WRREQ_DRAM"), med.get("TCC_EA0_WRREQ")
+    if wd is not None and wq:
+        n64 = med.get("TCC_EA0_WRREQ_64B", 0.0)
+        avg = (64 * n64 + 32 * max(wq - n64, 0.0)) / wq
+        out.append(("L2 write requests to DRAM / all", f"{wd:.0f} / {wq:.0f} ({100 * wd / wq:.1f} %)"))
+        out.append(("DRAM write bytes (DRAM requests x mean request size)", f"{wd * avg / 1e6:.2f} MB"))
+    return out
 
 
 def source_digest(names):
@@ -114,14 +157,31 @@ def counter_values(pmc_dir, counter):
     return vals
 
 
+def all_counters(pmc_dirs):
+    """{counter: {kernel: [values per dispatch]}} over every counter in the given runs."""
+    out = {}
+    for d in pmc_dirs or []:
+        with open(_one(os.path.join(d, "*counter_collection.csv"))) as f:
+            for row in csv.DictReader(f):
+                name = row["Counter_Name"].removesuffix("_sum")
+                out.setdefault(name, {}).setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
 def _match(values, fragment):
     hits = [v for k, v in values.items() if fragment in k]
     return [x for h in hits for x in h]
 
 
-def summarize(trace_dir, fetch_dir, write_dir, out_dir, command, workload="window", extra_dir=None):
+def summarize(trace_dir, fetch_dir, write_dir, out_dir, command, workload="window", extra_dirs=None,
+              bench_json=None):
     title, kernels = WORKLOADS[workload]
-    extra = {c: counter_values(extra_dir, c) for c in EXTRA_COUNTERS} if extra_dir else {}
+    extra = all_counters(extra_dirs)
+    bench = None
+    if bench_json:
+        with open(bench_json) as f:
+            lines = [ln for ln in f.read().splitlines() if ln.startswith("{")]
+        bench = json.loads(lines[-1]) if lines else None
     stats = kernel_stats(trace_dir)
     if fetch_dir is None:  # kernel trace only
         return trace_only(stats, kernels, title, out_dir, command, workload)
@@ -166,10 +226,19 @@ def summarize(trace_dir, fetch_dir, write_dir, out_dir, command, workload="windo
             f.write(f"| HBM bytes per launch (scaled) | {(fb + wb) / 1e6:.2f} MB "
                     f"(read {fb / 1e6:.2f}, write {wb / 1e6:.2f}) |\n")
             f.write(f"| kernel sources digest | {digest} |\n")
-            for c, vals in extra.items():
+            med = {}
+            for c, vals in sorted(extra.items()):
                 v = _match(vals, frag)
                 if v:
-                    f.write(f"| {c} median per dispatch | {statistics.median(v):.0f} |\n")
+                    med[c] = statistics.median(v)
+                    f.write(f"| {c} median per dispatch | {med[c]:.0f} |\n")
+            for label, value in derived_lines(med, s["avg_ns"]):
+                f.write(f"| {label} | {value} |\n")
+            k = (bench or {}).get("kernels", {}).get(key) or {}
+            if k.get("ms"):
+                f.write(f"| the same run's bench.py, HIP events around back-to-back launches | "
+                        f"{k['ms'] * 1e3:.2f} us per launch ({100 * (s['avg_ns'] / 1e3 / (k['ms'] * 1e3) - 1):+.1f} % "
+                        f"trace vs events) |\n")
     with open(tpath, "w") as f:
         json.dump(traffic, f, indent=1)
         f.write("\n")
@@ -204,12 +273,14 @@ def main():
     ap.add_argument("out_dir")
     ap.add_argument("--command", required=True)
     ap.add_argument("--workload", default="window", choices=sorted(WORKLOADS))
-    ap.add_argument("--extra-pmc", default=None, help="directory of a rocprofv3 --pmc run of EXTRA_COUNTERS")
+    ap.add_argument("--extra-pmc", action="append", default=[],
+                    help="directory of a further rocprofv3 --pmc run (repeatable)")
+    ap.add_argument("--bench-json", default=None, help="stdout of the traced bench.py run (its JSON line)")
     a = ap.parse_args()
     fetch = None if a.fetch_dir == "-" else a.fetch_dir
     write = None if a.write_dir == "-" else a.write_dir
-    print(json.dumps(summarize(a.trace_dir, fetch, write, a.out_dir, a.command, a.workload, a.extra_pmc),
-                     indent=1))
+    print(json.dumps(summarize(a.trace_dir, fetch, write, a.out_dir, a.command, a.workload, a.extra_pmc,
+                               a.bench_json), indent=1))
 
 
 if __name__ == "__main__":
