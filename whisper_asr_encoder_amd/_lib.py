@@ -14,7 +14,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libedda.so")
+# EDDA_LIBRARY names another build of the same library (e.g. the host-sanitizer build the ABI
+# tests run against); default: the in-tree libedda.so.
+LIB_PATH = os.environ.get("EDDA_LIBRARY") or os.path.join(HERE, "libedda.so")
 
 D_MODEL = 1280
 N_HEADS = 20
