@@ -38,6 +38,8 @@
 // ahead of the partner wave's softmax arithmetic on the same SIMD.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -179,6 +181,21 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
     for (int j = 0; j < kKT / 8; ++j) issue_part(it, j);
   };
   constexpr int IPW = kKT / 8;
+  // The same copy for a tile wholly inside [k_lo, k_hi) (every tile but the last), which
+  // needs no clamp: a wave-uniform 64-bit source base (tile, part j) plus a per-lane 32-bit
+  // offset that depends only on the lane and the parity of j (the row swizzle), so the copy
+  // costs no vector arithmetic.
+  const uint64_t dma_sbase = (uint64_t)(uintptr_t)(dma_base + (size_t)(k_lo + quarter * kKT) * kQkvCols);
+  uint32_t dma_voff[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    dma_voff[par] = (uint32_t)(drow * kQkvCols * 2 + 16 * ((lane & 7) ^ swz(8 * par + drow)));
+  auto issue_part_inside = [&](int it, int j) {
+    const uint32_t st = smem_addr + (it % kStages) * kStageB + quarter * 2 * kTileB + qg * kTileB + j * 1024;
+    const uint64_t src = dma_sbase + (uint64_t)(it * kIterKeys + 8 * j) * (kQkvCols * 2);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 ::"v"(dma_voff[j & 1]), "s"(src), "s"(st) : "m0");
+  };
 
   // Per-lane LDS offsets.
   int kfrag_off[4];
@@ -217,7 +234,12 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
   // scores come first so that they are complete before this wave's next softmax while the
   // PV products finish.  dma >= 0: also issue the four DMA instructions of tile dma, one
   // per MFMA pair, so the address unit never sees a burst.
-  auto phase = [&](int pv_it, int qk_it, bool last, int dma) {
+  // inside: tile dma lies wholly inside [k_lo, k_hi) (the unclamped copy form).
+  auto phase = [&](int pv_it, int qk_it, bool last, int dma, auto inside) {
+    auto dma_part = [&](int j) {
+      if constexpr (decltype(inside)::value) issue_part_inside(dma, j);
+      else issue_part(dma, j);
+    };
     __builtin_amdgcn_s_setprio(1);
     f16x8 vfr[2][2], kf[4];
     if (qk_it >= 0) {
@@ -244,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
 #pragma unroll
         for (int s = 1; s < 4; ++s) {
           sacc[qb] = mfma_32x32x16(kf[s], qf[qb][s], sacc[qb]);
-          if (pv_it < 0 && dma >= 0 && (s & 1)) issue_part(dma, 2 * qb + (s >> 1));
+          if (pv_it < 0 && dma >= 0 && (s & 1)) dma_part(2 * qb + (s >> 1));
         }
       }
     }
@@ -256,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
         for (int db = 0; db < 2; ++db) {
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) oacc[qb][db] = mfma_32x32x16(vfr[sg][db], pf[qb][sg], oacc[qb][db]);
-          if (dma >= 0) issue_part(dma, 2 * sg + db);
+          if (dma >= 0) dma_part(2 * sg + db);
         }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -398,62 +420,78 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
   };
 
   const int dma0 = n_iter > 2 ? 2 : -1;
+  using In = std::integral_constant<bool, true>;
+  using NoIn = std::integral_constant<bool, false>;
   if (qg == 0) {
     even_barrier(0);
     load_q();
-    phase(-1, 0, nl == 0, dma0);
+    phase(-1, 0, nl == 0, dma0, NoIn());
     odd_barrier();
     softmax(true);
     int i = 1;
-    for (; i + 2 < n_iter; ++i) {
+    for (; i + 3 < n_iter; ++i) {  // copies tile i + 2 <= n_iter - 2: inside the interval
       even_barrier(i);
-      phase(i - 1, i, false, i + 2);
+      phase(i - 1, i, false, i + 2, In());
       odd_barrier();
       softmax(false);
     }
+    if (i + 2 < n_iter) {  // copies the last tile
+      even_barrier(i);
+      phase(i - 1, i, false, i + 2, NoIn());
+      odd_barrier();
+      softmax(false);
+      ++i;
+    }
     if (i < nl) {
       even_barrier(i);
-      phase(i - 1, i, false, -1);
+      phase(i - 1, i, false, -1, NoIn());
       odd_barrier();
       softmax(false);
     }
     if (nl > 0) {
       even_barrier(nl);
-      phase(nl - 1, nl, true, -1);
+      phase(nl - 1, nl, true, -1, NoIn());
       odd_barrier();
       softmax(false);
     }
     even_barrier(n_iter);
-    phase(nl, -1, false, -1);
+    phase(nl, -1, false, -1, NoIn());
     odd_barrier();
   } else {
     even_barrier(0);
     load_q();
     odd_barrier();
-    phase(-1, 0, nl == 0, dma0);
+    phase(-1, 0, nl == 0, dma0, NoIn());
     even_barrier(1);
     softmax(true);
     int i = 1;
-    for (; i + 2 < n_iter; ++i) {
+    for (; i + 3 < n_iter; ++i) {
       odd_barrier();
-      phase(i - 1, i, false, i + 2);
+      phase(i - 1, i, false, i + 2, In());
       even_barrier(i + 1);
       softmax(false);
     }
+    if (i + 2 < n_iter) {
+      odd_barrier();
+      phase(i - 1, i, false, i + 2, NoIn());
+      even_barrier(i + 1);
+      softmax(false);
+      ++i;
+    }
     if (i < nl) {
       odd_barrier();
-      phase(i - 1, i, false, -1);
+      phase(i - 1, i, false, -1, NoIn());
       even_barrier(i + 1);
       softmax(false);
     }
     if (nl > 0) {
       odd_barrier();
-      phase(nl - 1, nl, true, -1);
+      phase(nl - 1, nl, true, -1, NoIn());
       even_barrier(nl + 1);
       softmax(false);
     }
     odd_barrier();
-    phase(nl, -1, false, -1);
+    phase(nl, -1, false, -1, NoIn());
   }
 
   // Merge the four key quarters of each query group in one LDS round (the ring is free:
