@@ -47,9 +47,10 @@ WORKLOADS = {
         "flash_attn_kernel": ("flash_attn", ["flash_attn.hip"]),
         "gemm_bias_kernelILi128ELi64E": ("out_gemm", ["gemm.hip"]),
     }),
-    "verify": ("block verification, 16 queries, 32 layers (causal self-attention over a "
-               "360-slot cache, cross-attention over 1500 frames)", {
-        # Mask mode 0 (mask rows: the causal self-attention), mode 1 (none: cross-attention).
+    "verify": ("block verification over the 8 drawn cache lengths (44-360 slots), 32 layers each: "
+               "16-query causal blocks and 5-beam token trees (mask rows), cross-attention over 1500 "
+               "frames (no mask)", {
+        # Mask mode 0 (mask rows: causal blocks and beam trees), mode 1 (none: cross-attention).
         "verify_kernelILi0E": ("verify_causal", ["verify_attn.hip"]),
         "verify_kernelILi1E": ("verify_cross", ["verify_attn.hip"]),
     }),
@@ -101,6 +102,14 @@ def derived_lines(med, mean_ns):
         out.append(("MFMA work executed (busy cycles x 1024 FLOP)", f"{busy * FLOP_PER_BUSY / 1e9:.3f} GFLOP"))
         out.append(("MfmaUtil at the nominal 2.4 GHz over the trace's mean duration "
                     "(busy / (1024 SIMDs x 2.4 GHz x duration))", f"{100 * util:.1f} %"))
+        cu_cycles, wgs = med.get("SQ_BUSY_CU_CYCLES"), med.get("_workgroups")
+        if cu_cycles and wgs:
+            cus = min(wgs, SIMDS // 4)  # one workgroup per CU at most for these kernels
+            per_cu = cu_cycles / cus
+            out.append(("shader clock under this load (SQ_BUSY_CU_CYCLES / busy CUs / duration)",
+                        f"{per_cu / mean_ns:.2f} GHz ({per_cu:.0f} cycles per busy CU)"))
+            out.append(("MfmaUtil at that clock over the busy CUs' SIMDs (busy / (4 x busy CUs x cycles))",
+                        f"{100 * busy / (4 * cus * per_cu):.1f} %"))
         gui = med.get("GRBM_GUI_ACTIVE")
         if gui:
             out.append(("rocprof's MfmaUtil formula, busy / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) "
@@ -165,6 +174,8 @@ def all_counters(pmc_dirs):
             for row in csv.DictReader(f):
                 name = row["Counter_Name"].removesuffix("_sum")
                 out.setdefault(name, {}).setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+                wgs = int(row["Grid_Size"]) // max(int(row["Workgroup_Size"]), 1)
+                out.setdefault("_workgroups", {}).setdefault(row["Kernel_Name"], []).append(float(wgs))
     return out
 
 
@@ -206,16 +217,22 @@ def summarize(trace_dir, fetch_dir, write_dir, out_dir, command, workload="windo
         fv, wv = _match(fetch, frag), _match(write, frag)
         if not st or not fv or not wv:
             continue
-        s = st[0]
+        # Every instantiation matching the fragment (e.g. the verification kernel's chunk and
+        # wave counts, chosen by cache length) counts: calls-weighted mean over them.
+        calls = sum(v["calls"] for v in st)
+        s = {"calls": calls, "avg_ns": sum(v["avg_ns"] * v["calls"] for v in st) / calls,
+             "min_ns": min(v["min_ns"] for v in st), "max_ns": max(v["max_ns"] for v in st)}
         fb = statistics.median(fv) * 1024.0 * f_scale
         wb = statistics.median(wv) * 1024.0 * w_scale
         digest = source_digest(srcs)
         traffic[key] = {"bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
                         "source_digest": digest}
-        name = [k for k in stats if frag in k][0]
+        names = [k for k in stats if frag in k]
         with open(os.path.join(out_dir, f"{key}_{workload}.md"), "w") as f:
             f.write(f"# {key}: {title}\n\n")
-            f.write(f"Kernel symbol: `{name}`\n\n")
+            f.write("Kernel symbol" + ("s" if len(names) > 1 else "") + ": " +
+                    ", ".join(f"`{n}` ({stats[n]['calls']} calls, {stats[n]['avg_ns'] / 1e3:.2f} us)" for n in names)
+                    + "\n\n")
             f.write("Commands (run from the repository root on one MI355X):\n\n```\n" + command.strip() + "\n```\n\n")
             f.write("| figure | value |\n|---|---|\n")
             f.write(f"| dispatches in the trace run | {s['calls']} |\n")
@@ -231,7 +248,8 @@ def summarize(trace_dir, fetch_dir, write_dir, out_dir, command, workload="windo
                 v = _match(vals, frag)
                 if v:
                     med[c] = statistics.median(v)
-                    f.write(f"| {c} median per dispatch | {med[c]:.0f} |\n")
+                    if not c.startswith("_"):
+                        f.write(f"| {c} median per dispatch | {med[c]:.0f} |\n")
             for label, value in derived_lines(med, s["avg_ns"]):
                 f.write(f"| {label} | {value} |\n")
             k = (bench or {}).get("kernels", {}).get(key) or {}
