@@ -98,10 +98,10 @@ def test_cross_kv(torch):
     check(host(dv.cross_v[0]), v, "cross V")
 
 
-def run_layer(torch, layer, trial, kind, n_kv=None, in_place=False, frames=1500):
+def run_layer(torch, layer, trial, kind, n_kv=None, in_place=False, frames=1500, no_mask=False):
     """One decoder layer on GPU and oracle; kind = 'causal' (chain of 16), 'tree' (5 beams) or
     'single' (one token: a plain decoding step); `frames` rows of the encoder output feed the
-    cross-attention."""
+    cross-attention; no_mask: the self-attention admits every slot (mask_rows NULL)."""
     from whisper_asr_encoder_amd.encoder import DecoderVerifier
     w = I.decoder_layer_weights(layer)
     if kind == "single":
@@ -134,7 +134,7 @@ def run_layer(torch, layer, trial, kind, n_kv=None, in_place=False, frames=1500)
     k_d, v_d = dev(torch, kc), dev(torch, vc)
     xd = dev(torch, x)
     y = xd if in_place else torch.full((n_q, 1280), float("nan"), dtype=torch.float16, device="cuda")
-    mask = case.mask
+    mask = None if no_mask else case.mask
     dv.layer(xd, 0, slots, k_d, v_d, nk, None if mask is None else VerifyRows(torch, mask), y)
     torch.cuda.synchronize()
     ref = DL.decoder_verify_layer(x, w, slots, kc, vc, nk, mask, ck16, cv16)
@@ -167,6 +167,70 @@ def test_decoder_layer_short_encoder_output(torch, frames):
     y, kd, _, ref, _, _, slots = run_layer(torch, 7, 5, "causal", frames=frames)
     check(y, ref["y"], "y")
     check(kd[slots], ref["k_cache"][slots], "appended K rows")
+
+
+@pytest.mark.parametrize("n_kv,kind,no_mask", [(256, "causal", False), (257, "tree", False), (512, "causal", False),
+                                              (300, "causal", True), (40, "single", False), (513, "causal", False),
+                                              (700, "tree", False)])
+def test_decoder_layer_cache_lengths(torch, n_kv, kind, no_mask):
+    """Caches at the chunk boundaries of the single-launch layer's self-attention (one 32-key
+    chunk per wave up to 256 keys, two up to 512), an unmasked self-attention, and caches
+    beyond 512 keys, which take the eight-launch form of the layer."""
+    say(f"decoder layer: n_kv {n_kv} {kind}{' no mask' if no_mask else ''}")
+    y, kd, vd, ref, kc, vc, slots = run_layer(torch, 11, 2, kind, n_kv=n_kv, no_mask=no_mask)
+    check(y, ref["y"], "y")
+    others = np.setdiff1d(np.arange(kc.shape[0]), slots)
+    assert np.array_equal(kd[others], kc[others].astype(np.float32)), "cache rows outside the block changed"
+    check(kd[slots], ref["k_cache"][slots], "appended K rows")
+    check(vd[slots], ref["v_cache"][slots], "appended V rows")
+
+
+def test_decoder_layer_repeatable_and_graph_replay(torch):
+    """The layer's result does not depend on which workgroup takes which work item: two eager
+    calls on fresh copies of the caches, and three replays of a captured graph (with eager work
+    between them), all bit-identical; the counters are zero after each."""
+    from whisper_asr_encoder_amd.encoder import DecoderVerifier
+    say("decoder layer: repeat and graph replay")
+    w = I.decoder_layer_weights(6)
+    case = I.verify_tree_case(3, 6)
+    n_q, nk = case.q.shape[0], case.n_kv
+    slots = [int(s) for s in case.query_slots]
+    cap = nk + 4
+    kc = np.zeros((cap, 20, 64), dtype=np.float16)
+    vc = np.zeros((cap, 20, 64), dtype=np.float16)
+    kc[:nk], vc[:nk] = case.k, case.v
+    dv = DecoderVerifier([w], max_kv=cap)
+    dv.set_encoder_output(dev(torch, I.encoder_workload(1, layers=1).x))
+    x = dev(torch, I.decoder_block_input(3, n_q))
+    mask = VerifyRows(torch, case.mask)
+    outs = []
+    for _ in range(2):
+        k_d, v_d = dev(torch, kc), dev(torch, vc)
+        y = torch.full((n_q, 1280), float("nan"), dtype=torch.float16, device="cuda")
+        dv.layer(x, 0, slots, k_d, v_d, nk, mask, y)
+        torch.cuda.synchronize()
+        assert not dv.workspace[:_lib.VERIFY_COUNTER_BYTES].any().item(), "counters not returned to zero"
+        outs.append((y.clone(), k_d.clone(), v_d.clone()))
+    assert all(torch.equal(a, b) for a, b in zip(*outs)), "two eager calls differ"
+    k_g, v_g = dev(torch, kc), dev(torch, vc)
+    y_g = torch.full((n_q, 1280), float("nan"), dtype=torch.float16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dv.layer(x, 0, slots, k_g, v_g, nk, mask, y_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dv.layer(x, 0, slots, k_g, v_g, nk, mask, y_g)
+    for i in range(3):
+        y_g.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, outs[0][0]), f"graph replay {i} differs from the eager result"
+        assert torch.equal(k_g, outs[0][1]) and torch.equal(v_g, outs[0][2]), f"replay {i}: caches differ"
+        assert not dv.workspace[:_lib.VERIFY_COUNTER_BYTES].any().item(), "counters not returned to zero"
+        torch.mul(x, 1.0)  # eager work between replays
 
 
 def test_decoder_layer_short_cache_in_place(torch):

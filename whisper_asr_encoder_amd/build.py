@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libedda.so")
-SOURCES = ["api.cpp", "gemm.hip", "flash_attn.hip", "verify_attn.hip", "norm_im2col.hip", "skinny.hip"]
+SOURCES = ["api.cpp", "gemm.hip", "flash_attn.hip", "verify_attn.hip", "norm_im2col.hip", "skinny.hip", "decoder_fused.hip"]
 ARCH = "gfx950"
 
 COMMON = [

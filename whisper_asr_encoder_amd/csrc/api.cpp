@@ -382,6 +382,15 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 constexpr size_t kSplitCounterOffset = (size_t)EDDA_N_HEADS * 256;
 static_assert(kSplitCounterOffset + (EDDA_D_MODEL / 16) * 64 <= EDDA_VERIFY_COUNTER_BYTES,
               "split-K counters must fit in the counter region");
+// The single-launch layer's ticket and exit counters, then one done flag per work item: the
+// region's last free lines.
+constexpr size_t kFusedCtlOffset = 12288;
+constexpr size_t kFusedFlagOffset = kFusedCtlOffset + 2 * 256;
+static_assert(kSplitCounterOffset + (EDDA_D_MODEL / 16) * 64 <= kFusedCtlOffset &&
+                  kFusedFlagOffset + edda::kDecoderFusedMaxItems * 4 <= EDDA_VERIFY_COUNTER_BYTES,
+              "fused-layer counters and flags must fit in the counter region");
+// Persistent workgroups of the single-launch layer: one per compute unit of an MI355X.
+constexpr int kFusedWorkgroups = 256;
 
 struct DecoderWs {
   size_t verify, h, qkv, o, x1, x2, f, total;
@@ -396,16 +405,20 @@ DecoderWs decoder_ws(int32_t n_q, int32_t n_kv, int32_t n_frames) {
   // lines the 20-head verification leaves unused.
   const size_t v3 = EDDA_VERIFY_COUNTER_BYTES + std::max(edda::skinny_split_part_bytes(EDDA_D_MODEL, EDDA_D_MODEL),
                                                          edda::skinny_split_part_bytes(EDDA_D_MODEL, EDDA_D_FF));
-  size_t off = align256(std::max(std::max(v1, v2), v3));
+  const size_t v4 = EDDA_VERIFY_COUNTER_BYTES + edda::decoder_fused_part_bytes(n_q, n_frames);
+  size_t off = align256(std::max(std::max(v1, v2), std::max(v3, v4)));
   w.verify = 0;
   const size_t row = (size_t)n_q * 2;
+  // h, o and f hold 16 rows whatever n_q: the single-launch layer keeps them in MFMA fragment
+  // order, which spans all 16 rows of the block GEMMs' operand.
+  const size_t row16 = (size_t)EDDA_MAX_VERIFY_QUERIES * 2;
   w.h = off;
-  w.qkv = w.h + align256(row * EDDA_D_MODEL);
+  w.qkv = w.h + align256(row16 * EDDA_D_MODEL);
   w.o = w.qkv + align256(row * EDDA_QKV_COLS);
-  w.x1 = w.o + align256(row * EDDA_D_MODEL);
+  w.x1 = w.o + align256(row16 * EDDA_D_MODEL);
   w.x2 = w.x1 + align256(row * EDDA_D_MODEL);
   w.f = w.x2 + align256(row * EDDA_D_MODEL);
-  w.total = w.f + align256(row * EDDA_D_FF);
+  w.total = w.f + align256(row16 * EDDA_D_FF);
   return w;
 }
 }  // namespace
@@ -492,6 +505,21 @@ edda_status decoder_layer(const char* fn, const void* x, int32_t n_q, const int3
     char msg[96];                         \
     snprintf(msg, sizeof msg, "%s " what " launch", fn); \
     return from_hip(e, msg);              \
+  }
+  if (!q8 && edda::decoder_fused_supported(n_q, n_kv, n_frames)) {
+    // One launch: the eight steps below as work items of persistent workgroups.
+    edda::DecoderFusedParams p{};
+    p.x = x, p.y = y, p.n_q = n_q, p.slots = sl, p.k_cache = k_cache, p.v_cache = v_cache, p.n_kv = n_kv;
+    p.mask = mask_rows, p.cross_k = cross_k, p.cross_v = cross_v, p.n_frames = n_frames;
+    const void* w[18] = {wt->ln1_gamma, wt->ln1_beta, wt->qkv.w,       wt->b_qkv,      wt->o.w,        wt->b_o,
+                         wt->ln2_gamma, wt->ln2_beta, wt->q_cross.w,   wt->b_q_cross,  wt->o_cross.w,  wt->b_o_cross,
+                         wt->ln3_gamma, wt->ln3_beta, wt->fc1.w,       wt->b_fc1,      wt->fc2.w,      wt->b_fc2};
+    for (int i = 0; i < 18; ++i) p.w[i] = w[i];
+    p.qkv = qkv, p.o = o, p.x1 = x1, p.qc = o, p.h = h, p.x2 = x2, p.f = f;
+    p.verify_counters = ws, p.ctl = ws + kFusedCtlOffset, p.flags = ws + kFusedFlagOffset, p.part = sk_part;
+    p.workgroups = kFusedWorkgroups;
+    EDDA_STEP(edda::launch_decoder_layer_fused(p, s), "single-launch layer");
+    return ok();
   }
   // Eight launches: LayerNorms run inside the block GEMMs that consume them, and the QKV
   // epilogue writes the block's K and V rows into their cache slots.

@@ -1,0 +1,522 @@
+// Kernel 8: the decoder's verification layer in one launch.
+//
+// The layer is eight dependent steps, each a few microseconds of latency-bound work on a
+// 16-token block (LN1 + QKV + cache append, self-attention, output projection + residual,
+// LN2 + cross query, cross-attention, cross output projection + residual, LN3 + fc1 + GELU,
+// fc2 + residual).  Run as eight launches, every step pays a launch, a cold start and its
+// weights' first round trip after the previous step ended.  Here one launch of persistent
+// workgroups takes work items from a single atomic ticket counter, items numbered step by
+// step; an item of step p first issues the loads that depend on nothing computed in this
+// launch (its weight fragments into registers, the old K/V cache rows, the cross-attention
+// K/V), then waits until every item of step p - 1 has counted itself done, then loads its
+// activations and finishes.  Workgroups run ahead of the step being computed, so the next
+// steps' weights stream in while the current step runs.
+//
+// Deadlock freedom without co-residency: tickets are handed out in increasing order and an
+// item waits only for items of earlier steps, which hold lower tickets and so were all claimed
+// by workgroups that are running and that themselves wait only on earlier steps.  The waits
+// are bounded (a launch always ends).  Each item, once its stores are acknowledged, sets its
+// own done flag (a store; atomics on one line serialise at the memory side, ~12 ns each, and
+// polls of that line queue with them); an item's wait reads the flags of the step before.
+// The last workgroup to leave clears the ticket, the exit count and the flags, which the
+// launch leaves zero as it found them.
+//
+// Memory ordering across the XCDs' separate L2 caches: everything one step writes and a
+// later step reads (activations, appended cache rows) is stored with agent-scope atomic
+// stores, which write through to the device's coherence point; an item's stores are
+// acknowledged (vmcnt 0) before its workgroup barrier and its done flag.  A waiting item,
+// once it has seen the flags, reads such data with device-coherent loads (the sc1 cache
+// policy, 16 bytes a lane through buffer loads).  Loads issued before the wait (weights, old
+// cache rows, cross-attention K/V, the layer input) touch nothing this launch writes and are
+// plain.  (Measured and dropped: one agent-scope acquire fence per item and plain loads
+// after it; each fence invalidates the whole XCD's L2 under the other workgroups on it, and
+// the layer ran 55 % slower.  A release fence's L2 write-back costs 4-14 us, hence the
+// write-through stores.)
+//
+// Work items (the block GEMMs as kernel 6: weights as the MFMA A operand, 8 waves over the
+// 32-deep K steps, summed in LDS; a LayerNorm is computed once per item):
+//   0  LN1 + QKV + K/V cache append, 32 columns          120 items, x from the layer input
+//   1  self-attention, one item per head (<= 512 keys)   20
+//   2  output projection + residual x, 16 columns        80
+//   3  LN2 + cross query, 16 columns                     80
+//   4  cross-attention, 256-key splits x 20 heads        20 * ceil(n_frames / 256)
+//   5  cross output projection + residual x1             80
+//   6  LN3 + fc1 + GELU, 64 columns                      80
+//   7  fc2 (K = 5120) + residual x2, 16 columns          80
+#include <math.h>
+
+#include <type_traits>
+
+#include "device.hpp"
+#include "kernels.hpp"
+#include "layer_norm_row.hpp"
+#include "verify_core.hpp"
+
+namespace edda {
+namespace {
+
+constexpr int kFWaves = 8;
+constexpr int kFThreads = kFWaves * kWave;
+constexpr int kFCols = 16;
+constexpr int kFLnGroups = kDModel / 256;
+constexpr int kFALd = kDModel + 8;  // LDS row stride (halves) of the normalised rows
+constexpr int kSteps = 8;
+constexpr int kCtlStride = 64;  // uint32 words: the two counters 256 bytes apart
+constexpr int kSpinLimit = 1 << 20;  // polls (seconds) before a wait gives up
+constexpr int kCoarseSleep = 127;    // s_sleep units of 64 clocks between polls
+constexpr int kFineSleep = 16;
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Device-coherent loads (sc1 cache policy) at a byte offset from a wave-uniform base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+constexpr int kSc1 = 16;  // cache-policy operand of the buffer-load builtins: sc1
+__device__ __forceinline__ f16x8 load16c(const f16* base, uint32_t elem) {
+  return __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(coherent_rsrc(base), 2 * elem, 0, kSc1));
+}
+__device__ __forceinline__ f16x4 load8c(const f16* base, uint32_t elem) {
+  return __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(coherent_rsrc(base), 2 * elem, 0, kSc1));
+}
+__device__ __forceinline__ f16x2 load4c(const f16* base, uint32_t elem) {
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_raw_buffer_load_b32(coherent_rsrc(base), 2 * elem, 0, kSc1));
+}
+__device__ __forceinline__ uint32_t ld32c(const void* p) {
+  return __hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st64c(void* p, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st32c(void* p, uint32_t v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float gelu_exact_f(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+
+// The wait of an item of step p: wave 0 reads done flags (64 per load instruction, at most
+// kMaxPollLoads per lane) until all are set (bounded), then the workgroup proceeds.  First,
+// rarely, those of step p - 2 (an item claimed well ahead of its turn), then more often those
+// of step p - 1: every poll is a device-coherent load that competes with the weight and
+// activation traffic, and measured on the layer, polling less often (up to ~0.7 us between
+// polls) ran faster than polling more often or keeping two polls in flight.  Reads only: a
+// flag line is never the target of atomics, which the memory side would serialise.
+constexpr int kMaxPollLoads = 4;  // flags of up to 256 items per step
+template <int kSleep>
+__device__ __forceinline__ void poll_flags(const uint32_t* flags, int begin, int end) {
+  const int lane = threadIdx.x;
+  for (int i = 0; i < kSpinLimit; ++i) {
+    bool set = true;
+#pragma unroll
+    for (int k = 0; k < kMaxPollLoads; ++k) {
+      // Unconditional loads (indices past the step clamped to its first flag, their values
+      // ignored): one wait for all of them.
+      const int j = begin + lane + kWave * k;
+      set &= ld32c(&flags[j < end ? j : begin]) != 0u || j >= end;
+    }
+    if (__all(set)) return;
+    __builtin_amdgcn_s_sleep(kSleep);
+  }
+}
+struct StepWait {
+  const uint32_t* flags;  // null: no wait (step 0)
+  int coarse_begin, coarse_end;  // flag indices of step p - 2 (empty for p < 2)
+  int begin, end;                // flag indices of step p - 1
+  __device__ void operator()() const {
+    if (flags && threadIdx.x < kWave) {
+      if (coarse_end > coarse_begin) poll_flags<kCoarseSleep>(flags, coarse_begin, coarse_end);
+      poll_flags<kFineSleep>(flags, begin, end);
+    }
+    __syncthreads();
+  }
+};
+
+// Every thread's stores acknowledged, then the item's done flag.
+__device__ __forceinline__ void publish(uint32_t* flag) {
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (threadIdx.x == 0) st32c(flag, 1u);
+}
+
+struct FusedArgs {
+  const f16* x;
+  f16* y;
+  int n_q;
+  Slots slots;
+  f16* k_cache;
+  f16* v_cache;
+  int n_kv;
+  const uint32_t* mask;
+  int mask_words;
+  const f16* cross_k;
+  const f16* cross_v;
+  int n_frames;
+  int cross_splits;
+  // weights ([out][in] fp16) and LayerNorm parameters; biases may be null
+  const f16 *ln1_g, *ln1_b, *w_qkv, *b_qkv, *w_o, *b_o;
+  const f16 *ln2_g, *ln2_b, *w_qc, *b_qc, *w_oc, *b_oc;
+  const f16 *ln3_g, *ln3_b, *w_fc1, *b_fc1, *w_fc2, *b_fc2;
+  // workspace
+  f16 *qkv, *o, *x1, *qc, *h, *x2, *f;
+  uint32_t* verify_counters;
+  float* part_ml;
+  float* part_o;
+  uint32_t* ctl;  // ticket at ctl[0], exit count at ctl[kCtlStride]
+  uint32_t* flags;  // one done flag per item
+  int step_end[kSteps];  // running item totals
+};
+
+// The operands of one block GEMM: C[M, N] = act(A W^T + bias) + residual.
+struct GemmOp {
+  const f16* w;  // [N][K]
+  const f16* bias;
+  const f16* a;  // [M][K] operand rows, or the LayerNorm's input rows
+  const f16* gamma;
+  const f16* beta;
+  const f16* res;  // [M][N] or null
+  f16* c;          // [M][N]
+  int N, K;
+};
+
+constexpr int kMaxBlocks = 4;  // column blocks of one GEMM item
+struct GemmSmem {
+  float red[kFWaves][kMaxBlocks * kFCols][kFCols + 1];
+  alignas(16) f16 a_lds[16 * kFALd];
+};
+
+// One block-GEMM item: NB column blocks of 16 (C[:, n0 .. n0 + 16 NB)) over the whole K = 256 NU
+// (wave w takes the 32-deep steps w, w + 8, ...).  A_FRESH / RES_FRESH: the operand rows / the
+// residual were written in this launch (coherent loads after the wait).  A_FRAG / C_FRAG: A is
+// read, C written, in fragment order (C_FRAG: no residual, no append).  Per block the arithmetic is kernel 6's (same fragments,
+// same summation order over steps and waves).
+template <int kGroups>
+__device__ __forceinline__ LnRow<kGroups> layer_norm_load_coherent(const f16* x, uint32_t row0,
+                                                                   const f16* __restrict__ gamma,
+                                                                   const f16* __restrict__ beta, int lane) {
+  LnRow<kGroups> r;
+#pragma unroll
+  for (int c = 0; c < kGroups; ++c) {
+    const int f = 4 * (c * kWave + lane);
+    r.v[c] = load8c(x, row0 + f);
+    r.g[c] = *reinterpret_cast<const f16x4*>(gamma + f);
+    r.b[c] = *reinterpret_cast<const f16x4*>(beta + f);
+  }
+  return r;
+}
+
+// Fragment order of a [16][K] operand consumed by the block GEMMs: for each 32-deep step s, the
+// 64 lanes' 16-byte fragments in lane order (lane 16 g + r holds row r, k = 32 s + 8 g ..
+// 8 g + 7), so a consumer's load instruction reads 1 KB contiguous (row-major rows give 16
+// separate 64-byte pieces per instruction).  Element (m, k) sits at frag_index(m, k).
+__device__ __forceinline__ uint32_t frag_index(int m, int k) {
+  return (uint32_t)((((k >> 5) * 4 + ((k >> 3) & 3)) * 16 + m) * 8 + (k & 7));
+}
+
+template <int NB, int NU, int ACT, bool LN, bool A_FRESH, bool A_FRAG, bool RES_FRESH, bool APPEND, bool C_FRAG>
+__device__ __forceinline__ void gemm_item(const FusedArgs& fa, const GemmOp& op, int item, const StepWait& wait,
+                                          GemmSmem& sm, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int M = fa.n_q, K = op.K, N = op.N;
+  const int n0 = item * NB * kFCols;
+  // LayerNorm rows wave and wave + 8 that exist before the launch: loaded ahead of the weights
+  // (a wave's loads return in order, so rows queued behind 80 KB of weights would wait for them).
+  const int r0 = wave, r1 = wave + kFWaves;
+  LnRow<kFLnGroups> row0, row1;
+  if constexpr (LN && !A_FRESH) {
+    row0 = layer_norm_load<kFLnGroups>(op.a + (size_t)min(r0, M - 1) * kDModel, op.gamma, op.beta, lane);
+    row1 = layer_norm_load<kFLnGroups>(op.a + (size_t)min(r1, M - 1) * kDModel, op.gamma, op.beta, lane);
+  }
+  // Weight fragments: row n0 + 16 b + r16, 8 consecutive k of each step.
+  f16x8 wf[NB][NU];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const f16* wrow = op.w + (size_t)(n0 + kFCols * b + r16) * K + 8 * g;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) wf[b][u] = load16(wrow + 32 * (wave + 8 * u));
+  }
+  // Epilogue thread: block eb, row em, columns en, en + 1 of the block.
+  const int eb = tid >> 7, em = (tid >> 3) & 15, en = 2 * (tid & 7);
+  const int ecol = n0 + kFCols * eb + en;
+  const bool epi = tid < NB * 128 && em < M;
+  f16x2 bias2 = {};
+  if (op.bias && epi) bias2 = *reinterpret_cast<const f16x2*>(op.bias + ecol);
+  f16x2 res2 = {};
+  if constexpr (!RES_FRESH) {
+    if (op.res && epi) res2 = *reinterpret_cast<const f16x2*>(op.res + (size_t)em * N + ecol);
+  }
+  wait();
+
+  const int arow = min(r16, M - 1);
+  f16x8 xf[NU];
+  if constexpr (LN) {
+    // Rows written in this launch: both rows' loads are issued before either is used.
+    if constexpr (A_FRESH) {
+      row0 = layer_norm_load_coherent<kFLnGroups>(op.a, (uint32_t)min(r0, M - 1) * kDModel, op.gamma, op.beta, lane);
+      row1 = layer_norm_load_coherent<kFLnGroups>(op.a, (uint32_t)min(r1, M - 1) * kDModel, op.gamma, op.beta, lane);
+    }
+    if (r0 < M)
+      layer_norm_finish<kFLnGroups>(row0, lane, [&](int f, f16x4 v) { *reinterpret_cast<f16x4*>(&sm.a_lds[r0 * kFALd + f]) = v; });
+    if (r1 < M)
+      layer_norm_finish<kFLnGroups>(row1, lane, [&](int f, f16x4 v) { *reinterpret_cast<f16x4*>(&sm.a_lds[r1 * kFALd + f]) = v; });
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+      xf[u] = *reinterpret_cast<const f16x8*>(&sm.a_lds[arow * kFALd + 32 * (wave + 8 * u) + 8 * g]);
+  } else {
+    if constexpr (A_FRAG) {
+      static_assert(A_FRESH, "fragment-ordered operands are written in the launch");
+#pragma unroll
+      for (int u = 0; u < NU; ++u) xf[u] = load16c(op.a, (uint32_t)(((wave + 8 * u) * kWave + lane) * 8));
+    } else {
+      const uint32_t xrow = (uint32_t)(arow * K + 8 * g);
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        xf[u] = A_FRESH ? load16c(op.a, xrow + 32 * (wave + 8 * u)) : load16(op.a + xrow + 32 * (wave + 8 * u));
+    }
+  }
+  if constexpr (RES_FRESH) {
+    if (op.res && epi) res2 = load4c(op.res, (uint32_t)(em * N + ecol));
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    f32x4 acc = {};
+#pragma unroll
+    for (int u = 0; u < NU; ++u) acc = mfma_16x16x32(wf[b][u], xf[u], acc);
+    // acc[r] = C^T[n = 16 b + 4 g + r][m = r16] over this wave's steps.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.red[wave][kFCols * b + 4 * g + r][r16] = acc[r];
+  }
+  __syncthreads();
+  if (!epi) return;
+  float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kFWaves; ++w) {
+    v0 += sm.red[w][kFCols * eb + en][em];
+    v1 += sm.red[w][kFCols * eb + en + 1][em];
+  }
+  v0 += (float)bias2[0];
+  v1 += (float)bias2[1];
+  if constexpr (ACT == 1) {
+    v0 = gelu_exact_f(v0);
+    v1 = gelu_exact_f(v1);
+  }
+  v0 += (float)res2[0];
+  v1 += (float)res2[1];
+  const uint32_t out = __builtin_bit_cast(uint32_t, pack_rne(v0, v1));
+  if constexpr (C_FRAG) {
+    static_assert(!APPEND, "the appended rows come from a row-major QKV block");
+    st32c(op.c + frag_index(em, ecol), out);  // columns ecol, ecol + 1 are adjacent there too
+    return;
+  }
+  st32c(op.c + (size_t)em * N + ecol, out);
+  if constexpr (APPEND) {
+    const int col = ecol - kDModel;  // 0 .. 1279: K, 1280 .. 2559: V (a pair never straddles)
+    if (col >= 0) {
+      const size_t row = (size_t)fa.slots.s[em] * kDModel;
+      if (col < kDModel) st32c(fa.k_cache + row + col, out);
+      else st32c(fa.v_cache + row + col - kDModel, out);
+    }
+  }
+}
+
+// Memory policies of the attention items (verify_core.hpp).
+struct SelfIo {
+  static constexpr bool kFreshRows = true;
+  const uint32_t* fresh_bits;  // LDS bitmap of the block's cache slots
+  StepWait w;
+  __device__ bool fresh(int key) const { return (fresh_bits[key >> 5] >> (key & 31)) & 1u; }
+  __device__ void wait() const { w(); }
+  __device__ static f16x8 load_q(const f16* base, uint32_t off) { return load16c(base, off); }
+  __device__ static f16x8 load_fresh(const f16* base, uint32_t off) { return load16c(base, off); }
+  // O in fragment order (the output projection's operand); four dims never straddle a fragment.
+  __device__ static void store_o(const vcore::Args& a, int mq, int head, int d0, f16x4 v) {
+    st64c(a.o + frag_index(mq, head * kHeadDim + d0), __builtin_bit_cast(uint64_t, v));
+  }
+};
+struct CrossIo {
+  static constexpr bool kFreshRows = false;
+  StepWait w;
+  __device__ bool fresh(int) const { return false; }
+  __device__ void wait() const { w(); }
+  __device__ static f16x8 load_q(const f16* base, uint32_t off) { return load16c(base, off); }
+  __device__ static f16x8 load_fresh(const f16* base, uint32_t off) { return load16(base + off); }
+  __device__ static void store_o(const vcore::Args& a, int mq, int head, int d0, f16x4 v) {
+    st64c(a.o + frag_index(mq, head * kHeadDim + d0), __builtin_bit_cast(uint64_t, v));
+  }
+};
+
+constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+template <int CPW>
+constexpr size_t kArenaBytes =
+    cmax(cmax(sizeof(vcore::Smem<CPW, kFWaves>), sizeof(vcore::Smem<1, kFWaves>)), sizeof(GemmSmem));
+
+// SELF_CPW: 32-key chunks per wave of the self-attention (1: n_kv <= 256, 2: <= 512).
+// SELF_MODE: vcore::kMaskRows or kMaskNone.
+template <int SELF_CPW, int SELF_MODE>
+__global__ __launch_bounds__(kFThreads) void decoder_layer_kernel(FusedArgs fa) {
+  __shared__ __attribute__((aligned(16))) unsigned char arena[kArenaBytes<SELF_CPW>];
+  __shared__ uint32_t fresh_bits[16];
+  __shared__ int s_item;
+  uint32_t* const ctl = fa.ctl;
+  const int total = fa.step_end[kSteps - 1];
+  if (threadIdx.x == 0) s_item = (int)__hip_atomic_fetch_add(&ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  int item = s_item;
+  while (item < total) {
+    // The thread index laundered once per item: without this the compiler hoists every
+    // step's lane-dependent offsets out of the loop and keeps them all live (spills).
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    // The next ticket is claimed now and used after this item: its round trip overlaps the
+    // item.  (Holding two tickets keeps the order argument: the next item is of this step or
+    // a later one, and this workgroup finishes the current item first.)
+    uint32_t next = 0;
+    if (tid == 0) next = __hip_atomic_fetch_add(&ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int p = 0;
+    while (item >= fa.step_end[p]) ++p;
+    const int local = item - (p ? fa.step_end[p - 1] : 0);
+    const StepWait wait{p >= 1 ? fa.flags : nullptr, p >= 3 ? fa.step_end[p - 3] : 0, p >= 2 ? fa.step_end[p - 2] : 0,
+                        p >= 2 ? fa.step_end[p - 2] : 0, p >= 1 ? fa.step_end[p - 1] : 0};
+    GemmSmem& gs = *reinterpret_cast<GemmSmem*>(arena);
+    switch (p) {
+      case 0:
+        gemm_item<2, 5, 0, true, false, false, false, true, false>(
+            fa, GemmOp{fa.w_qkv, fa.b_qkv, fa.x, fa.ln1_g, fa.ln1_b, nullptr, fa.qkv, kQkvCols, kDModel}, local, wait,
+            gs, tid);
+        break;
+      case 1: {
+        if (tid < 16) fresh_bits[tid] = 0u;
+        __syncthreads();
+        if (tid < fa.n_q) atomicOr(&fresh_bits[fa.slots.s[tid] >> 5], 1u << (fa.slots.s[tid] & 31));
+        __syncthreads();
+        const vcore::Args a{fa.qkv, kQkvCols, fa.n_q, fa.k_cache, fa.v_cache, fa.n_kv, kHeads, fa.mask, fa.mask_words,
+                            nullptr, fa.o, fa.verify_counters, fa.part_ml, fa.part_o};
+        vcore::verify_unit<SELF_MODE, SELF_CPW, kFWaves>(a, 0, local, 1,
+                                                         *reinterpret_cast<vcore::Smem<SELF_CPW, kFWaves>*>(arena),
+                                                         SelfIo{fresh_bits, wait}, tid);
+        break;
+      }
+      case 2:
+        gemm_item<1, 5, 0, false, true, true, false, false, false>(
+            fa, GemmOp{fa.w_o, fa.b_o, fa.o, nullptr, nullptr, fa.x, fa.x1, kDModel, kDModel}, local, wait, gs, tid);
+        break;
+      case 3:
+        gemm_item<1, 5, 0, true, true, false, false, false, false>(
+            fa, GemmOp{fa.w_qc, fa.b_qc, fa.x1, fa.ln2_g, fa.ln2_b, nullptr, fa.qc, kDModel, kDModel}, local, wait, gs,
+            tid);
+        break;
+      case 4: {
+        const vcore::Args a{fa.qc, kDModel, fa.n_q, fa.cross_k, fa.cross_v, fa.n_frames, kHeads, nullptr, 0,
+                            nullptr, fa.h, fa.verify_counters, fa.part_ml, fa.part_o};
+        vcore::verify_unit<vcore::kMaskNone, 1, kFWaves>(a, local % fa.cross_splits, local / fa.cross_splits,
+                                                         fa.cross_splits,
+                                                         *reinterpret_cast<vcore::Smem<1, kFWaves>*>(arena),
+                                                         CrossIo{wait}, tid);
+        break;
+      }
+      case 5:
+        gemm_item<1, 5, 0, false, true, true, true, false, false>(
+            fa, GemmOp{fa.w_oc, fa.b_oc, fa.h, nullptr, nullptr, fa.x1, fa.x2, kDModel, kDModel}, local, wait, gs, tid);
+        break;
+      case 6:
+        gemm_item<4, 5, 1, true, true, false, false, false, true>(
+            fa, GemmOp{fa.w_fc1, fa.b_fc1, fa.x2, fa.ln3_g, fa.ln3_b, nullptr, fa.f, 4 * kDModel, kDModel}, local,
+            wait, gs, tid);
+        break;
+      default:
+        gemm_item<1, 20, 0, false, true, true, true, false, false>(
+            fa, GemmOp{fa.w_fc2, fa.b_fc2, fa.f, nullptr, nullptr, fa.x2, fa.y, kDModel, 4 * kDModel}, local, wait, gs,
+            tid);
+        break;
+    }
+    publish(&fa.flags[item]);
+    if (tid == 0) s_item = (int)next;
+    __syncthreads();
+    item = s_item;
+  }
+  // The last workgroup to leave (every other one has left, so nothing else touches the
+  // counters or flags in this launch) clears them for the next launch.
+  __shared__ int s_last;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&ctl[kCtlStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  for (int i = threadIdx.x; i < total; i += kFThreads) st32c(&fa.flags[i], 0u);
+  if (threadIdx.x == 0) {
+    st32c(&ctl[0], 0u);
+    st32c(&ctl[kCtlStride], 0u);
+  }
+}
+
+}  // namespace
+
+int decoder_fused_items(int n_frames) {
+  const int cross_splits = (n_frames + kFWaves * vcore::kWaveKeys - 1) / (kFWaves * vcore::kWaveKeys);
+  // QKV, self-attention, the four 16-column GEMMs, cross-attention, fc1
+  return kQkvCols / (2 * kFCols) + kHeads + 4 * (kDModel / kFCols) + kHeads * cross_splits + 4 * kDModel / (4 * kFCols);
+}
+
+bool decoder_fused_supported(int n_q, int n_kv, int n_frames) {
+  const int cross_splits = (n_frames + kFWaves * vcore::kWaveKeys - 1) / (kFWaves * vcore::kWaveKeys);
+  return n_q >= 1 && n_q <= 16 && n_kv >= 1 && n_kv <= 2 * kFWaves * vcore::kWaveKeys && n_frames >= 1 &&
+         kHeads * cross_splits <= kMaxPollLoads * kWave && decoder_fused_items(n_frames) <= kDecoderFusedMaxItems;
+}
+
+hipError_t launch_decoder_layer_fused(const DecoderFusedParams& p, hipStream_t stream) {
+  if (!decoder_fused_supported(p.n_q, p.n_kv, p.n_frames) || p.workgroups < 1) return hipErrorInvalidValue;
+  FusedArgs fa{};
+  fa.x = static_cast<const f16*>(p.x);
+  fa.y = static_cast<f16*>(p.y);
+  fa.n_q = p.n_q;
+  fa.slots = p.slots;
+  fa.k_cache = static_cast<f16*>(p.k_cache);
+  fa.v_cache = static_cast<f16*>(p.v_cache);
+  fa.n_kv = p.n_kv;
+  fa.mask = p.mask;
+  fa.mask_words = (p.n_kv + 31) / 32;
+  fa.cross_k = static_cast<const f16*>(p.cross_k);
+  fa.cross_v = static_cast<const f16*>(p.cross_v);
+  fa.n_frames = p.n_frames;
+  fa.cross_splits = (p.n_frames + kFWaves * vcore::kWaveKeys - 1) / (kFWaves * vcore::kWaveKeys);
+  const f16* w[18];
+  for (int i = 0; i < 18; ++i) w[i] = static_cast<const f16*>(p.w[i]);
+  fa.ln1_g = w[0], fa.ln1_b = w[1], fa.w_qkv = w[2], fa.b_qkv = w[3], fa.w_o = w[4], fa.b_o = w[5];
+  fa.ln2_g = w[6], fa.ln2_b = w[7], fa.w_qc = w[8], fa.b_qc = w[9], fa.w_oc = w[10], fa.b_oc = w[11];
+  fa.ln3_g = w[12], fa.ln3_b = w[13], fa.w_fc1 = w[14], fa.b_fc1 = w[15], fa.w_fc2 = w[16], fa.b_fc2 = w[17];
+  fa.qkv = static_cast<f16*>(p.qkv);
+  fa.o = static_cast<f16*>(p.o);
+  fa.x1 = static_cast<f16*>(p.x1);
+  fa.qc = static_cast<f16*>(p.qc);
+  fa.h = static_cast<f16*>(p.h);
+  fa.x2 = static_cast<f16*>(p.x2);
+  fa.f = static_cast<f16*>(p.f);
+  fa.verify_counters = static_cast<uint32_t*>(p.verify_counters);
+  fa.part_ml = static_cast<float*>(p.part);
+  fa.part_o = fa.part_ml + (size_t)fa.cross_splits * p.n_q * kHeads * 2;
+  fa.ctl = static_cast<uint32_t*>(p.ctl);
+  fa.flags = static_cast<uint32_t*>(p.flags);
+  const int counts[kSteps] = {kQkvCols / (2 * kFCols), kHeads, kDModel / kFCols, kDModel / kFCols,
+                              kHeads * fa.cross_splits, kDModel / kFCols, 4 * kDModel / (4 * kFCols),
+                              kDModel / kFCols};
+  int run = 0;
+  for (int i = 0; i < kSteps; ++i) fa.step_end[i] = (run += counts[i]);
+  if (run != decoder_fused_items(p.n_frames)) return hipErrorInvalidValue;
+  const dim3 grid(p.workgroups), block(kFThreads);
+  const bool rows = p.mask != nullptr;
+  if (p.n_kv <= kFWaves * vcore::kWaveKeys) {
+    if (rows) hipLaunchKernelGGL((decoder_layer_kernel<1, vcore::kMaskRows>), grid, block, 0, stream, fa);
+    else hipLaunchKernelGGL((decoder_layer_kernel<1, vcore::kMaskNone>), grid, block, 0, stream, fa);
+  } else {
+    if (rows) hipLaunchKernelGGL((decoder_layer_kernel<2, vcore::kMaskRows>), grid, block, 0, stream, fa);
+    else hipLaunchKernelGGL((decoder_layer_kernel<2, vcore::kMaskNone>), grid, block, 0, stream, fa);
+  }
+  return hipGetLastError();
+}
+
+size_t decoder_fused_part_bytes(int n_q, int n_frames) {
+  const int cs = (n_frames + kFWaves * vcore::kWaveKeys - 1) / (kFWaves * vcore::kWaveKeys);
+  return cs > 1 ? (size_t)cs * n_q * kHeads * (2 + kHeadDim) * sizeof(float) : 0;
+}
+
+}  // namespace edda

@@ -79,4 +79,37 @@ hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, co
                          int mask_mode, const uint32_t* mask, const float* sinks, void* o, void* workspace,
                          hipStream_t stream);
 
+// The decoder's verification layer in one launch of `workgroups` persistent workgroups
+// (kernel 8, fp16 weights, n_kv <= 512).  w: ln1_gamma, ln1_beta, w_qkv, b_qkv, w_o, b_o,
+// ln2_gamma, ln2_beta, w_q_cross, b_q_cross, w_o_cross, b_o_cross, ln3_gamma, ln3_beta, w_fc1,
+// b_fc1, w_fc2, b_fc2 (biases may be null).  qkv .. f: workspace rows ([16][3840], [16][1280]
+// x5, [16][5120]); qc may alias o.  verify_counters: 20 per-head counters 256 bytes apart;
+// ctl: 2 counters 256 bytes apart; flags: decoder_fused_items(n_frames) words; all zero before
+// the launch and left zero by it.  part: decoder_fused_part_bytes(n_q, n_frames).
+struct DecoderFusedParams {
+  const void* x;
+  void* y;
+  int n_q;
+  Slots slots;
+  void* k_cache;
+  void* v_cache;
+  int n_kv;
+  const uint32_t* mask;  // rows [n_q][ceil(n_kv / 32)] or null (every slot admitted)
+  const void* cross_k;
+  const void* cross_v;
+  int n_frames;
+  const void* w[18];
+  void *qkv, *o, *x1, *qc, *h, *x2, *f;
+  void* verify_counters;
+  void* ctl;
+  void* flags;
+  void* part;
+  int workgroups;
+};
+constexpr int kDecoderFusedMaxItems = 768;
+int decoder_fused_items(int n_frames);
+bool decoder_fused_supported(int n_q, int n_kv, int n_frames);
+size_t decoder_fused_part_bytes(int n_q, int n_frames);
+hipError_t launch_decoder_layer_fused(const DecoderFusedParams& p, hipStream_t stream);
+
 }  // namespace edda
