@@ -393,7 +393,7 @@ static_assert(kSplitCounterOffset + (EDDA_D_MODEL / 16) * 64 <= kFusedCtlOffset 
 constexpr int kFusedWorkgroups = 256;
 
 struct DecoderWs {
-  size_t verify, h, qkv, o, x1, x2, f, total;
+  size_t verify, h, qkv, o, x1, x2, f, qc, total;
 };
 
 DecoderWs decoder_ws(int32_t n_q, int32_t n_kv, int32_t n_frames) {
@@ -418,7 +418,8 @@ DecoderWs decoder_ws(int32_t n_q, int32_t n_kv, int32_t n_frames) {
   w.x1 = w.o + align256(row16 * EDDA_D_MODEL);
   w.x2 = w.x1 + align256(row * EDDA_D_MODEL);
   w.f = w.x2 + align256(row * EDDA_D_MODEL);
-  w.total = w.f + align256(row16 * EDDA_D_FF);
+  w.qc = w.f + align256(row16 * EDDA_D_FF);  // the single-launch layer's cross query
+  w.total = w.qc + align256(row * EDDA_D_MODEL);
   return w;
 }
 }  // namespace
@@ -515,7 +516,7 @@ edda_status decoder_layer(const char* fn, const void* x, int32_t n_q, const int3
                          wt->ln2_gamma, wt->ln2_beta, wt->q_cross.w,   wt->b_q_cross,  wt->o_cross.w,  wt->b_o_cross,
                          wt->ln3_gamma, wt->ln3_beta, wt->fc1.w,       wt->b_fc1,      wt->fc2.w,      wt->b_fc2};
     for (int i = 0; i < 18; ++i) p.w[i] = w[i];
-    p.qkv = qkv, p.o = o, p.x1 = x1, p.qc = o, p.h = h, p.x2 = x2, p.f = f;
+    p.qkv = qkv, p.o = o, p.x1 = x1, p.qc = ws + L.qc, p.h = h, p.x2 = x2, p.f = f;
     p.verify_counters = ws, p.ctl = ws + kFusedCtlOffset, p.flags = ws + kFusedFlagOffset, p.part = sk_part;
     p.workgroups = kFusedWorkgroups;
     EDDA_STEP(edda::launch_decoder_layer_fused(p, s), "single-launch layer");

@@ -8,7 +8,7 @@
 // workgroups takes work items from a single atomic ticket counter, items numbered step by
 // step; an item of step p first issues the loads that depend on nothing computed in this
 // launch (its weight fragments into registers, the old K/V cache rows, the cross-attention
-// K/V), then waits until every item of step p - 1 has counted itself done, then loads its
+// K/V), then waits until every item of step p - 1 has set its done flag, then loads its
 // activations and finishes.  Workgroups run ahead of the step being computed, so the next
 // steps' weights stream in while the current step runs.
 //
@@ -22,16 +22,21 @@
 // launch leaves zero as it found them.
 //
 // Memory ordering across the XCDs' separate L2 caches: everything one step writes and a
-// later step reads (activations, appended cache rows) is stored with agent-scope atomic
-// stores, which write through to the device's coherence point; an item's stores are
-// acknowledged (vmcnt 0) before its workgroup barrier and its done flag.  A waiting item,
-// once it has seen the flags, reads such data with device-coherent loads (the sc1 cache
-// policy, 16 bytes a lane through buffer loads).  Loads issued before the wait (weights, old
-// cache rows, cross-attention K/V, the layer input) touch nothing this launch writes and are
-// plain.  (Measured and dropped: one agent-scope acquire fence per item and plain loads
-// after it; each fence invalidates the whole XCD's L2 under the other workgroups on it, and
-// the layer ran 55 % slower.  A release fence's L2 write-back costs 4-14 us, hence the
-// write-through stores.)
+// later step reads is stored with agent-scope atomic stores, which write through to the
+// device's coherence point, and an item's stores are acknowledged (vmcnt 0) before its
+// workgroup barrier and its done flag.  Every workspace buffer is written by one step and read
+// only after that step's flags are all set, and no item reads it earlier in the launch; an L2
+// cache therefore never holds a stale copy of it (the caches are invalidated at kernel start),
+// and consumers read it with plain loads, which miss in their L2 and fetch from the coherence
+// point.  The self-attention reads the appended K/V rows from the QKV block, not from the
+// cache: with a cache that is only 16-byte aligned, a row's 128-byte line can hold the end of
+// a neighbouring old row that another item loaded before its wait.  Loads issued before a wait
+// (weights, old cache rows, cross-attention K/V, the layer input) touch nothing this launch
+// writes.  Measured and dropped: an agent-scope acquire fence per item with plain loads after
+// it (each fence invalidates the whole XCD's L2 under the other workgroups on it: the layer
+// ran 55 % slower); release fences (their L2 write-back costs 4-14 us, hence the write-through
+// stores); 8-byte device-coherent loads of the activations (2-3x slower than plain 16-byte
+// loads).
 //
 // Work items (the block GEMMs as kernel 6: weights as the MFMA A operand, 8 waves over the
 // 32-deep K steps, summed in LDS; a LayerNorm is computed once per item):
@@ -61,26 +66,13 @@ constexpr int kFCols = 16;
 constexpr int kFLnGroups = kDModel / 256;
 constexpr int kFALd = kDModel + 8;  // LDS row stride (halves) of the normalised rows
 constexpr int kSteps = 8;
+constexpr int kCrossMergeBatch = 8;  // 1500 frames: 6 splits of 256 keys
 constexpr int kCtlStride = 64;  // uint32 words: the two counters 256 bytes apart
 constexpr int kSpinLimit = 1 << 20;  // polls (seconds) before a wait gives up
 constexpr int kCoarseSleep = 127;    // s_sleep units of 64 clocks between polls
-constexpr int kFineSleep = 16;
+constexpr int kFineSleep = 8;
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Device-coherent loads (sc1 cache policy) at a byte offset from a wave-uniform base.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
-}
-constexpr int kSc1 = 16;  // cache-policy operand of the buffer-load builtins: sc1
-__device__ __forceinline__ f16x8 load16c(const f16* base, uint32_t elem) {
-  return __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(coherent_rsrc(base), 2 * elem, 0, kSc1));
-}
-__device__ __forceinline__ f16x4 load8c(const f16* base, uint32_t elem) {
-  return __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(coherent_rsrc(base), 2 * elem, 0, kSc1));
-}
-__device__ __forceinline__ f16x2 load4c(const f16* base, uint32_t elem) {
-  return __builtin_bit_cast(f16x2, __builtin_amdgcn_raw_buffer_load_b32(coherent_rsrc(base), 2 * elem, 0, kSc1));
-}
 __device__ __forceinline__ uint32_t ld32c(const void* p) {
   return __hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -98,9 +90,9 @@ __device__ __forceinline__ float gelu_exact_f(float v) { return 0.5f * v * (1.0f
 // kMaxPollLoads per lane) until all are set (bounded), then the workgroup proceeds.  First,
 // rarely, those of step p - 2 (an item claimed well ahead of its turn), then more often those
 // of step p - 1: every poll is a device-coherent load that competes with the weight and
-// activation traffic, and measured on the layer, polling less often (up to ~0.7 us between
-// polls) ran faster than polling more often or keeping two polls in flight.  Reads only: a
-// flag line is never the target of atomics, which the memory side would serialise.
+// activation traffic (measured on the layer: polling every ~0.25 us beat both polling
+// continuously and keeping two polls in flight; polling every ~0.5 us or more ran slower).
+// Reads only: a flag line is never the target of atomics, which the memory side serialises.
 constexpr int kMaxPollLoads = 4;  // flags of up to 256 items per step
 template <int kSleep>
 __device__ __forceinline__ void poll_flags(const uint32_t* flags, int begin, int end) {
@@ -187,23 +179,9 @@ struct GemmSmem {
 // One block-GEMM item: NB column blocks of 16 (C[:, n0 .. n0 + 16 NB)) over the whole K = 256 NU
 // (wave w takes the 32-deep steps w, w + 8, ...).  A_FRESH / RES_FRESH: the operand rows / the
 // residual were written in this launch (coherent loads after the wait).  A_FRAG / C_FRAG: A is
-// read, C written, in fragment order (C_FRAG: no residual, no append).  Per block the arithmetic is kernel 6's (same fragments,
+// read, C written, in fragment order (C_FRAG: no residual, no append).  (A_FRESH only decides
+// whether the LayerNorm rows are loaded before or after the wait.)  Per block the arithmetic is kernel 6's (same fragments,
 // same summation order over steps and waves).
-template <int kGroups>
-__device__ __forceinline__ LnRow<kGroups> layer_norm_load_coherent(const f16* x, uint32_t row0,
-                                                                   const f16* __restrict__ gamma,
-                                                                   const f16* __restrict__ beta, int lane) {
-  LnRow<kGroups> r;
-#pragma unroll
-  for (int c = 0; c < kGroups; ++c) {
-    const int f = 4 * (c * kWave + lane);
-    r.v[c] = load8c(x, row0 + f);
-    r.g[c] = *reinterpret_cast<const f16x4*>(gamma + f);
-    r.b[c] = *reinterpret_cast<const f16x4*>(beta + f);
-  }
-  return r;
-}
-
 // Fragment order of a [16][K] operand consumed by the block GEMMs: for each 32-deep step s, the
 // 64 lanes' 16-byte fragments in lane order (lane 16 g + r holds row r, k = 32 s + 8 g ..
 // 8 g + 7), so a consumer's load instruction reads 1 KB contiguous (row-major rows give 16
@@ -219,13 +197,26 @@ __device__ __forceinline__ void gemm_item(const FusedArgs& fa, const GemmOp& op,
   const int r16 = lane & 15, g = lane >> 4;
   const int M = fa.n_q, K = op.K, N = op.N;
   const int n0 = item * NB * kFCols;
-  // LayerNorm rows wave and wave + 8 that exist before the launch: loaded ahead of the weights
-  // (a wave's loads return in order, so rows queued behind 80 KB of weights would wait for them).
-  const int r0 = wave, r1 = wave + kFWaves;
-  LnRow<kFLnGroups> row0, row1;
+  // LayerNorm input rows: staged through LDS by all threads, 16-byte chunk t + 512 i of the
+  // M x 1280 block each (a wave's load is 1 KB contiguous).  Rows that exist before the launch
+  // are loaded ahead of the weights (a wave's loads return in order, so rows queued behind
+  // 80 KB of weights would wait for them); gamma and beta (constants) before the wait.
+  constexpr int kLnChunks = 16 * kDModel / 8, kLnPerThread = kLnChunks / kFThreads;
+  static_assert(kLnChunks % kFThreads == 0, "LayerNorm chunks per thread");
+  f16x8 raw[LN ? kLnPerThread : 1];
+  f16x4 gam[LN ? kFLnGroups : 1], bet[LN ? kFLnGroups : 1];
+  auto ln_chunk = [&](int i) { return (uint32_t)((tid + kFThreads * i) * 8); };  // element index
   if constexpr (LN && !A_FRESH) {
-    row0 = layer_norm_load<kFLnGroups>(op.a + (size_t)min(r0, M - 1) * kDModel, op.gamma, op.beta, lane);
-    row1 = layer_norm_load<kFLnGroups>(op.a + (size_t)min(r1, M - 1) * kDModel, op.gamma, op.beta, lane);
+#pragma unroll
+    for (int i = 0; i < kLnPerThread; ++i)
+      if ((int)ln_chunk(i) < M * kDModel) raw[i] = load16(op.a + ln_chunk(i));
+  }
+  if constexpr (LN) {
+#pragma unroll
+    for (int c = 0; c < kFLnGroups; ++c) {
+      gam[c] = *reinterpret_cast<const f16x4*>(op.gamma + 4 * (c * kWave + lane));
+      bet[c] = *reinterpret_cast<const f16x4*>(op.beta + 4 * (c * kWave + lane));
+    }
   }
   // Weight fragments: row n0 + 16 b + r16, 8 consecutive k of each step.
   f16x8 wf[NB][NU];
@@ -250,15 +241,34 @@ __device__ __forceinline__ void gemm_item(const FusedArgs& fa, const GemmOp& op,
   const int arow = min(r16, M - 1);
   f16x8 xf[NU];
   if constexpr (LN) {
-    // Rows written in this launch: both rows' loads are issued before either is used.
     if constexpr (A_FRESH) {
-      row0 = layer_norm_load_coherent<kFLnGroups>(op.a, (uint32_t)min(r0, M - 1) * kDModel, op.gamma, op.beta, lane);
-      row1 = layer_norm_load_coherent<kFLnGroups>(op.a, (uint32_t)min(r1, M - 1) * kDModel, op.gamma, op.beta, lane);
+#pragma unroll
+      for (int i = 0; i < kLnPerThread; ++i)
+        if ((int)ln_chunk(i) < M * kDModel) raw[i] = load16(op.a + ln_chunk(i));
     }
-    if (r0 < M)
-      layer_norm_finish<kFLnGroups>(row0, lane, [&](int f, f16x4 v) { *reinterpret_cast<f16x4*>(&sm.a_lds[r0 * kFALd + f]) = v; });
-    if (r1 < M)
-      layer_norm_finish<kFLnGroups>(row1, lane, [&](int f, f16x4 v) { *reinterpret_cast<f16x4*>(&sm.a_lds[r1 * kFALd + f]) = v; });
+#pragma unroll
+    for (int i = 0; i < kLnPerThread; ++i) {
+      const int e = (int)ln_chunk(i), row = e / kDModel;
+      if (e < M * kDModel) *reinterpret_cast<f16x8*>(&sm.a_lds[row * kFALd + e - row * kDModel]) = raw[i];
+    }
+    __syncthreads();
+    // Rows wave and wave + 8, normalised in place (each row belongs to one wave); both rows'
+    // statistics interleaved (a row past M is computed from whatever the buffer holds and not
+    // stored).
+    const int r0 = wave, r1 = wave + kFWaves;
+    LnRow<kFLnGroups> row[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < kFLnGroups; ++c) {
+        row[h].v[c] = *reinterpret_cast<const f16x4*>(&sm.a_lds[(wave + kFWaves * h) * kFALd + 4 * (c * kWave + lane)]);
+        row[h].g[c] = gam[c];
+        row[h].b[c] = bet[c];
+      }
+    layer_norm_finish2<kFLnGroups>(
+        row[0], row[1], lane,
+        [&](int f, f16x4 v) { if (r0 < M) *reinterpret_cast<f16x4*>(&sm.a_lds[r0 * kFALd + f]) = v; },
+        [&](int f, f16x4 v) { if (r1 < M) *reinterpret_cast<f16x4*>(&sm.a_lds[r1 * kFALd + f]) = v; });
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < NU; ++u)
@@ -267,16 +277,16 @@ __device__ __forceinline__ void gemm_item(const FusedArgs& fa, const GemmOp& op,
     if constexpr (A_FRAG) {
       static_assert(A_FRESH, "fragment-ordered operands are written in the launch");
 #pragma unroll
-      for (int u = 0; u < NU; ++u) xf[u] = load16c(op.a, (uint32_t)(((wave + 8 * u) * kWave + lane) * 8));
+      for (int u = 0; u < NU; ++u) xf[u] = load16(op.a + ((wave + 8 * u) * kWave + lane) * 8);
     } else {
       const uint32_t xrow = (uint32_t)(arow * K + 8 * g);
 #pragma unroll
       for (int u = 0; u < NU; ++u)
-        xf[u] = A_FRESH ? load16c(op.a, xrow + 32 * (wave + 8 * u)) : load16(op.a + xrow + 32 * (wave + 8 * u));
+        xf[u] = load16(op.a + xrow + 32 * (wave + 8 * u));
     }
   }
   if constexpr (RES_FRESH) {
-    if (op.res && epi) res2 = load4c(op.res, (uint32_t)(em * N + ecol));
+    if (op.res && epi) res2 = *reinterpret_cast<const f16x2*>(op.res + (size_t)em * N + ecol);
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -323,13 +333,18 @@ __device__ __forceinline__ void gemm_item(const FusedArgs& fa, const GemmOp& op,
 // Memory policies of the attention items (verify_core.hpp).
 struct SelfIo {
   static constexpr bool kFreshRows = true;
-  const uint32_t* fresh_bits;  // LDS bitmap of the block's cache slots
+  const int8_t* fresh_row;  // LDS: block row of each cache slot, -1 for a slot not in the block
+  const f16* qkv;           // the block's packed QKV rows: its K and V are the appended rows
   StepWait w;
-  __device__ bool fresh(int key) const { return (fresh_bits[key >> 5] >> (key & 31)) & 1u; }
+  __device__ bool fresh(int key) const { return fresh_row[key] >= 0; }
   __device__ void wait() const { w(); }
-  __device__ static f16x8 load_q(const f16* base, uint32_t off) { return load16c(base, off); }
-  __device__ static f16x8 load_fresh(const f16* base, uint32_t off) { return load16c(base, off); }
-  // O in fragment order (the output projection's operand); four dims never straddle a fragment.
+  __device__ static f16x8 load_q(const f16* base, uint32_t off) { return load16(base + off); }
+  // The appended rows read from the QKV block (written once in the launch, read after its
+  // flags) rather than from the cache, whose lines may also hold the end of an old row.
+  __device__ f16x8 fresh_k(int key, int col) const { return load16(qkv + fresh_row[key] * kQkvCols + kDModel + col); }
+  __device__ f16x8 fresh_v(int key, int col) const {
+    return load16(qkv + fresh_row[key] * kQkvCols + 2 * kDModel + col);
+  }
   __device__ static void store_o(const vcore::Args& a, int mq, int head, int d0, f16x4 v) {
     st64c(a.o + frag_index(mq, head * kHeadDim + d0), __builtin_bit_cast(uint64_t, v));
   }
@@ -339,8 +354,9 @@ struct CrossIo {
   StepWait w;
   __device__ bool fresh(int) const { return false; }
   __device__ void wait() const { w(); }
-  __device__ static f16x8 load_q(const f16* base, uint32_t off) { return load16c(base, off); }
-  __device__ static f16x8 load_fresh(const f16* base, uint32_t off) { return load16(base + off); }
+  __device__ static f16x8 load_q(const f16* base, uint32_t off) { return load16(base + off); }
+  __device__ f16x8 fresh_k(int, int) const { return f16x8{}; }
+  __device__ f16x8 fresh_v(int, int) const { return f16x8{}; }
   __device__ static void store_o(const vcore::Args& a, int mq, int head, int d0, f16x4 v) {
     st64c(a.o + frag_index(mq, head * kHeadDim + d0), __builtin_bit_cast(uint64_t, v));
   }
@@ -356,7 +372,7 @@ constexpr size_t kArenaBytes =
 template <int SELF_CPW, int SELF_MODE>
 __global__ __launch_bounds__(kFThreads) void decoder_layer_kernel(FusedArgs fa) {
   __shared__ __attribute__((aligned(16))) unsigned char arena[kArenaBytes<SELF_CPW>];
-  __shared__ uint32_t fresh_bits[16];
+  __shared__ int8_t fresh_row[2 * kFWaves * vcore::kWaveKeys];
   __shared__ int s_item;
   uint32_t* const ctl = fa.ctl;
   const int total = fa.step_end[kSteps - 1];
@@ -386,15 +402,15 @@ __global__ __launch_bounds__(kFThreads) void decoder_layer_kernel(FusedArgs fa) 
             gs, tid);
         break;
       case 1: {
-        if (tid < 16) fresh_bits[tid] = 0u;
+        fresh_row[tid] = -1;  // 512 threads, 512 slots
         __syncthreads();
-        if (tid < fa.n_q) atomicOr(&fresh_bits[fa.slots.s[tid] >> 5], 1u << (fa.slots.s[tid] & 31));
+        if (tid < fa.n_q) fresh_row[fa.slots.s[tid]] = (int8_t)tid;
         __syncthreads();
         const vcore::Args a{fa.qkv, kQkvCols, fa.n_q, fa.k_cache, fa.v_cache, fa.n_kv, kHeads, fa.mask, fa.mask_words,
                             nullptr, fa.o, fa.verify_counters, fa.part_ml, fa.part_o};
         vcore::verify_unit<SELF_MODE, SELF_CPW, kFWaves>(a, 0, local, 1,
                                                          *reinterpret_cast<vcore::Smem<SELF_CPW, kFWaves>*>(arena),
-                                                         SelfIo{fresh_bits, wait}, tid);
+                                                         SelfIo{fresh_row, fa.qkv, wait}, tid);
         break;
       }
       case 2:
@@ -409,7 +425,8 @@ __global__ __launch_bounds__(kFThreads) void decoder_layer_kernel(FusedArgs fa) 
       case 4: {
         const vcore::Args a{fa.qc, kDModel, fa.n_q, fa.cross_k, fa.cross_v, fa.n_frames, kHeads, nullptr, 0,
                             nullptr, fa.h, fa.verify_counters, fa.part_ml, fa.part_o};
-        vcore::verify_unit<vcore::kMaskNone, 1, kFWaves>(a, local % fa.cross_splits, local / fa.cross_splits,
+        vcore::verify_unit<vcore::kMaskNone, 1, kFWaves, CrossIo, kCrossMergeBatch>(a, local % fa.cross_splits,
+                                                                                     local / fa.cross_splits,
                                                          fa.cross_splits,
                                                          *reinterpret_cast<vcore::Smem<1, kFWaves>*>(arena),
                                                          CrossIo{wait}, tid);
@@ -492,8 +509,8 @@ hipError_t launch_decoder_layer_fused(const DecoderFusedParams& p, hipStream_t s
   fa.x2 = static_cast<f16*>(p.x2);
   fa.f = static_cast<f16*>(p.f);
   fa.verify_counters = static_cast<uint32_t*>(p.verify_counters);
-  fa.part_ml = static_cast<float*>(p.part);
-  fa.part_o = fa.part_ml + (size_t)fa.cross_splits * p.n_q * kHeads * 2;
+  fa.part_o = static_cast<float*>(p.part);  // o partials first (16-byte aligned), then (m, l)
+  fa.part_ml = fa.part_o + (size_t)fa.cross_splits * p.n_q * kHeads * kHeadDim;
   fa.ctl = static_cast<uint32_t*>(p.ctl);
   fa.flags = static_cast<uint32_t*>(p.flags);
   const int counts[kSteps] = {kQkvCols / (2 * kFCols), kHeads, kDModel / kFCols, kDModel / kFCols,

@@ -83,7 +83,7 @@ hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, co
 // (kernel 8, fp16 weights, n_kv <= 512).  w: ln1_gamma, ln1_beta, w_qkv, b_qkv, w_o, b_o,
 // ln2_gamma, ln2_beta, w_q_cross, b_q_cross, w_o_cross, b_o_cross, ln3_gamma, ln3_beta, w_fc1,
 // b_fc1, w_fc2, b_fc2 (biases may be null).  qkv .. f: workspace rows ([16][3840], [16][1280]
-// x5, [16][5120]); qc may alias o.  verify_counters: 20 per-head counters 256 bytes apart;
+// x5, [16][5120]), no two aliased.  verify_counters: 20 per-head counters 256 bytes apart;
 // ctl: 2 counters 256 bytes apart; flags: decoder_fused_items(n_frames) words; all zero before
 // the launch and left zero by it.  part: decoder_fused_part_bytes(n_q, n_frames).
 struct DecoderFusedParams {

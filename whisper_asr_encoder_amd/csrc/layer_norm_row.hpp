@@ -1,7 +1,8 @@
 // LayerNorm of one row by one wave, shared by the LayerNorm kernel and the block-row GEMM
 // that normalises its own operand rows: y = (x - mean) / sqrt(var + 1e-5) * gamma + beta,
 // var the biased variance, statistics in fp32 over values held in registers (two passes over
-// the registers, one read of the row), one rounding to fp16.  Each lane holds kGroups groups
+// the registers, one read of the row), one rounding to fp16.  (The fused decoder layer uses
+// the same arithmetic.)  Each lane holds kGroups groups
 // of 4 consecutive features (feature 4 (c * 64 + lane) + j), so a wave reads 512 contiguous
 // bytes per group; both callers get bit-identical rows.
 #pragma once
@@ -61,24 +62,32 @@ __device__ __forceinline__ LnRow<kGroups> layer_norm_load(const f16* __restrict_
 }
 
 // store(f, value) receives the normalised fp16 values of features f .. f + 3.
-template <int kGroups, typename Store>
-__device__ __forceinline__ void layer_norm_finish(const LnRow<kGroups>& r, int lane, Store store) {
+// The lane's sums run in four independent accumulators (one per position j of a group, added
+// in group order, then combined as (s0 + s1) + (s2 + s3)): a 20-long chain of dependent adds
+// would leave the wave waiting on the adder's latency.
+template <int kGroups>
+__device__ __forceinline__ float ln_stats(const LnRow<kGroups>& r, float& rstd) {
   constexpr int kFeatures = 256 * kGroups;
-  float s = 0.0f;
+  float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < kGroups; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s += (float)r.v[c][j];
-  const float mean = ln_wave_sum(s) * (1.0f / kFeatures);
-  float q = 0.0f;
+    for (int j = 0; j < 4; ++j) s[j] += (float)r.v[c][j];
+  const float mean = ln_wave_sum((s[0] + s[1]) + (s[2] + s[3])) * (1.0f / kFeatures);
+  float q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < kGroups; ++c)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float d = (float)r.v[c][j] - mean;
-      q += d * d;
+      q[j] += d * d;
     }
-  const float rstd = 1.0f / sqrtf(ln_wave_sum(q) * (1.0f / kFeatures) + kLnEps);
+  rstd = 1.0f / sqrtf(ln_wave_sum((q[0] + q[1]) + (q[2] + q[3])) * (1.0f / kFeatures) + kLnEps);
+  return mean;
+}
+
+template <int kGroups, typename Store>
+__device__ __forceinline__ void ln_apply(const LnRow<kGroups>& r, float mean, float rstd, int lane, Store store) {
 #pragma unroll
   for (int c = 0; c < kGroups; ++c) {
     float o[4];
@@ -87,6 +96,24 @@ __device__ __forceinline__ void layer_norm_finish(const LnRow<kGroups>& r, int l
     const f16x2 lo = pack_rne(o[0], o[1]), hi = pack_rne(o[2], o[3]);
     store(4 * (c * kWave + lane), (f16x4){lo[0], lo[1], hi[0], hi[1]});
   }
+}
+
+template <int kGroups, typename Store>
+__device__ __forceinline__ void layer_norm_finish(const LnRow<kGroups>& r, int lane, Store store) {
+  float rstd;
+  const float mean = ln_stats<kGroups>(r, rstd);
+  ln_apply<kGroups>(r, mean, rstd, lane, store);
+}
+
+// Two rows by one wave, their statistics interleaved (each row's arithmetic as above).
+template <int kGroups, typename Store0, typename Store1>
+__device__ __forceinline__ void layer_norm_finish2(const LnRow<kGroups>& r0, const LnRow<kGroups>& r1, int lane,
+                                                   Store0 store0, Store1 store1) {
+  float rstd0, rstd1;
+  const float mean0 = ln_stats<kGroups>(r0, rstd0);
+  const float mean1 = ln_stats<kGroups>(r1, rstd1);
+  ln_apply<kGroups>(r0, mean0, rstd0, lane, store0);
+  ln_apply<kGroups>(r1, mean1, rstd1, lane, store1);
 }
 
 template <int kGroups, typename Store>

@@ -159,10 +159,11 @@ __global__ __launch_bounds__(kSkThreads) void skinny_gemm_kernel(const f16* __re
                                                              ln.beta, lane);
     const LnRow<kLnGroups> row1 = layer_norm_load<kLnGroups>(A + (size_t)min(r1, M - 1) * kDModel, ln.gamma,
                                                              ln.beta, lane);
-    if (r0 < M)
-      layer_norm_finish<kLnGroups>(row0, lane, [&](int f, f16x4 v) { *reinterpret_cast<f16x4*>(&a_lds[r0 * kALd + f]) = v; });
-    if (r1 < M)
-      layer_norm_finish<kLnGroups>(row1, lane, [&](int f, f16x4 v) { *reinterpret_cast<f16x4*>(&a_lds[r1 * kALd + f]) = v; });
+    // Both rows' statistics interleaved; a row past M (clamped to row M - 1) is not stored.
+    layer_norm_finish2<kLnGroups>(
+        row0, row1, lane,
+        [&](int f, f16x4 v) { if (r0 < M) *reinterpret_cast<f16x4*>(&a_lds[r0 * kALd + f]) = v; },
+        [&](int f, f16x4 v) { if (r1 < M) *reinterpret_cast<f16x4*>(&a_lds[r1 * kALd + f]) = v; });
     __syncthreads();
   }
   if (group0) {

@@ -70,8 +70,9 @@ hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, co
   float* part_o = nullptr;
   if (n_splits > 1) {
     counters = static_cast<uint32_t*>(workspace);
-    part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
-    part_o = part_ml + (size_t)n_splits * n_q * n_heads * 2;
+    // o partials first (16-byte aligned for the merge's 16-byte loads), then (m, l).
+    part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
+    part_ml = part_o + (size_t)n_splits * n_q * n_heads * kHeadDim;
   }
   const dim3 grid(n_splits, n_heads);
   int threads = kVThreads;

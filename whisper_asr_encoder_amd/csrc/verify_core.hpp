@@ -36,7 +36,7 @@ constexpr int kVtLd = kWaveKeys + 4;  // V^T row stride (halves): 72 B, 8-byte a
 constexpr int kCounterStride = 64;  // uint32 words
 // s_waitcnt immediate: vmcnt 0, expcnt and lgkmcnt at their maxima (no wait).
 constexpr int kWaitVmcnt0 = 0x0F70;
-constexpr int kMergeBatch = 16;  // splits whose partials the merging unit loads at once
+constexpr int kMergeBatch = 16;  // default: splits whose partials the merging unit loads at once
 
 enum MaskMode { kMaskRows = 0, kMaskNone = 1, kMaskCausal = 2 };
 
@@ -49,6 +49,14 @@ __device__ __forceinline__ void store_coherent(float* p, float a, float b) {
 __device__ __forceinline__ f32x2 load_coherent(const float* p) {
   return __builtin_bit_cast(f32x2, __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)),
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Four floats (16-byte aligned) read with the device-coherent cache policy (sc1) through a
+// buffer load: at a float index from a wave-uniform base.
+__device__ __forceinline__ f32x4 load_coherent4(const float* base, uint32_t idx) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, 0x7fffffff, 0x00020000);
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 4 * idx, 0, 16));
 }
 
 __device__ __forceinline__ float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
@@ -116,7 +124,8 @@ struct PlainIo {
   __device__ bool fresh(int) const { return false; }
   __device__ void wait() const {}
   __device__ static f16x8 load_q(const f16* base, uint32_t off) { return load16(base + off); }
-  __device__ static f16x8 load_fresh(const f16* base, uint32_t off) { return load16(base + off); }
+  __device__ f16x8 fresh_k(int, int) const { return f16x8{}; }
+  __device__ f16x8 fresh_v(int, int) const { return f16x8{}; }
   // O row-major: [n_q][n_heads][64].
   __device__ static void store_o(const Args& a, int mq, int head, int d0, f16x4 v) {
     *reinterpret_cast<f16x4*>(a.o + ((size_t)mq * a.n_heads + head) * kHeadDim + d0) = v;
@@ -125,11 +134,12 @@ struct PlainIo {
 
 // The unit (split, head) of n_splits.  Io supplies the memory policy: wait() runs after the
 // K/V loads of the rows that exist before the unit starts and before every other load; keys
-// for which fresh(key) holds are loaded only after it, through load_fresh(base, element
-// offset); Q through load_q(base, element offset); O's four values (query mq, head, dims d0 ..
+// for which fresh(key) holds are loaded only after it, through fresh_k / fresh_v(key, column
+// within the [n_heads * 64] row); Q through load_q(base, element offset); O's four values (query mq, head, dims d0 ..
 // d0 + 3) stored through store_o(args, mq, head, d0, values).  Threads of a workgroup all call this (it has barriers); it
-// returns per thread.  tid: the thread's index in the workgroup.
-template <int kMode, int CPW, int NW, typename Io>
+// returns per thread.  tid: the thread's index in the workgroup.  MB: splits whose partials
+// the merging unit loads at once.
+template <int kMode, int CPW, int NW, typename Io, int MB = kMergeBatch>
 __device__ __forceinline__ void verify_unit(const Args& a, int split, int head, int n_splits, Smem<CPW, NW>& sm,
                                             const Io& io, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
@@ -194,17 +204,18 @@ __device__ __forceinline__ void verify_unit(const Args& a, int split, int head, 
     for (int c = 0; c < CPW; ++c) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const uint32_t off = k_off(c, blk);
-        if (io.fresh(min(chunk_key0(c) + 16 * blk + r16, last_key))) {
-          kf[c][blk][0] = io.load_fresh(a.k, off);
-          kf[c][blk][1] = io.load_fresh(a.k, off + 32);
+        const int key = min(chunk_key0(c) + 16 * blk + r16, last_key);
+        if (io.fresh(key)) {
+          kf[c][blk][0] = io.fresh_k(key, head * kHeadDim + 8 * G);
+          kf[c][blk][1] = io.fresh_k(key, head * kHeadDim + 8 * G + 32);
         }
       }
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int k0 = v_key(c, r, 0), k1 = v_key(c, r, 1);
-        if (io.fresh(k0)) va[c][r] = io.load_fresh(a.v, v_off(k0, r));
-        if (io.fresh(k1)) vb[c][r] = io.load_fresh(a.v, v_off(k1, r));
+        const int col = head * kHeadDim + 8 * ((lane + kWave * r) & 7);
+        if (io.fresh(k0)) va[c][r] = io.fresh_v(k0, col);
+        if (io.fresh(k1)) vb[c][r] = io.fresh_v(k1, col);
       }
     }
   }
@@ -342,28 +353,26 @@ __device__ __forceinline__ void verify_unit(const Args& a, int split, int head, 
   // Every split has arrived: reset the counter for the next call.
   if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!row_ok) return;
-  // Merge the splits kMergeBatch at a time: every load of a batch is issued before any
+  // Merge the splits MB at a time: every load of a batch is issued before any
   // is used (indices past the last split are clamped and their weights dropped), and
   // the running (M, L, sum) is rescaled to each batch's maximum.
   M = -INFINITY;
   L = 0.0f;
   f32x4 sum = {};
-  for (int s0 = 0; s0 < n_splits; s0 += kMergeBatch) {
-    float pm[kMergeBatch], pl[kMergeBatch];
-    f32x4 po[kMergeBatch];
+  for (int s0 = 0; s0 < n_splits; s0 += MB) {
+    float pm[MB], pl[MB];
+    f32x4 po[MB];
 #pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) {
+    for (int i = 0; i < MB; ++i) {
       const int slot = min(s0 + i, n_splits - 1) * slot_step + slot0;
       const f32x2 ml = load_coherent(a.part_ml + (uint32_t)(slot * 2));
-      const f32x2 o01 = load_coherent(a.part_o + (uint32_t)(slot * kHeadDim + d0));
-      const f32x2 o23 = load_coherent(a.part_o + (uint32_t)(slot * kHeadDim + d0 + 2));
+      po[i] = load_coherent4(a.part_o, (uint32_t)(slot * kHeadDim + d0));
       pm[i] = ml[0];
       pl[i] = ml[1];
-      po[i] = (f32x4){o01[0], o01[1], o23[0], o23[1]};
     }
     float mb = M;
 #pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i)
+    for (int i = 0; i < MB; ++i)
       if (s0 + i < n_splits) mb = fmaxf(mb, pm[i]);
     if (mb == -INFINITY) continue;  // no admitted key so far
     const float s = M == -INFINITY ? 0.0f : exp2_fast(M - mb);
@@ -371,7 +380,7 @@ __device__ __forceinline__ void verify_unit(const Args& a, int split, int head, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) sum[j] *= s;
 #pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) {
+    for (int i = 0; i < MB; ++i) {
       // 0 for a split with no admitted key (m = -inf) and for indices past the last split.
       const float wt = s0 + i < n_splits ? exp2_fast(pm[i] - mb) : 0.0f;
       L += pl[i] * wt;
