@@ -112,10 +112,11 @@ def test_linear_q8(torch, rows, k, n, act, res):
     check(y.float().cpu().numpy(), ref, "y")
 
 
-def run_layer(torch, layer, trial, kind, q8, frames=1500):
+def run_layer(torch, layer, trial, kind, q8, frames=1500, n_kv=None):
     from whisper_asr_encoder_amd.encoder import DecoderVerifier
     w = I.decoder_layer_weights(layer)
-    case = I.verify_self_case(trial, layer) if kind == "causal" else I.verify_tree_case(trial, layer)
+    case = (I.verify_self_case(trial, layer, n_kv=n_kv) if kind == "causal"
+            else I.verify_tree_case(trial, layer, n_kv=n_kv))
     n_q, nk = case.q.shape[0], case.n_kv
     slots = list(range(nk - n_q, nk)) if kind == "causal" else [int(s) for s in case.query_slots]
     cap = nk + 8
@@ -138,16 +139,19 @@ def run_layer(torch, layer, trial, kind, q8, frames=1500):
     return w, x, slots, kc, vc, nk, case.mask, ck16, cv16, y.float().cpu().numpy(), k_d.float().cpu().numpy()
 
 
-@pytest.mark.parametrize("trial,layer,kind,frames", [(0, 0, "causal", 1500), (3, 31, "causal", 1500),
-                                                    (1, 5, "tree", 1500), (2, 11, "causal", 300)])
-def test_decoder_layer_q8(torch, trial, layer, kind, frames):
-    say(f"Q8 decoder verification layer trial {trial} layer {layer} {kind}, {frames} frames")
-    w, x, slots, kc, vc, nk, mask, ck16, cv16, y, kd = run_layer(torch, layer, trial, kind, q8=True, frames=frames)
+@pytest.mark.parametrize("trial,layer,kind,frames,n_kv", [(0, 0, "causal", 1500, None), (3, 31, "causal", 1500, None),
+                                                         (1, 5, "tree", 1500, None), (2, 11, "causal", 300, None),
+                                                         (4, 2, "causal", 1500, 600)])
+def test_decoder_layer_q8(torch, trial, layer, kind, frames, n_kv):
+    """Caches up to 512 keys take the single-launch layer, a 600-key cache the eight launches."""
+    say(f"Q8 decoder verification layer trial {trial} layer {layer} {kind}, {frames} frames, n_kv {n_kv}")
+    w, x, slots, kc, vc, nk, mask, ck16, cv16, y, kd = run_layer(torch, layer, trial, kind, q8=True, frames=frames,
+                                                                 n_kv=n_kv)
     wq = Q.DequantizedDecoderWeights(w, Q.quantize_decoder_weights(w))
     ref = DL.decoder_verify_layer(x, wq, slots, kc, vc, nk, mask, ck16, cv16)
     check(y, ref["y"], "y")
     check(kd[slots], ref["k_cache"][slots], "appended K rows")
-    y16 = run_layer(torch, layer, trial, kind, q8=False, frames=frames)[9]
+    y16 = run_layer(torch, layer, trial, kind, q8=False, frames=frames, n_kv=n_kv)[9]
     rel = np.linalg.norm(y - y16) / np.linalg.norm(y16)
     say(f"  Q8 vs fp16 weights: y relative Frobenius distance {rel:.3e} (weight quantization)")
     assert rel < 2e-2

@@ -507,7 +507,7 @@ edda_status decoder_layer(const char* fn, const void* x, int32_t n_q, const int3
     snprintf(msg, sizeof msg, "%s " what " launch", fn); \
     return from_hip(e, msg);              \
   }
-  if (!q8 && edda::decoder_fused_supported(n_q, n_kv, n_frames)) {
+  if (edda::decoder_fused_supported(n_q, n_kv, n_frames)) {
     // One launch: the eight steps below as work items of persistent workgroups.
     edda::DecoderFusedParams p{};
     p.x = x, p.y = y, p.n_q = n_q, p.slots = sl, p.k_cache = k_cache, p.v_cache = v_cache, p.n_kv = n_kv;
@@ -516,6 +516,8 @@ edda_status decoder_layer(const char* fn, const void* x, int32_t n_q, const int3
                          wt->ln2_gamma, wt->ln2_beta, wt->q_cross.w,   wt->b_q_cross,  wt->o_cross.w,  wt->b_o_cross,
                          wt->ln3_gamma, wt->ln3_beta, wt->fc1.w,       wt->b_fc1,      wt->fc2.w,      wt->b_fc2};
     for (int i = 0; i < 18; ++i) p.w[i] = w[i];
+    const Mat* m6[6] = {&wt->qkv, &wt->o, &wt->q_cross, &wt->o_cross, &wt->fc1, &wt->fc2};
+    for (int i = 0; i < 6; ++i) p.scales[i] = q8 ? m6[i]->scales : nullptr;
     p.qkv = qkv, p.o = o, p.x1 = x1, p.qc = ws + L.qc, p.h = h, p.x2 = x2, p.f = f;
     p.verify_counters = ws, p.ctl = ws + kFusedCtlOffset, p.flags = ws + kFusedFlagOffset, p.part = sk_part;
     p.workgroups = kFusedWorkgroups;

@@ -148,6 +148,8 @@ struct FusedArgs {
   const f16 *ln1_g, *ln1_b, *w_qkv, *b_qkv, *w_o, *b_o;
   const f16 *ln2_g, *ln2_b, *w_qc, *b_qc, *w_oc, *b_oc;
   const f16 *ln3_g, *ln3_b, *w_fc1, *b_fc1, *w_fc2, *b_fc2;
+  // Q8_0 scales of w_qkv, w_o, w_qc, w_oc, w_fc1, w_fc2 (the w_* then hold codes), or null
+  const f16* scales[6];
   // workspace
   f16 *qkv, *o, *x1, *qc, *h, *x2, *f;
   uint32_t* verify_counters;
@@ -160,7 +162,8 @@ struct FusedArgs {
 
 // The operands of one block GEMM: C[M, N] = act(A W^T + bias) + residual.
 struct GemmOp {
-  const f16* w;  // [N][K]
+  const void* w;       // fp16 [N][K], or Q8_0 int8 codes [N][K]
+  const f16* scales;   // null, or the Q8_0 scales fp16 [K / 32][N]
   const f16* bias;
   const f16* a;  // [M][K] operand rows, or the LayerNorm's input rows
   const f16* gamma;
@@ -179,7 +182,8 @@ struct GemmSmem {
 // One block-GEMM item: NB column blocks of 16 (C[:, n0 .. n0 + 16 NB)) over the whole K = 256 NU
 // (wave w takes the 32-deep steps w, w + 8, ...).  A_FRESH / RES_FRESH: the operand rows / the
 // residual were written in this launch (coherent loads after the wait).  A_FRAG / C_FRAG: A is
-// read, C written, in fragment order (C_FRAG: no residual, no append).  (A_FRESH only decides
+// read, C written, in fragment order (C_FRAG: no residual, no append).  Q8: the weights are
+// Q8_0 codes and scales, each step's dot products scaled in fp32 as in kernel 6.  (A_FRESH only decides
 // whether the LayerNorm rows are loaded before or after the wait.)  Per block the arithmetic is kernel 6's (same fragments,
 // same summation order over steps and waves).
 // Fragment order of a [16][K] operand consumed by the block GEMMs: for each 32-deep step s, the
@@ -190,7 +194,8 @@ __device__ __forceinline__ uint32_t frag_index(int m, int k) {
   return (uint32_t)((((k >> 5) * 4 + ((k >> 3) & 3)) * 16 + m) * 8 + (k & 7));
 }
 
-template <int NB, int NU, int ACT, bool LN, bool A_FRESH, bool A_FRAG, bool RES_FRESH, bool APPEND, bool C_FRAG>
+template <int NB, int NU, int ACT, bool LN, bool A_FRESH, bool A_FRAG, bool RES_FRESH, bool APPEND, bool C_FRAG,
+          bool Q8>
 __device__ __forceinline__ void gemm_item(const FusedArgs& fa, const GemmOp& op, int item, const StepWait& wait,
                                           GemmSmem& sm, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
@@ -219,12 +224,26 @@ __device__ __forceinline__ void gemm_item(const FusedArgs& fa, const GemmOp& op,
     }
   }
   // Weight fragments: row n0 + 16 b + r16, 8 consecutive k of each step.
-  f16x8 wf[NB][NU];
+  // Q8: 8 bytes of codes of the same row and k, and the scales of the lane's four output
+  // columns n0 + 16 b + 4 g + r at the step.
+  using WFrag = std::conditional_t<Q8, u32x2, f16x8>;
+  WFrag wf[NB][NU];
+  f16x4 wd[Q8 ? NB : 1][Q8 ? NU : 1];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const f16* wrow = op.w + (size_t)(n0 + kFCols * b + r16) * K + 8 * g;
+    const int n = n0 + kFCols * b;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) wf[b][u] = load16(wrow + 32 * (wave + 8 * u));
+    for (int u = 0; u < NU; ++u) {
+      const int st = wave + 8 * u;
+      if constexpr (Q8) {
+        const int8_t* crow = static_cast<const int8_t*>(op.w) + (size_t)(n + r16) * K + 8 * g;
+        wf[b][u] = *reinterpret_cast<const u32x2*>(crow + 32 * st);
+        wd[b][u] = *reinterpret_cast<const f16x4*>(op.scales + (size_t)st * N + n + 4 * g);
+      } else {
+        const f16* wrow = static_cast<const f16*>(op.w) + (size_t)(n + r16) * K + 8 * g;
+        wf[b][u] = load16(wrow + 32 * st);
+      }
+    }
   }
   // Epilogue thread: block eb, row em, columns en, en + 1 of the block.
   const int eb = tid >> 7, em = (tid >> 3) & 15, en = 2 * (tid & 7);
@@ -292,7 +311,15 @@ __device__ __forceinline__ void gemm_item(const FusedArgs& fa, const GemmOp& op,
   for (int b = 0; b < NB; ++b) {
     f32x4 acc = {};
 #pragma unroll
-    for (int u = 0; u < NU; ++u) acc = mfma_16x16x32(wf[b][u], xf[u], acc);
+    for (int u = 0; u < NU; ++u) {
+      if constexpr (Q8) {
+        const f32x4 t = mfma_16x16x32(codes_to_f16(wf[b][u]), xf[u], (f32x4){});
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = fmaf((float)wd[b][u][r], t[r], acc[r]);
+      } else {
+        acc = mfma_16x16x32(wf[b][u], xf[u], acc);
+      }
+    }
     // acc[r] = C^T[n = 16 b + 4 g + r][m = r16] over this wave's steps.
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.red[wave][kFCols * b + 4 * g + r][r16] = acc[r];
@@ -368,8 +395,8 @@ constexpr size_t kArenaBytes =
     cmax(cmax(sizeof(vcore::Smem<CPW, kFWaves>), sizeof(vcore::Smem<1, kFWaves>)), sizeof(GemmSmem));
 
 // SELF_CPW: 32-key chunks per wave of the self-attention (1: n_kv <= 256, 2: <= 512).
-// SELF_MODE: vcore::kMaskRows or kMaskNone.
-template <int SELF_CPW, int SELF_MODE>
+// SELF_MODE: vcore::kMaskRows or kMaskNone.  Q8: Q8_0 projection weights.
+template <int SELF_CPW, int SELF_MODE, bool Q8>
 __global__ __launch_bounds__(kFThreads) void decoder_layer_kernel(FusedArgs fa) {
   __shared__ __attribute__((aligned(16))) unsigned char arena[kArenaBytes<SELF_CPW>];
   __shared__ int8_t fresh_row[2 * kFWaves * vcore::kWaveKeys];
@@ -397,8 +424,8 @@ __global__ __launch_bounds__(kFThreads) void decoder_layer_kernel(FusedArgs fa) 
     GemmSmem& gs = *reinterpret_cast<GemmSmem*>(arena);
     switch (p) {
       case 0:
-        gemm_item<2, 5, 0, true, false, false, false, true, false>(
-            fa, GemmOp{fa.w_qkv, fa.b_qkv, fa.x, fa.ln1_g, fa.ln1_b, nullptr, fa.qkv, kQkvCols, kDModel}, local, wait,
+        gemm_item<2, 5, 0, true, false, false, false, true, false, Q8>(
+            fa, GemmOp{fa.w_qkv, fa.scales[0], fa.b_qkv, fa.x, fa.ln1_g, fa.ln1_b, nullptr, fa.qkv, kQkvCols, kDModel}, local, wait,
             gs, tid);
         break;
       case 1: {
@@ -414,12 +441,12 @@ __global__ __launch_bounds__(kFThreads) void decoder_layer_kernel(FusedArgs fa) 
         break;
       }
       case 2:
-        gemm_item<1, 5, 0, false, true, true, false, false, false>(
-            fa, GemmOp{fa.w_o, fa.b_o, fa.o, nullptr, nullptr, fa.x, fa.x1, kDModel, kDModel}, local, wait, gs, tid);
+        gemm_item<1, 5, 0, false, true, true, false, false, false, Q8>(
+            fa, GemmOp{fa.w_o, fa.scales[1], fa.b_o, fa.o, nullptr, nullptr, fa.x, fa.x1, kDModel, kDModel}, local, wait, gs, tid);
         break;
       case 3:
-        gemm_item<1, 5, 0, true, true, false, false, false, false>(
-            fa, GemmOp{fa.w_qc, fa.b_qc, fa.x1, fa.ln2_g, fa.ln2_b, nullptr, fa.qc, kDModel, kDModel}, local, wait, gs,
+        gemm_item<1, 5, 0, true, true, false, false, false, false, Q8>(
+            fa, GemmOp{fa.w_qc, fa.scales[2], fa.b_qc, fa.x1, fa.ln2_g, fa.ln2_b, nullptr, fa.qc, kDModel, kDModel}, local, wait, gs,
             tid);
         break;
       case 4: {
@@ -433,17 +460,17 @@ __global__ __launch_bounds__(kFThreads) void decoder_layer_kernel(FusedArgs fa) 
         break;
       }
       case 5:
-        gemm_item<1, 5, 0, false, true, true, true, false, false>(
-            fa, GemmOp{fa.w_oc, fa.b_oc, fa.h, nullptr, nullptr, fa.x1, fa.x2, kDModel, kDModel}, local, wait, gs, tid);
+        gemm_item<1, 5, 0, false, true, true, true, false, false, Q8>(
+            fa, GemmOp{fa.w_oc, fa.scales[3], fa.b_oc, fa.h, nullptr, nullptr, fa.x1, fa.x2, kDModel, kDModel}, local, wait, gs, tid);
         break;
       case 6:
-        gemm_item<4, 5, 1, true, true, false, false, false, true>(
-            fa, GemmOp{fa.w_fc1, fa.b_fc1, fa.x2, fa.ln3_g, fa.ln3_b, nullptr, fa.f, 4 * kDModel, kDModel}, local,
+        gemm_item<4, 5, 1, true, true, false, false, false, true, Q8>(
+            fa, GemmOp{fa.w_fc1, fa.scales[4], fa.b_fc1, fa.x2, fa.ln3_g, fa.ln3_b, nullptr, fa.f, 4 * kDModel, kDModel}, local,
             wait, gs, tid);
         break;
       default:
-        gemm_item<1, 20, 0, false, true, true, true, false, false>(
-            fa, GemmOp{fa.w_fc2, fa.b_fc2, fa.f, nullptr, nullptr, fa.x2, fa.y, kDModel, 4 * kDModel}, local, wait, gs,
+        gemm_item<1, 20, 0, false, true, true, true, false, false, Q8>(
+            fa, GemmOp{fa.w_fc2, fa.scales[5], fa.b_fc2, fa.f, nullptr, nullptr, fa.x2, fa.y, kDModel, 4 * kDModel}, local, wait, gs,
             tid);
         break;
     }
@@ -519,14 +546,18 @@ hipError_t launch_decoder_layer_fused(const DecoderFusedParams& p, hipStream_t s
   int run = 0;
   for (int i = 0; i < kSteps; ++i) fa.step_end[i] = (run += counts[i]);
   if (run != decoder_fused_items(p.n_frames)) return hipErrorInvalidValue;
+  for (int i = 0; i < 6; ++i) fa.scales[i] = static_cast<const f16*>(p.scales[i]);
+  const bool q8 = p.scales[0] != nullptr;
   const dim3 grid(p.workgroups), block(kFThreads);
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, fa); };
   const bool rows = p.mask != nullptr;
-  if (p.n_kv <= kFWaves * vcore::kWaveKeys) {
-    if (rows) hipLaunchKernelGGL((decoder_layer_kernel<1, vcore::kMaskRows>), grid, block, 0, stream, fa);
-    else hipLaunchKernelGGL((decoder_layer_kernel<1, vcore::kMaskNone>), grid, block, 0, stream, fa);
+  const bool one_chunk = p.n_kv <= kFWaves * vcore::kWaveKeys;
+  if (q8) {
+    if (one_chunk) rows ? go(decoder_layer_kernel<1, vcore::kMaskRows, true>) : go(decoder_layer_kernel<1, vcore::kMaskNone, true>);
+    else rows ? go(decoder_layer_kernel<2, vcore::kMaskRows, true>) : go(decoder_layer_kernel<2, vcore::kMaskNone, true>);
   } else {
-    if (rows) hipLaunchKernelGGL((decoder_layer_kernel<2, vcore::kMaskRows>), grid, block, 0, stream, fa);
-    else hipLaunchKernelGGL((decoder_layer_kernel<2, vcore::kMaskNone>), grid, block, 0, stream, fa);
+    if (one_chunk) rows ? go(decoder_layer_kernel<1, vcore::kMaskRows, false>) : go(decoder_layer_kernel<1, vcore::kMaskNone, false>);
+    else rows ? go(decoder_layer_kernel<2, vcore::kMaskRows, false>) : go(decoder_layer_kernel<2, vcore::kMaskNone, false>);
   }
   return hipGetLastError();
 }

@@ -48,6 +48,17 @@ __device__ __forceinline__ f16x8 pack8(float a0, float a1, float a2, float a3, f
 __device__ __forceinline__ f16x8 load16(const f16* p) { return *reinterpret_cast<const f16x8*>(p); }
 __device__ __forceinline__ void store16(f16* p, f16x8 v) { *reinterpret_cast<f16x8*>(p) = v; }
 
+// Eight int8 Q8_0 codes (little-endian bytes of q) as fp16 values (exact: |code| <= 127).
+__device__ __forceinline__ f16x8 codes_to_f16(u32x2 q) {
+  f16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[j] = (f16)(float)(int8_t)(q[0] >> (8 * j));
+    r[4 + j] = (f16)(float)(int8_t)(q[1] >> (8 * j));
+  }
+  return r;
+}
+
 // 2^x on the transcendental unit (v_exp_f32); x <= 0 here, tiny results flush to 0.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -80,7 +80,7 @@ hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, co
                          hipStream_t stream);
 
 // The decoder's verification layer in one launch of `workgroups` persistent workgroups
-// (kernel 8, fp16 weights, n_kv <= 512).  w: ln1_gamma, ln1_beta, w_qkv, b_qkv, w_o, b_o,
+// (kernel 8, fp16 or Q8_0 projection weights, n_kv <= 512).  w: ln1_gamma, ln1_beta, w_qkv, b_qkv, w_o, b_o,
 // ln2_gamma, ln2_beta, w_q_cross, b_q_cross, w_o_cross, b_o_cross, ln3_gamma, ln3_beta, w_fc1,
 // b_fc1, w_fc2, b_fc2 (biases may be null).  qkv .. f: workspace rows ([16][3840], [16][1280]
 // x5, [16][5120]), no two aliased.  verify_counters: 20 per-head counters 256 bytes apart;
@@ -99,6 +99,7 @@ struct DecoderFusedParams {
   const void* cross_v;
   int n_frames;
   const void* w[18];
+  const void* scales[6];  // Q8_0 scales of w_qkv, w_o, w_q_cross, w_o_cross, w_fc1, w_fc2 (w: codes), or all null
   void *qkv, *o, *x1, *qc, *h, *x2, *f;
   void* verify_counters;
   void* ctl;

@@ -87,16 +87,6 @@ struct WFragQ8 {
   f16x4 d;
 };
 
-__device__ __forceinline__ f16x8 codes_to_f16(u32x2 q) {
-  f16x8 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    r[j] = (f16)(float)(int8_t)(q[0] >> (8 * j));
-    r[4 + j] = (f16)(float)(int8_t)(q[1] >> (8 * j));
-  }
-  return r;
-}
-
 template <int ACT, bool RES, bool LN, bool APPEND, bool SPLIT, bool Q8>
 __global__ __launch_bounds__(kSkThreads) void skinny_gemm_kernel(const f16* __restrict__ A,
                                                                  const void* __restrict__ Bt,
