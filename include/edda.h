@@ -368,6 +368,43 @@ edda_status edda_decoder_verify_layer(const void* x, int32_t n_q, const int32_t*
 /* Bytes of workspace edda_decoder_verify_layer needs (0 if the shape is invalid). */
 size_t edda_decoder_verify_workspace_bytes(int32_t n_q, int32_t n_kv, int32_t n_frames);
 
+/* One layer of a stack: its weights, its self-attention caches and its cross K/V. */
+typedef struct {
+  edda_decoder_layer_weights weights;
+  void* k_cache;        /* [cache_slots, 20, 64] fp16 */
+  void* v_cache;
+  const void* cross_k;  /* [n_frames, 20, 64] fp16 */
+  const void* cross_v;
+} edda_decoder_stack_layer;
+
+/* Largest cache edda_decoder_verify_stack serves (every Whisper self-attention cache: the
+ * decoder context is 448 tokens). */
+#define EDDA_DECODER_STACK_MAX_KV 512
+/* Leading bytes of its workspace that must be zero before first use (each call leaves them so). */
+#define EDDA_DECODER_STACK_ZERO_BYTES 40960
+
+/*
+ * n_layers consecutive decoder layers over one block (layer l's y is layer l + 1's x; y is the
+ * last layer's output), each as edda_decoder_verify_layer with the same slots, n_kv, mask_rows
+ * and n_frames, in ceil(n_layers / 8) launches (each layer's weights stream in while the layer
+ * before it runs). Results are bit-identical to calling edda_decoder_verify_layer layer by layer
+ * (for n_kv <= EDDA_DECODER_STACK_MAX_KV that entry point takes the same one-launch kernel).
+ *  layers      HOST array of n_layers >= 1 layers (pointers device, 16-byte aligned).
+ *  x, y        [n_q, 1280] fp16 (y may equal x).
+ *  workspace   at least edda_decoder_verify_stack_workspace_bytes(n_q, n_kv, n_frames) bytes,
+ *              256-byte aligned, whose first EDDA_DECODER_STACK_ZERO_BYTES bytes are zero before
+ *              its first use; calls sharing it must not overlap.
+ * Other arguments and errors as for edda_decoder_verify_layer; EDDA_ERR_UNSUPPORTED for n_kv
+ * above EDDA_DECODER_STACK_MAX_KV or n_frames above 6144 (the kernel's work-item budget).
+ */
+edda_status edda_decoder_verify_stack(const void* x, int32_t n_q, const int32_t* slots, int32_t cache_slots,
+                                      int32_t n_kv, const uint32_t* mask_rows, int32_t n_frames,
+                                      const edda_decoder_stack_layer* layers, int32_t n_layers, void* y,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace edda_decoder_verify_stack needs (0 if the shape is invalid or unsupported). */
+size_t edda_decoder_verify_stack_workspace_bytes(int32_t n_q, int32_t n_kv, int32_t n_frames);
+
 /* ------------------------------------------------------------------------------------
  * Q8_0 decoder weights ("audio.cpp PR #1223", PR description and results table: the decoder
  * runs with Q8_0 weights beside an F16 encoder). The pages name the format only; it is read

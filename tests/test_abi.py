@@ -279,6 +279,48 @@ def test_decoder_verify_layer_rejects(lib, kw, status):
     assert dec(lib, **kw) == status
 
 
+def stack(lib, x=A, n_q=16, slots=tuple(range(24, 40)), cap=448, n_kv=40, mask=None, frames=1500, n_layers=3,
+          lover=None, wover=None, y=B, ws=B + (1 << 24), ws_bytes=1 << 30, layers="default"):
+    arr = (_lib.DecoderStackLayer * max(n_layers, 1))()
+    for l in range(max(n_layers, 1)):
+        arr[l] = _lib.DecoderStackLayer(_lib.DecoderLayerWeights(*([A] * 18)), A, A, A, A)
+    for k, v in (wover or {}).items():
+        setattr(arr[n_layers - 1].weights, k, v)
+    for k, v in (lover or {}).items():
+        setattr(arr[n_layers - 1], k, v)
+    sl = None
+    if slots is not None:
+        sl = ctypes.cast((ctypes.c_int32 * max(len(slots), 1))(*slots), ctypes.POINTER(ctypes.c_int32))
+    return lib.edda_decoder_verify_stack(x, n_q, sl, cap, n_kv, mask, frames, arr if layers == "default" else layers,
+                                         n_layers, y, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID), (dict(slots=None), INVALID), (dict(layers=None), INVALID), (dict(y=None), INVALID),
+    (dict(n_layers=0), INVALID), (dict(n_q=17, slots=tuple(range(17))), INVALID), (dict(n_kv=500), INVALID),
+    (dict(frames=0), INVALID), (dict(n_q=2, slots=(5, 5)), INVALID), (dict(n_q=2, slots=(3, 40)), INVALID),
+    (dict(cap=600, n_kv=513), UNSUPPORTED), (dict(frames=6145), UNSUPPORTED),
+    (dict(wover=dict(w_fc1=None)), INVALID), (dict(lover=dict(cross_v=None)), INVALID),
+    (dict(lover=dict(k_cache=None)), INVALID), (dict(wover=dict(b_fc2=ODD)), MISALIGNED),
+    (dict(lover=dict(v_cache=ODD)), MISALIGNED), (dict(ws=B + 16), MISALIGNED), (dict(x=ODD), MISALIGNED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=1 << 20), WORKSPACE),
+])
+def test_decoder_verify_stack_rejects(lib, kw, status):
+    assert stack(lib, **kw) == status
+    assert lib.edda_last_error()
+
+
+def test_decoder_stack_workspace_bytes(lib):
+    n = lib.edda_decoder_verify_stack_workspace_bytes(16, 448, 1500)
+    # zeroed counters and flags, cross partials (3 splits of 512 frames), carry rows, 8 blocks of
+    # per-layer rows
+    block = 16 * 2 * (3840 + 6 * 1280 + 5120)
+    assert n == _lib.DECODER_STACK_ZERO_BYTES + 3 * 16 * 20 * 66 * 4 + 16 * 1280 * 2 + 8 * block
+    assert lib.edda_decoder_verify_stack_workspace_bytes(16, 513, 1500) == 0
+    assert lib.edda_decoder_verify_stack_workspace_bytes(17, 448, 1500) == 0
+    assert lib.edda_decoder_verify_stack_workspace_bytes(1, 448, 6145) == 0
+
+
 @pytest.mark.parametrize("args,status", [
     ((None, 1500, A, A, None, B, B), INVALID), ((A, 0, A, A, None, B, B), INVALID),
     ((A, 1500, A, None, None, B, B), INVALID), ((A, 1500, A, A, ODD, B, B), MISALIGNED),

@@ -290,3 +290,69 @@ def test_decoder_layer_matches_composition_of_public_entries(torch, trial, layer
     torch.cuda.synchronize()
     assert torch.equal(k_f, k_c) and torch.equal(v_f, v_c), "cache contents differ"
     check(host(y_f), host(y_c).astype(np.float64), "y, fused vs composed")
+
+
+@pytest.mark.parametrize("n_layers,kind,in_place", [(4, "causal", False), (10, "tree", True)])
+def test_decoder_stack_matches_layer_by_layer(torch, n_layers, kind, in_place):
+    """edda_decoder_verify_stack (several layers per launch: 4 in one launch, 10 in two) against
+    edda_decoder_verify_layer called layer by layer: y and every layer's caches bit for bit.
+    The per-layer entry point is held to the oracle by the tests above; the first layers of the
+    stack are also checked against the oracle chain here."""
+    from whisper_asr_encoder_amd.encoder import DecoderVerifier
+    say(f"decoder stack of {n_layers} layers ({kind}{', y = x' if in_place else ''}) vs layer by layer")
+    weights = [I.decoder_layer_weights(l) for l in range(n_layers)]
+    cases = [I.verify_self_case(1, l) if kind == "causal" else I.verify_tree_case(1, l) for l in range(n_layers)]
+    n_q, nk = cases[0].q.shape[0], cases[0].n_kv
+    slots = list(range(nk - n_q, nk)) if kind == "causal" else [int(s) for s in cases[0].query_slots]
+    cap = nk + 4
+    dv = DecoderVerifier(weights, max_kv=cap)
+    enc = I.encoder_workload(1, layers=1).x
+    cross = [DL.cross_kv(enc, w.w_ck, w.w_cv, w.b_cv) for w in weights[:2]]
+    dv.set_encoder_output(dev(torch, enc))
+    for l in range(2):  # the oracle's own cross K/V (fp16) for the layers checked against it
+        dv.cross_k[l].copy_(dev(torch, cross[l][0].astype(np.float16)))
+        dv.cross_v[l].copy_(dev(torch, cross[l][1].astype(np.float16)))
+    host_caches = []
+    for c in cases:
+        kc = np.zeros((cap, 20, 64), dtype=np.float16)
+        vc = np.zeros((cap, 20, 64), dtype=np.float16)
+        kc[:nk], vc[:nk] = c.k, c.v
+        host_caches.append((kc, vc))
+    mask = VerifyRows(torch, cases[0].mask)
+    x0 = I.decoder_block_input(1, n_q)
+    # Layer by layer.
+    caches_a = [(dev(torch, k), dev(torch, v)) for k, v in host_caches]
+    xa = dev(torch, x0)
+    ya = torch.empty_like(xa)
+    cur = xa
+    for l in range(n_layers):
+        dv.layer(cur, l, slots, caches_a[l][0], caches_a[l][1], nk, mask, ya)
+        cur = ya
+    # The stack.
+    caches_b = [(dev(torch, k), dev(torch, v)) for k, v in host_caches]
+    xb = dev(torch, x0)
+    yb = xb if in_place else torch.full_like(xb, float("nan"))
+    dv.stack(xb, slots, caches_b, nk, mask, yb)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yb), "stack output differs from layer-by-layer"
+    for l in range(n_layers):
+        assert torch.equal(caches_a[l][0], caches_b[l][0]) and torch.equal(caches_a[l][1], caches_b[l][1]), \
+            f"layer {l} caches differ"
+    assert not dv.stack_workspace[:_lib.DECODER_STACK_ZERO_BYTES].any().item(), "counters or flags not cleared"
+    # The first two layers of the stack against the oracle chain.
+    dv2 = DecoderVerifier(weights[:2], max_kv=cap)
+    for l in range(2):
+        dv2.cross_k[l].copy_(dv.cross_k[l])
+        dv2.cross_v[l].copy_(dv.cross_v[l])
+    caches_c = [(dev(torch, k), dev(torch, v)) for k, v in host_caches[:2]]
+    yc = torch.empty_like(xb)
+    dv2.stack(dev(torch, x0), slots, caches_c, nk, mask, yc)
+    torch.cuda.synchronize()
+    ref_x = x0
+    for l in range(2):
+        kc, vc = host_caches[l]
+        ck, cv = cross[l]
+        ref = DL.decoder_verify_layer(ref_x, weights[l], slots, kc, vc, nk, cases[0].mask, ck.astype(np.float16),
+                                      cv.astype(np.float16))
+        ref_x = ref["y"]
+    check(host(yc), ref_x, "y after two layers")

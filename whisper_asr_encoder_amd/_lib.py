@@ -25,6 +25,8 @@ QKV_COLS = 3 * D_MODEL
 MAX_VERIFY_QUERIES = 16
 NOALLOC_MAX_KV = 8192  # most keys edda_verify_attn_noalloc takes (its static scratch)
 VERIFY_COUNTER_BYTES = 16384  # leading workspace bytes of edda_verify_attn: zero before first use
+DECODER_STACK_MAX_KV = 512  # largest cache edda_decoder_verify_stack serves
+DECODER_STACK_ZERO_BYTES = 40960  # leading bytes of its workspace: zero before first use
 
 STATUS = {0: "EDDA_OK", 1: "EDDA_ERR_INVALID_ARGUMENT", 2: "EDDA_ERR_UNSUPPORTED",
           3: "EDDA_ERR_MISALIGNED", 4: "EDDA_ERR_WORKSPACE", 5: "EDDA_ERR_HIP"}
@@ -37,6 +39,7 @@ EXPORTS = ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_encode
            "edda_decoder_verify_layer", "edda_decoder_verify_workspace_bytes", "edda_cross_kv",
            "edda_verify_attn_ex", "edda_verify_workspace_bytes_ex",
            "edda_quantize_q8_0", "edda_linear_q8", "edda_decoder_verify_layer_q8",
+           "edda_decoder_verify_stack", "edda_decoder_verify_stack_workspace_bytes",
            "edda_last_error", "edda_version")
 
 D_FF = 5120
@@ -67,6 +70,12 @@ class DecoderLayerWeightsQ8(ctypes.Structure):
     _fields_ = [(name, Q8Matrix if name.startswith("w_") else ctypes.c_void_p) for name in (
         "ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_gamma", "ln2_beta", "w_q_cross",
         "b_q_cross", "w_o_cross", "b_o_cross", "ln3_gamma", "ln3_beta", "w_fc1", "b_fc1", "w_fc2", "b_fc2")]
+
+
+class DecoderStackLayer(ctypes.Structure):
+    """edda_decoder_stack_layer: a layer's weights, its caches and its cross K/V (device)."""
+    _fields_ = [("weights", DecoderLayerWeights), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("cross_k", ctypes.c_void_p), ("cross_v", ctypes.c_void_p)]
 
 
 class EddaError(RuntimeError):
@@ -110,6 +119,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                               ctypes.POINTER(DecoderLayerWeights), vp, vp, sz, vp]
     lib.edda_decoder_verify_layer_q8.argtypes = [vp, i32, ctypes.POINTER(i32), vp, vp, i32, i32, vp, vp, vp, i32,
                                                  ctypes.POINTER(DecoderLayerWeightsQ8), vp, vp, sz, vp]
+    lib.edda_decoder_verify_stack.argtypes = [vp, i32, ctypes.POINTER(i32), i32, i32, vp, i32,
+                                              ctypes.POINTER(DecoderStackLayer), i32, vp, vp, sz, vp]
+    lib.edda_decoder_verify_stack_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.edda_decoder_verify_stack_workspace_bytes.restype = sz
     lib.edda_quantize_q8_0.argtypes = [vp, i32, i32, vp, vp, vp]
     lib.edda_linear_q8.argtypes = [vp, ctypes.c_int64, i32, vp, vp, i32, vp, i32, vp, ctypes.c_int64, vp, vp]
     lib.edda_decoder_verify_workspace_bytes.argtypes = [i32, i32, i32]
@@ -124,7 +137,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                  "edda_linear",
                  "edda_layer_norm", "edda_encoder_layer", "edda_encoder_stem", "edda_decoder_verify_layer",
                  "edda_cross_kv", "edda_verify_attn_ex", "edda_quantize_q8_0", "edda_linear_q8",
-                 "edda_decoder_verify_layer_q8"):
+                 "edda_decoder_verify_layer_q8", "edda_decoder_verify_stack"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -393,6 +406,28 @@ def edda_decoder_verify_layer(x, slots, k_cache, v_cache, n_kv, mask_rows, cross
     _check(fn(_ptr(x), n_q, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), _ptr(k_cache), _ptr(v_cache),
               cache_slots, n_kv, _ptr(mask_rows), _ptr(cross_k), _ptr(cross_v), n_frames, ctypes.byref(weights),
               _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def decoder_verify_stack_workspace_bytes(n_q: int, n_kv: int, n_frames: int) -> int:
+    return int(load().edda_decoder_verify_stack_workspace_bytes(n_q, n_kv, n_frames))
+
+
+def edda_decoder_verify_stack(x, slots, cache_slots, n_kv, mask_rows, n_frames, layers, y, workspace, stream=None):
+    """Consecutive decoder layers over the block rows x [n_q, 1280] into y; layers: a ctypes
+    array of DecoderStackLayer (weights, caches [cache_slots, 20, 64] updated in place, cross
+    K/V [n_frames, 20, 64]); slots host ints; mask_rows as for edda_verify_attn (or None)."""
+    lib = load()
+    torch = _require(x, "x")
+    n_q = x.shape[0]
+    _require(x, "x", (n_q, D_MODEL), torch.float16)
+    _require(y, "y", (n_q, D_MODEL), torch.float16)
+    if mask_rows is not None:
+        _require(mask_rows, "mask_rows", (n_q, (n_kv + 31) // 32))
+    arr = (ctypes.c_int32 * n_q)(*[int(v) for v in slots])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.edda_decoder_verify_stack(_ptr(x), n_q, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), cache_slots,
+                                         n_kv, _ptr(mask_rows), n_frames, layers, len(layers), _ptr(y),
+                                         _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def edda_cross_kv(enc, w_k, w_v, b_v, cross_k, cross_v, stream=None):

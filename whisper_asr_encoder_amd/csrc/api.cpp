@@ -454,6 +454,18 @@ struct DecoderMats {
   const void* b_fc2;
 };
 
+// One layer's pointers for the single-launch layer kernel.
+void fused_layer_ptrs(const DecoderMats& wt, bool q8, void* k_cache, void* v_cache, const void* cross_k,
+                      const void* cross_v, edda::DecoderFusedLayer* d) {
+  const void* w[18] = {wt.ln1_gamma, wt.ln1_beta, wt.qkv.w,     wt.b_qkv,     wt.o.w,       wt.b_o,
+                       wt.ln2_gamma, wt.ln2_beta, wt.q_cross.w, wt.b_q_cross, wt.o_cross.w, wt.b_o_cross,
+                       wt.ln3_gamma, wt.ln3_beta, wt.fc1.w,     wt.b_fc1,     wt.fc2.w,     wt.b_fc2};
+  for (int i = 0; i < 18; ++i) d->w[i] = w[i];
+  const Mat* m6[6] = {&wt.qkv, &wt.o, &wt.q_cross, &wt.o_cross, &wt.fc1, &wt.fc2};
+  for (int i = 0; i < 6; ++i) d->scales[i] = q8 ? m6[i]->scales : nullptr;
+  d->k_cache = k_cache, d->v_cache = v_cache, d->cross_k = cross_k, d->cross_v = cross_v;
+}
+
 edda_status decoder_layer(const char* fn, const void* x, int32_t n_q, const int32_t* slots, void* k_cache,
                           void* v_cache, int32_t cache_slots, int32_t n_kv, const uint32_t* mask_rows,
                           const void* cross_k, const void* cross_v, int32_t n_frames, const DecoderMats* wt, void* y,
@@ -510,15 +522,13 @@ edda_status decoder_layer(const char* fn, const void* x, int32_t n_q, const int3
   if (edda::decoder_fused_supported(n_q, n_kv, n_frames)) {
     // One launch: the eight steps below as work items of persistent workgroups.
     edda::DecoderFusedParams p{};
-    p.x = x, p.y = y, p.n_q = n_q, p.slots = sl, p.k_cache = k_cache, p.v_cache = v_cache, p.n_kv = n_kv;
-    p.mask = mask_rows, p.cross_k = cross_k, p.cross_v = cross_v, p.n_frames = n_frames;
-    const void* w[18] = {wt->ln1_gamma, wt->ln1_beta, wt->qkv.w,       wt->b_qkv,      wt->o.w,        wt->b_o,
-                         wt->ln2_gamma, wt->ln2_beta, wt->q_cross.w,   wt->b_q_cross,  wt->o_cross.w,  wt->b_o_cross,
-                         wt->ln3_gamma, wt->ln3_beta, wt->fc1.w,       wt->b_fc1,      wt->fc2.w,      wt->b_fc2};
-    for (int i = 0; i < 18; ++i) p.w[i] = w[i];
-    const Mat* m6[6] = {&wt->qkv, &wt->o, &wt->q_cross, &wt->o_cross, &wt->fc1, &wt->fc2};
-    for (int i = 0; i < 6; ++i) p.scales[i] = q8 ? m6[i]->scales : nullptr;
-    p.qkv = qkv, p.o = o, p.x1 = x1, p.qc = ws + L.qc, p.h = h, p.x2 = x2, p.f = f;
+    p.x = x, p.y = y, p.n_q = n_q, p.slots = sl, p.n_kv = n_kv, p.mask = mask_rows, p.n_frames = n_frames;
+    p.n_layers = 1;
+    fused_layer_ptrs(*wt, q8, k_cache, v_cache, cross_k, cross_v, &p.layer[0]);
+    // This workspace's rows as a one-layer block (offsets from its start).
+    p.lws = ws, p.lws_stride = 0;
+    p.off_qkv = (uint32_t)L.qkv, p.off_o = (uint32_t)L.o, p.off_x1 = (uint32_t)L.x1, p.off_qc = (uint32_t)L.qc;
+    p.off_h = (uint32_t)L.h, p.off_x2 = (uint32_t)L.x2, p.off_f = (uint32_t)L.f, p.off_y = 0;  // y: the output
     p.verify_counters = ws, p.ctl = ws + kFusedCtlOffset, p.flags = ws + kFusedFlagOffset, p.part = sk_part;
     p.workgroups = kFusedWorkgroups;
     EDDA_STEP(edda::launch_decoder_layer_fused(p, s), "single-launch layer");
@@ -583,6 +593,138 @@ edda_status edda_decoder_verify_layer_q8(const void* x, int32_t n_q, const int32
                       wt->b_o_cross, wt->ln3_gamma, wt->ln3_beta, M(wt->w_fc1), wt->b_fc1, M(wt->w_fc2), wt->b_fc2};
   return decoder_layer(fn, x, n_q, slots, k_cache, v_cache, cache_slots, n_kv, mask_rows, cross_k, cross_v, n_frames,
                        &m, y, workspace, workspace_bytes, stream, true);
+}
+
+// ---------------------------------------------------------------------------------------
+// Several decoder layers per launch.
+// ---------------------------------------------------------------------------------------
+
+namespace {
+// Workspace of edda_decoder_verify_stack: the counter region (as for one layer: verification
+// counters, then the single-launch kernel's ticket and exit counters), the items' done flags
+// (both zero-initialised, EDDA_DECODER_STACK_ZERO_BYTES), the cross-attention partials, the
+// carry rows between launches, then one block of rows per layer of a launch.
+struct StackWs {
+  size_t part, carry, blocks, block, total;
+  size_t qkv, o, x1, qc, h, x2, f, y;  // offsets within a block
+};
+constexpr size_t kStackFlagOffset = EDDA_VERIFY_COUNTER_BYTES;
+static_assert(kStackFlagOffset + (size_t)edda::kDecoderFusedMaxLayers * edda::kDecoderFusedMaxItems * 4 <=
+                  EDDA_DECODER_STACK_ZERO_BYTES,
+              "stack flags must fit in the zeroed region");
+
+StackWs stack_ws(int32_t n_q, int32_t n_frames) {
+  StackWs w{};
+  const size_t rows = (size_t)EDDA_MAX_VERIFY_QUERIES * 2;  // bytes per feature column of a 16-row block
+  w.part = EDDA_DECODER_STACK_ZERO_BYTES;
+  w.carry = w.part + align256(edda::decoder_fused_part_bytes(n_q, n_frames));
+  w.blocks = w.carry + align256(rows * EDDA_D_MODEL);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t at = off; off += align256(bytes); return at; };
+  w.qkv = take(rows * EDDA_QKV_COLS);
+  w.o = take(rows * EDDA_D_MODEL);
+  w.x1 = take(rows * EDDA_D_MODEL);
+  w.qc = take(rows * EDDA_D_MODEL);
+  w.h = take(rows * EDDA_D_MODEL);
+  w.x2 = take(rows * EDDA_D_MODEL);
+  w.f = take(rows * EDDA_D_FF);
+  w.y = take(rows * EDDA_D_MODEL);
+  w.block = off;
+  w.total = w.blocks + (size_t)edda::kDecoderFusedMaxLayers * w.block;
+  return w;
+}
+}  // namespace
+
+size_t edda_decoder_verify_stack_workspace_bytes(int32_t n_q, int32_t n_kv, int32_t n_frames) {
+  if (n_q < 1 || n_q > EDDA_MAX_VERIFY_QUERIES || n_kv < 1 || n_frames < 1) return 0;
+  if (!edda::decoder_fused_supported(n_q, n_kv, n_frames)) return 0;
+  return stack_ws(n_q, n_frames).total;
+}
+
+edda_status edda_decoder_verify_stack(const void* x, int32_t n_q, const int32_t* slots, int32_t cache_slots,
+                                      int32_t n_kv, const uint32_t* mask_rows, int32_t n_frames,
+                                      const edda_decoder_stack_layer* layers, int32_t n_layers, void* y,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "edda_decoder_verify_stack";
+  if (!x || !slots || !layers || !y)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: x, slots, layers and y must be non-null", fn);
+  if (n_layers < 1) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_layers = %d must be >= 1", fn, n_layers);
+  if (n_q < 1 || n_q > EDDA_MAX_VERIFY_QUERIES)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_q = %d outside [1, %d]", fn, n_q, EDDA_MAX_VERIFY_QUERIES);
+  if (cache_slots < 1 || n_kv < 1 || n_kv > cache_slots || (int64_t)cache_slots * EDDA_D_MODEL >= kMaxRows)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_kv = %d must be in [1, cache_slots = %d]", fn, n_kv, cache_slots);
+  if (n_frames < 1 || (int64_t)n_frames * EDDA_D_MODEL >= kMaxRows)
+    return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_frames = %d out of range", fn, n_frames);
+  if (!edda::decoder_fused_supported(n_q, n_kv, n_frames))
+    return fail(EDDA_ERR_UNSUPPORTED,
+                "%s: n_kv = %d (at most %d) or n_frames = %d: run edda_decoder_verify_layer per layer", fn, n_kv,
+                EDDA_DECODER_STACK_MAX_KV, n_frames);
+  edda::Slots sl{};
+  for (int32_t t = 0; t < n_q; ++t) {
+    if (slots[t] < 0 || slots[t] >= n_kv)
+      return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: slots[%d] = %d outside [0, n_kv = %d)", fn, t, slots[t], n_kv);
+    for (int32_t u = 0; u < t; ++u)
+      if (slots[u] == slots[t]) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: slot %d repeated", fn, slots[t]);
+    sl.s[t] = slots[t];
+  }
+  if (!aligned(x, 16) || !aligned(y, 16) || (workspace && !aligned(workspace, 256)))
+    return fail(EDDA_ERR_MISALIGNED, "%s: x and y must be 16-byte, the workspace 256-byte aligned", fn);
+  if (mask_rows && !aligned(mask_rows, 4)) return fail(EDDA_ERR_MISALIGNED, "%s: mask_rows must be 4-byte aligned", fn);
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const edda_decoder_stack_layer& L = layers[l];
+    const edda_decoder_layer_weights& w = L.weights;
+    const void* required[] = {w.ln1_gamma, w.ln1_beta, w.w_qkv,     w.w_o,       w.ln2_gamma, w.ln2_beta,
+                              w.w_q_cross, w.w_o_cross, w.ln3_gamma, w.ln3_beta, w.w_fc1,     w.w_fc2,
+                              L.k_cache,   L.v_cache,   L.cross_k,   L.cross_v};
+    for (const void* q : required)
+      if (!q)
+        return fail(EDDA_ERR_INVALID_ARGUMENT,
+                    "%s: layer %d: every LayerNorm, weight-matrix, cache and cross K/V pointer is required", fn, l);
+    const void* all[] = {w.ln1_gamma, w.ln1_beta, w.w_qkv,     w.b_qkv,     w.w_o,       w.b_o,       w.ln2_gamma,
+                         w.ln2_beta,  w.w_q_cross, w.b_q_cross, w.w_o_cross, w.b_o_cross, w.ln3_gamma, w.ln3_beta,
+                         w.w_fc1,     w.b_fc1,     w.w_fc2,     w.b_fc2,     L.k_cache,   L.v_cache,   L.cross_k,
+                         L.cross_v};
+    for (const void* q : all)
+      if (q && !aligned(q, 16)) return fail(EDDA_ERR_MISALIGNED, "%s: layer %d: pointers must be 16-byte aligned", fn, l);
+  }
+  const StackWs W = stack_ws(n_q, n_frames);
+  if (!workspace || workspace_bytes < W.total)
+    return fail(EDDA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, W.total,
+                workspace ? workspace_bytes : (size_t)0);
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Launches of up to kDecoderFusedMaxLayers layers; between two launches the activations go
+  // through the carry rows (a launch may read and then overwrite them: it reads its input only
+  // in its first layer and writes its output in its last).
+  const int G = edda::kDecoderFusedMaxLayers;
+  for (int32_t l0 = 0; l0 < n_layers; l0 += G) {
+    const int n = std::min<int32_t>(G, n_layers - l0);
+    edda::DecoderFusedParams p{};
+    p.x = l0 == 0 ? x : ws + W.carry;
+    p.y = l0 + n == n_layers ? y : ws + W.carry;
+    p.n_q = n_q, p.slots = sl, p.n_kv = n_kv, p.mask = mask_rows, p.n_frames = n_frames, p.n_layers = n;
+    for (int i = 0; i < n; ++i) {
+      const edda_decoder_stack_layer& L = layers[l0 + i];
+      const edda_decoder_layer_weights& wt = L.weights;
+      const DecoderMats m{wt.ln1_gamma, wt.ln1_beta, {wt.w_qkv, nullptr}, wt.b_qkv, {wt.w_o, nullptr}, wt.b_o,
+                          wt.ln2_gamma, wt.ln2_beta, {wt.w_q_cross, nullptr}, wt.b_q_cross, {wt.w_o_cross, nullptr},
+                          wt.b_o_cross, wt.ln3_gamma, wt.ln3_beta, {wt.w_fc1, nullptr}, wt.b_fc1,
+                          {wt.w_fc2, nullptr}, wt.b_fc2};
+      fused_layer_ptrs(m, false, L.k_cache, L.v_cache, L.cross_k, L.cross_v, &p.layer[i]);
+    }
+    p.lws = ws + W.blocks, p.lws_stride = W.block;
+    p.off_qkv = (uint32_t)W.qkv, p.off_o = (uint32_t)W.o, p.off_x1 = (uint32_t)W.x1, p.off_qc = (uint32_t)W.qc;
+    p.off_h = (uint32_t)W.h, p.off_x2 = (uint32_t)W.x2, p.off_f = (uint32_t)W.f, p.off_y = (uint32_t)W.y;
+    p.verify_counters = ws, p.ctl = ws + kFusedCtlOffset, p.flags = ws + kStackFlagOffset, p.part = ws + W.part;
+    p.workgroups = kFusedWorkgroups;
+    const hipError_t e = edda::launch_decoder_layer_fused(p, s);
+    if (e != hipSuccess) {
+      char msg[96];
+      snprintf(msg, sizeof msg, "%s launch (layers %d..%d)", fn, l0, l0 + n - 1);
+      return from_hip(e, msg);
+    }
+  }
+  return ok();
 }
 
 edda_status edda_quantize_q8_0(const void* w, int32_t rows, int32_t cols, void* codes, void* scales, void* stream) {

@@ -40,12 +40,12 @@
 //
 // Work items (the block GEMMs as kernel 6: weights as the MFMA A operand, 8 waves over the
 // 32-deep K steps, summed in LDS; a LayerNorm is computed once per item):
-//   0  LN1 + QKV + K/V cache append, 32 columns          120 items, x from the layer input
+//   0  LN1 + QKV + K/V cache append, 64 columns          60 items, x from the layer input
 //   1  self-attention, one item per head (<= 512 keys)   20
-//   2  output projection + residual x, 16 columns        80
-//   3  LN2 + cross query, 16 columns                     80
-//   4  cross-attention, 256-key splits x 20 heads        20 * ceil(n_frames / 256)
-//   5  cross output projection + residual x1             80
+//   2  output projection + residual x, 32 columns        40
+//   3  LN2 + cross query, 32 columns                     40
+//   4  cross-attention, 512-key splits x 20 heads        20 * ceil(n_frames / 512)
+//   5  cross output projection + residual x1, 32 cols    40
 //   6  LN3 + fc1 + GELU, 64 columns                      80
 //   7  fc2 (K = 5120) + residual x2, 16 columns          80
 #include <math.h>
@@ -66,7 +66,14 @@ constexpr int kFCols = 16;
 constexpr int kFLnGroups = kDModel / 256;
 constexpr int kFALd = kDModel + 8;  // LDS row stride (halves) of the normalised rows
 constexpr int kSteps = 8;
-constexpr int kCrossMergeBatch = 8;  // 1500 frames: 6 splits of 256 keys
+// Item sizes (fewer, larger items keep fewer workgroups waiting per step): the QKV GEMM 64
+// columns (4 blocks) per item, the 1280-wide projections 32 (2 blocks), fc1 64, fc2 16 over
+// the whole K = 5120; cross-attention splits of 512 keys (8 waves of two 32-key chunks).
+constexpr int kQkvBlocks = 4, kProjBlocks = 2, kFc1Blocks = 4;
+constexpr int kCrossCpw = 2;
+constexpr int kCrossKeys = kCrossCpw * 8 * 32;
+constexpr int kCrossMergeBatch = 4;  // 1500 frames: 3 splits
+constexpr int kMaxStackLayers = kDecoderFusedMaxLayers;
 constexpr int kCtlStride = 64;  // uint32 words: the two counters 256 bytes apart
 constexpr int kSpinLimit = 1 << 20;  // polls (seconds) before a wait gives up
 constexpr int kCoarseSleep = 127;    // s_sleep units of 64 clocks between polls
@@ -130,34 +137,41 @@ __device__ __forceinline__ void publish(uint32_t* flag) {
   if (threadIdx.x == 0) st32c(flag, 1u);
 }
 
-struct FusedArgs {
-  const f16* x;
-  f16* y;
-  int n_q;
-  Slots slots;
+// The pointers of one layer.
+struct LayerPtrs {
+  // ln1_g, ln1_b, w_qkv, b_qkv, w_o, b_o, ln2_g, ln2_b, w_qc, b_qc, w_oc, b_oc, ln3_g, ln3_b,
+  // w_fc1, b_fc1, w_fc2, b_fc2 (weights [out][in] fp16, or Q8_0 codes; biases may be null)
+  const f16* w[18];
+  const f16* scales[6];  // Q8_0 scales of the six matrices, or null
   f16* k_cache;
   f16* v_cache;
+  const f16* cross_k;
+  const f16* cross_v;
+};
+
+struct FusedArgs {
+  const f16* x;  // input of the first layer
+  f16* y;        // output of the last layer
+  int n_q;
+  Slots slots;
   int n_kv;
   const uint32_t* mask;
   int mask_words;
-  const f16* cross_k;
-  const f16* cross_v;
   int n_frames;
   int cross_splits;
-  // weights ([out][in] fp16) and LayerNorm parameters; biases may be null
-  const f16 *ln1_g, *ln1_b, *w_qkv, *b_qkv, *w_o, *b_o;
-  const f16 *ln2_g, *ln2_b, *w_qc, *b_qc, *w_oc, *b_oc;
-  const f16 *ln3_g, *ln3_b, *w_fc1, *b_fc1, *w_fc2, *b_fc2;
-  // Q8_0 scales of w_qkv, w_o, w_qc, w_oc, w_fc1, w_fc2 (the w_* then hold codes), or null
-  const f16* scales[6];
-  // workspace
-  f16 *qkv, *o, *x1, *qc, *h, *x2, *f;
+  int n_layers;
+  // Workspace rows of layer l at lws + l * lws_stride + off_*; off_y: a layer's output (the
+  // next layer's input) except the last layer's, which goes to y.
+  char* lws;
+  size_t lws_stride;
+  uint32_t off_qkv, off_o, off_x1, off_qc, off_h, off_x2, off_f, off_y;
   uint32_t* verify_counters;
   float* part_ml;
   float* part_o;
   uint32_t* ctl;  // ticket at ctl[0], exit count at ctl[kCtlStride]
-  uint32_t* flags;  // one done flag per item
-  int step_end[kSteps];  // running item totals
+  uint32_t* flags;  // one done flag per item of every layer
+  int step_end[kSteps];  // running item totals of one layer
+  LayerPtrs layer[kMaxStackLayers];
 };
 
 // The operands of one block GEMM: C[M, N] = act(A W^T + bias) + residual.
@@ -171,6 +185,10 @@ struct GemmOp {
   const f16* res;  // [M][N] or null
   f16* c;          // [M][N]
   int N, K;
+  bool a_fresh;    // the LayerNorm rows were written in this launch (loaded after the wait)
+  bool res_fresh;  // the residual was written in this launch (loaded after the wait)
+  f16* k_cache;    // APPEND: the caches whose rows slots[m] receive the K and V columns
+  f16* v_cache;
 };
 
 constexpr int kMaxBlocks = 4;  // column blocks of one GEMM item
@@ -179,13 +197,6 @@ struct GemmSmem {
   alignas(16) f16 a_lds[16 * kFALd];
 };
 
-// One block-GEMM item: NB column blocks of 16 (C[:, n0 .. n0 + 16 NB)) over the whole K = 256 NU
-// (wave w takes the 32-deep steps w, w + 8, ...).  A_FRESH / RES_FRESH: the operand rows / the
-// residual were written in this launch (coherent loads after the wait).  A_FRAG / C_FRAG: A is
-// read, C written, in fragment order (C_FRAG: no residual, no append).  Q8: the weights are
-// Q8_0 codes and scales, each step's dot products scaled in fp32 as in kernel 6.  (A_FRESH only decides
-// whether the LayerNorm rows are loaded before or after the wait.)  Per block the arithmetic is kernel 6's (same fragments,
-// same summation order over steps and waves).
 // Fragment order of a [16][K] operand consumed by the block GEMMs: for each 32-deep step s, the
 // 64 lanes' 16-byte fragments in lane order (lane 16 g + r holds row r, k = 32 s + 8 g ..
 // 8 g + 7), so a consumer's load instruction reads 1 KB contiguous (row-major rows give 16
@@ -194,8 +205,14 @@ __device__ __forceinline__ uint32_t frag_index(int m, int k) {
   return (uint32_t)((((k >> 5) * 4 + ((k >> 3) & 3)) * 16 + m) * 8 + (k & 7));
 }
 
-template <int NB, int NU, int ACT, bool LN, bool A_FRESH, bool A_FRAG, bool RES_FRESH, bool APPEND, bool C_FRAG,
-          bool Q8>
+// One block-GEMM item: NB column blocks of 16 (C[:, n0 .. n0 + 16 NB)) over the whole K = 256 NU
+// (wave w takes the 32-deep steps w, w + 8, ...).  op.a_fresh / op.res_fresh: the LayerNorm
+// rows / the residual were written in this launch and are loaded after the wait (the other
+// operands a step reads after its wait always are).  A_FRAG / C_FRAG: A is read, C written, in
+// fragment order (C_FRAG: no residual, no append).  Q8: the weights are Q8_0 codes and scales,
+// each step's dot products scaled in fp32 as in kernel 6.  Per block the arithmetic is kernel
+// 6's (same fragments, same summation order over steps and waves).
+template <int NB, int NU, int ACT, bool LN, bool A_FRAG, bool APPEND, bool C_FRAG, bool Q8>
 __device__ __forceinline__ void gemm_item(const FusedArgs& fa, const GemmOp& op, int item, const StepWait& wait,
                                           GemmSmem& sm, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
@@ -211,10 +228,12 @@ __device__ __forceinline__ void gemm_item(const FusedArgs& fa, const GemmOp& op,
   f16x8 raw[LN ? kLnPerThread : 1];
   f16x4 gam[LN ? kFLnGroups : 1], bet[LN ? kFLnGroups : 1];
   auto ln_chunk = [&](int i) { return (uint32_t)((tid + kFThreads * i) * 8); };  // element index
-  if constexpr (LN && !A_FRESH) {
+  if constexpr (LN) {
+    if (!op.a_fresh) {
 #pragma unroll
-    for (int i = 0; i < kLnPerThread; ++i)
-      if ((int)ln_chunk(i) < M * kDModel) raw[i] = load16(op.a + ln_chunk(i));
+      for (int i = 0; i < kLnPerThread; ++i)
+        if ((int)ln_chunk(i) < M * kDModel) raw[i] = load16(op.a + ln_chunk(i));
+    }
   }
   if constexpr (LN) {
 #pragma unroll
@@ -252,15 +271,13 @@ __device__ __forceinline__ void gemm_item(const FusedArgs& fa, const GemmOp& op,
   f16x2 bias2 = {};
   if (op.bias && epi) bias2 = *reinterpret_cast<const f16x2*>(op.bias + ecol);
   f16x2 res2 = {};
-  if constexpr (!RES_FRESH) {
-    if (op.res && epi) res2 = *reinterpret_cast<const f16x2*>(op.res + (size_t)em * N + ecol);
-  }
+  if (op.res && !op.res_fresh && epi) res2 = *reinterpret_cast<const f16x2*>(op.res + (size_t)em * N + ecol);
   wait();
 
   const int arow = min(r16, M - 1);
   f16x8 xf[NU];
   if constexpr (LN) {
-    if constexpr (A_FRESH) {
+    if (op.a_fresh) {
 #pragma unroll
       for (int i = 0; i < kLnPerThread; ++i)
         if ((int)ln_chunk(i) < M * kDModel) raw[i] = load16(op.a + ln_chunk(i));
@@ -294,7 +311,6 @@ __device__ __forceinline__ void gemm_item(const FusedArgs& fa, const GemmOp& op,
       xf[u] = *reinterpret_cast<const f16x8*>(&sm.a_lds[arow * kFALd + 32 * (wave + 8 * u) + 8 * g]);
   } else {
     if constexpr (A_FRAG) {
-      static_assert(A_FRESH, "fragment-ordered operands are written in the launch");
 #pragma unroll
       for (int u = 0; u < NU; ++u) xf[u] = load16(op.a + ((wave + 8 * u) * kWave + lane) * 8);
     } else {
@@ -304,9 +320,7 @@ __device__ __forceinline__ void gemm_item(const FusedArgs& fa, const GemmOp& op,
         xf[u] = load16(op.a + xrow + 32 * (wave + 8 * u));
     }
   }
-  if constexpr (RES_FRESH) {
-    if (op.res && epi) res2 = *reinterpret_cast<const f16x2*>(op.res + (size_t)em * N + ecol);
-  }
+  if (op.res && op.res_fresh && epi) res2 = *reinterpret_cast<const f16x2*>(op.res + (size_t)em * N + ecol);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     f32x4 acc = {};
@@ -351,8 +365,8 @@ __device__ __forceinline__ void gemm_item(const FusedArgs& fa, const GemmOp& op,
     const int col = ecol - kDModel;  // 0 .. 1279: K, 1280 .. 2559: V (a pair never straddles)
     if (col >= 0) {
       const size_t row = (size_t)fa.slots.s[em] * kDModel;
-      if (col < kDModel) st32c(fa.k_cache + row + col, out);
-      else st32c(fa.v_cache + row + col - kDModel, out);
+      if (col < kDModel) st32c(op.k_cache + row + col, out);
+      else st32c(op.v_cache + row + col - kDModel, out);
     }
   }
 }
@@ -392,7 +406,7 @@ struct CrossIo {
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 template <int CPW>
 constexpr size_t kArenaBytes =
-    cmax(cmax(sizeof(vcore::Smem<CPW, kFWaves>), sizeof(vcore::Smem<1, kFWaves>)), sizeof(GemmSmem));
+    cmax(cmax(sizeof(vcore::Smem<CPW, kFWaves>), sizeof(vcore::Smem<kCrossCpw, kFWaves>)), sizeof(GemmSmem));
 
 // SELF_CPW: 32-key chunks per wave of the self-attention (1: n_kv <= 256, 2: <= 512).
 // SELF_MODE: vcore::kMaskRows or kMaskNone.  Q8: Q8_0 projection weights.
@@ -402,7 +416,8 @@ __global__ __launch_bounds__(kFThreads) void decoder_layer_kernel(FusedArgs fa) 
   __shared__ int8_t fresh_row[2 * kFWaves * vcore::kWaveKeys];
   __shared__ int s_item;
   uint32_t* const ctl = fa.ctl;
-  const int total = fa.step_end[kSteps - 1];
+  const int per_layer = fa.step_end[kSteps - 1];
+  const int total = per_layer * fa.n_layers;
   if (threadIdx.x == 0) s_item = (int)__hip_atomic_fetch_add(&ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   int item = s_item;
@@ -416,62 +431,88 @@ __global__ __launch_bounds__(kFThreads) void decoder_layer_kernel(FusedArgs fa) 
     // a later one, and this workgroup finishes the current item first.)
     uint32_t next = 0;
     if (tid == 0) next = __hip_atomic_fetch_add(&ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int layer = item / per_layer, in_layer = item - layer * per_layer;
     int p = 0;
-    while (item >= fa.step_end[p]) ++p;
-    const int local = item - (p ? fa.step_end[p - 1] : 0);
-    const StepWait wait{p >= 1 ? fa.flags : nullptr, p >= 3 ? fa.step_end[p - 3] : 0, p >= 2 ? fa.step_end[p - 2] : 0,
-                        p >= 2 ? fa.step_end[p - 2] : 0, p >= 1 ? fa.step_end[p - 1] : 0};
+    while (in_layer >= fa.step_end[p]) ++p;
+    const int local = in_layer - (p ? fa.step_end[p - 1] : 0);
+    // Steps are ordered across layers: global step layer * 8 + p waits for global steps - 1
+    // (fine) and - 2 (coarse).
+    auto flag_range = [&](int gstep, int& begin, int& end) {
+      const int l = gstep / kSteps, q = gstep % kSteps;
+      begin = l * per_layer + (q ? fa.step_end[q - 1] : 0);
+      end = l * per_layer + fa.step_end[q];
+    };
+    const int gstep = layer * kSteps + p;
+    StepWait wait{gstep >= 1 ? fa.flags : nullptr, 0, 0, 0, 0};
+    if (gstep >= 2) flag_range(gstep - 2, wait.coarse_begin, wait.coarse_end);
+    if (gstep >= 1) flag_range(gstep - 1, wait.begin, wait.end);
+    const LayerPtrs& L = fa.layer[layer];
+    char* const wsl = fa.lws + (size_t)layer * fa.lws_stride;
+    f16* const qkv = reinterpret_cast<f16*>(wsl + fa.off_qkv);
+    f16* const o = reinterpret_cast<f16*>(wsl + fa.off_o);
+    f16* const x1 = reinterpret_cast<f16*>(wsl + fa.off_x1);
+    f16* const qc = reinterpret_cast<f16*>(wsl + fa.off_qc);
+    f16* const h = reinterpret_cast<f16*>(wsl + fa.off_h);
+    f16* const x2 = reinterpret_cast<f16*>(wsl + fa.off_x2);
+    f16* const f = reinterpret_cast<f16*>(wsl + fa.off_f);
+    // The layer's input: the launch's input, or the previous layer's output (written in it).
+    const bool x_fresh = layer > 0;
+    const f16* const x =
+        x_fresh ? reinterpret_cast<const f16*>(fa.lws + (size_t)(layer - 1) * fa.lws_stride + fa.off_y) : fa.x;
+    f16* const y = layer == fa.n_layers - 1 ? fa.y : reinterpret_cast<f16*>(wsl + fa.off_y);
     GemmSmem& gs = *reinterpret_cast<GemmSmem*>(arena);
     switch (p) {
       case 0:
-        gemm_item<2, 5, 0, true, false, false, false, true, false, Q8>(
-            fa, GemmOp{fa.w_qkv, fa.scales[0], fa.b_qkv, fa.x, fa.ln1_g, fa.ln1_b, nullptr, fa.qkv, kQkvCols, kDModel}, local, wait,
-            gs, tid);
+        gemm_item<kQkvBlocks, 5, 0, true, false, true, false, Q8>(
+            fa, GemmOp{L.w[2], L.scales[0], L.w[3], x, L.w[0], L.w[1], nullptr, qkv, kQkvCols, kDModel, x_fresh, false,
+                       L.k_cache, L.v_cache},
+            local, wait, gs, tid);
         break;
       case 1: {
         fresh_row[tid] = -1;  // 512 threads, 512 slots
         __syncthreads();
         if (tid < fa.n_q) fresh_row[fa.slots.s[tid]] = (int8_t)tid;
         __syncthreads();
-        const vcore::Args a{fa.qkv, kQkvCols, fa.n_q, fa.k_cache, fa.v_cache, fa.n_kv, kHeads, fa.mask, fa.mask_words,
-                            nullptr, fa.o, fa.verify_counters, fa.part_ml, fa.part_o};
+        const vcore::Args a{qkv, kQkvCols, fa.n_q, L.k_cache, L.v_cache, fa.n_kv, kHeads, fa.mask, fa.mask_words,
+                            nullptr, o, fa.verify_counters, fa.part_ml, fa.part_o};
         vcore::verify_unit<SELF_MODE, SELF_CPW, kFWaves>(a, 0, local, 1,
                                                          *reinterpret_cast<vcore::Smem<SELF_CPW, kFWaves>*>(arena),
-                                                         SelfIo{fresh_row, fa.qkv, wait}, tid);
+                                                         SelfIo{fresh_row, qkv, wait}, tid);
         break;
       }
       case 2:
-        gemm_item<1, 5, 0, false, true, true, false, false, false, Q8>(
-            fa, GemmOp{fa.w_o, fa.scales[1], fa.b_o, fa.o, nullptr, nullptr, fa.x, fa.x1, kDModel, kDModel}, local, wait, gs, tid);
+        gemm_item<kProjBlocks, 5, 0, false, true, false, false, Q8>(
+            fa, GemmOp{L.w[4], L.scales[1], L.w[5], o, nullptr, nullptr, x, x1, kDModel, kDModel, true, x_fresh},
+            local, wait, gs, tid);
         break;
       case 3:
-        gemm_item<1, 5, 0, true, true, false, false, false, false, Q8>(
-            fa, GemmOp{fa.w_qc, fa.scales[2], fa.b_qc, fa.x1, fa.ln2_g, fa.ln2_b, nullptr, fa.qc, kDModel, kDModel}, local, wait, gs,
-            tid);
+        gemm_item<kProjBlocks, 5, 0, true, false, false, false, Q8>(
+            fa, GemmOp{L.w[8], L.scales[2], L.w[9], x1, L.w[6], L.w[7], nullptr, qc, kDModel, kDModel, true, false},
+            local, wait, gs, tid);
         break;
       case 4: {
-        const vcore::Args a{fa.qc, kDModel, fa.n_q, fa.cross_k, fa.cross_v, fa.n_frames, kHeads, nullptr, 0,
-                            nullptr, fa.h, fa.verify_counters, fa.part_ml, fa.part_o};
-        vcore::verify_unit<vcore::kMaskNone, 1, kFWaves, CrossIo, kCrossMergeBatch>(a, local % fa.cross_splits,
-                                                                                     local / fa.cross_splits,
-                                                         fa.cross_splits,
-                                                         *reinterpret_cast<vcore::Smem<1, kFWaves>*>(arena),
-                                                         CrossIo{wait}, tid);
+        const vcore::Args a{qc, kDModel, fa.n_q, L.cross_k, L.cross_v, fa.n_frames, kHeads, nullptr, 0,
+                            nullptr, h, fa.verify_counters, fa.part_ml, fa.part_o};
+        vcore::verify_unit<vcore::kMaskNone, kCrossCpw, kFWaves, CrossIo, kCrossMergeBatch>(
+            a, local % fa.cross_splits, local / fa.cross_splits, fa.cross_splits,
+            *reinterpret_cast<vcore::Smem<kCrossCpw, kFWaves>*>(arena), CrossIo{wait}, tid);
         break;
       }
       case 5:
-        gemm_item<1, 5, 0, false, true, true, true, false, false, Q8>(
-            fa, GemmOp{fa.w_oc, fa.scales[3], fa.b_oc, fa.h, nullptr, nullptr, fa.x1, fa.x2, kDModel, kDModel}, local, wait, gs, tid);
+        gemm_item<kProjBlocks, 5, 0, false, true, false, false, Q8>(
+            fa, GemmOp{L.w[10], L.scales[3], L.w[11], h, nullptr, nullptr, x1, x2, kDModel, kDModel, true, true},
+            local, wait, gs, tid);
         break;
       case 6:
-        gemm_item<4, 5, 1, true, true, false, false, false, true, Q8>(
-            fa, GemmOp{fa.w_fc1, fa.scales[4], fa.b_fc1, fa.x2, fa.ln3_g, fa.ln3_b, nullptr, fa.f, 4 * kDModel, kDModel}, local,
-            wait, gs, tid);
+        gemm_item<kFc1Blocks, 5, 1, true, false, false, true, Q8>(
+            fa, GemmOp{L.w[14], L.scales[4], L.w[15], x2, L.w[12], L.w[13], nullptr, f, 4 * kDModel, kDModel, true,
+                       false},
+            local, wait, gs, tid);
         break;
       default:
-        gemm_item<1, 20, 0, false, true, true, true, false, false, Q8>(
-            fa, GemmOp{fa.w_fc2, fa.scales[5], fa.b_fc2, fa.f, nullptr, nullptr, fa.x2, fa.y, kDModel, 4 * kDModel}, local, wait, gs,
-            tid);
+        gemm_item<1, 20, 0, false, true, false, false, Q8>(
+            fa, GemmOp{L.w[16], L.scales[5], L.w[17], f, nullptr, nullptr, x2, y, kDModel, 4 * kDModel, true, true},
+            local, wait, gs, tid);
         break;
     }
     publish(&fa.flags[item]);
@@ -496,58 +537,60 @@ __global__ __launch_bounds__(kFThreads) void decoder_layer_kernel(FusedArgs fa) 
 }  // namespace
 
 int decoder_fused_items(int n_frames) {
-  const int cross_splits = (n_frames + kFWaves * vcore::kWaveKeys - 1) / (kFWaves * vcore::kWaveKeys);
-  // QKV, self-attention, the four 16-column GEMMs, cross-attention, fc1
-  return kQkvCols / (2 * kFCols) + kHeads + 4 * (kDModel / kFCols) + kHeads * cross_splits + 4 * kDModel / (4 * kFCols);
+  const int cross_splits = (n_frames + kCrossKeys - 1) / kCrossKeys;
+  // QKV, self-attention, the three projections, cross-attention, fc1, fc2
+  return kQkvCols / (kQkvBlocks * kFCols) + kHeads + 3 * (kDModel / (kProjBlocks * kFCols)) + kHeads * cross_splits +
+         4 * kDModel / (kFc1Blocks * kFCols) + kDModel / kFCols;
 }
 
 bool decoder_fused_supported(int n_q, int n_kv, int n_frames) {
-  const int cross_splits = (n_frames + kFWaves * vcore::kWaveKeys - 1) / (kFWaves * vcore::kWaveKeys);
+  const int cross_splits = (n_frames + kCrossKeys - 1) / kCrossKeys;
   return n_q >= 1 && n_q <= 16 && n_kv >= 1 && n_kv <= 2 * kFWaves * vcore::kWaveKeys && n_frames >= 1 &&
          kHeads * cross_splits <= kMaxPollLoads * kWave && decoder_fused_items(n_frames) <= kDecoderFusedMaxItems;
 }
 
 hipError_t launch_decoder_layer_fused(const DecoderFusedParams& p, hipStream_t stream) {
-  if (!decoder_fused_supported(p.n_q, p.n_kv, p.n_frames) || p.workgroups < 1) return hipErrorInvalidValue;
+  if (!decoder_fused_supported(p.n_q, p.n_kv, p.n_frames) || p.workgroups < 1 || p.n_layers < 1 ||
+      p.n_layers > kMaxStackLayers)
+    return hipErrorInvalidValue;
   FusedArgs fa{};
   fa.x = static_cast<const f16*>(p.x);
   fa.y = static_cast<f16*>(p.y);
   fa.n_q = p.n_q;
   fa.slots = p.slots;
-  fa.k_cache = static_cast<f16*>(p.k_cache);
-  fa.v_cache = static_cast<f16*>(p.v_cache);
   fa.n_kv = p.n_kv;
   fa.mask = p.mask;
   fa.mask_words = (p.n_kv + 31) / 32;
-  fa.cross_k = static_cast<const f16*>(p.cross_k);
-  fa.cross_v = static_cast<const f16*>(p.cross_v);
   fa.n_frames = p.n_frames;
-  fa.cross_splits = (p.n_frames + kFWaves * vcore::kWaveKeys - 1) / (kFWaves * vcore::kWaveKeys);
-  const f16* w[18];
-  for (int i = 0; i < 18; ++i) w[i] = static_cast<const f16*>(p.w[i]);
-  fa.ln1_g = w[0], fa.ln1_b = w[1], fa.w_qkv = w[2], fa.b_qkv = w[3], fa.w_o = w[4], fa.b_o = w[5];
-  fa.ln2_g = w[6], fa.ln2_b = w[7], fa.w_qc = w[8], fa.b_qc = w[9], fa.w_oc = w[10], fa.b_oc = w[11];
-  fa.ln3_g = w[12], fa.ln3_b = w[13], fa.w_fc1 = w[14], fa.b_fc1 = w[15], fa.w_fc2 = w[16], fa.b_fc2 = w[17];
-  fa.qkv = static_cast<f16*>(p.qkv);
-  fa.o = static_cast<f16*>(p.o);
-  fa.x1 = static_cast<f16*>(p.x1);
-  fa.qc = static_cast<f16*>(p.qc);
-  fa.h = static_cast<f16*>(p.h);
-  fa.x2 = static_cast<f16*>(p.x2);
-  fa.f = static_cast<f16*>(p.f);
+  fa.cross_splits = (p.n_frames + kCrossKeys - 1) / kCrossKeys;
+  fa.n_layers = p.n_layers;
+  fa.lws = static_cast<char*>(p.lws);
+  fa.lws_stride = p.lws_stride;
+  fa.off_qkv = p.off_qkv, fa.off_o = p.off_o, fa.off_x1 = p.off_x1, fa.off_qc = p.off_qc;
+  fa.off_h = p.off_h, fa.off_x2 = p.off_x2, fa.off_f = p.off_f, fa.off_y = p.off_y;
   fa.verify_counters = static_cast<uint32_t*>(p.verify_counters);
   fa.part_o = static_cast<float*>(p.part);  // o partials first (16-byte aligned), then (m, l)
   fa.part_ml = fa.part_o + (size_t)fa.cross_splits * p.n_q * kHeads * kHeadDim;
   fa.ctl = static_cast<uint32_t*>(p.ctl);
   fa.flags = static_cast<uint32_t*>(p.flags);
-  const int counts[kSteps] = {kQkvCols / (2 * kFCols), kHeads, kDModel / kFCols, kDModel / kFCols,
-                              kHeads * fa.cross_splits, kDModel / kFCols, 4 * kDModel / (4 * kFCols),
-                              kDModel / kFCols};
+  const bool q8 = p.layer[0].scales[0] != nullptr;
+  for (int l = 0; l < p.n_layers; ++l) {
+    const DecoderFusedLayer& s = p.layer[l];
+    if ((s.scales[0] != nullptr) != q8) return hipErrorInvalidValue;
+    LayerPtrs& d = fa.layer[l];
+    for (int i = 0; i < 18; ++i) d.w[i] = static_cast<const f16*>(s.w[i]);
+    for (int i = 0; i < 6; ++i) d.scales[i] = static_cast<const f16*>(s.scales[i]);
+    d.k_cache = static_cast<f16*>(s.k_cache);
+    d.v_cache = static_cast<f16*>(s.v_cache);
+    d.cross_k = static_cast<const f16*>(s.cross_k);
+    d.cross_v = static_cast<const f16*>(s.cross_v);
+  }
+  const int counts[kSteps] = {kQkvCols / (kQkvBlocks * kFCols), kHeads, kDModel / (kProjBlocks * kFCols),
+                              kDModel / (kProjBlocks * kFCols), kHeads * fa.cross_splits,
+                              kDModel / (kProjBlocks * kFCols), 4 * kDModel / (kFc1Blocks * kFCols), kDModel / kFCols};
   int run = 0;
   for (int i = 0; i < kSteps; ++i) fa.step_end[i] = (run += counts[i]);
   if (run != decoder_fused_items(p.n_frames)) return hipErrorInvalidValue;
-  for (int i = 0; i < 6; ++i) fa.scales[i] = static_cast<const f16*>(p.scales[i]);
-  const bool q8 = p.scales[0] != nullptr;
   const dim3 grid(p.workgroups), block(kFThreads);
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, fa); };
   const bool rows = p.mask != nullptr;
@@ -563,7 +606,7 @@ hipError_t launch_decoder_layer_fused(const DecoderFusedParams& p, hipStream_t s
 }
 
 size_t decoder_fused_part_bytes(int n_q, int n_frames) {
-  const int cs = (n_frames + kFWaves * vcore::kWaveKeys - 1) / (kFWaves * vcore::kWaveKeys);
+  const int cs = (n_frames + kCrossKeys - 1) / kCrossKeys;
   return cs > 1 ? (size_t)cs * n_q * kHeads * (2 + kHeadDim) * sizeof(float) : 0;
 }
 

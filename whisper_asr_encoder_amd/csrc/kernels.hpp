@@ -79,28 +79,38 @@ hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, co
                          int mask_mode, const uint32_t* mask, const float* sinks, void* o, void* workspace,
                          hipStream_t stream);
 
-// The decoder's verification layer in one launch of `workgroups` persistent workgroups
-// (kernel 8, fp16 or Q8_0 projection weights, n_kv <= 512).  w: ln1_gamma, ln1_beta, w_qkv, b_qkv, w_o, b_o,
-// ln2_gamma, ln2_beta, w_q_cross, b_q_cross, w_o_cross, b_o_cross, ln3_gamma, ln3_beta, w_fc1,
-// b_fc1, w_fc2, b_fc2 (biases may be null).  qkv .. f: workspace rows ([16][3840], [16][1280]
-// x5, [16][5120]), no two aliased.  verify_counters: 20 per-head counters 256 bytes apart;
-// ctl: 2 counters 256 bytes apart; flags: decoder_fused_items(n_frames) words; all zero before
-// the launch and left zero by it.  part: decoder_fused_part_bytes(n_q, n_frames).
+// The decoder's verification layer, n_layers consecutive layers of it, in one launch of
+// `workgroups` persistent workgroups (kernel 8, fp16 or Q8_0 projection weights, n_kv <= 512).
+// Layer l's w: ln1_gamma, ln1_beta, w_qkv, b_qkv, w_o, b_o, ln2_gamma, ln2_beta, w_q_cross,
+// b_q_cross, w_o_cross, b_o_cross, ln3_gamma, ln3_beta, w_fc1, b_fc1, w_fc2, b_fc2 (biases may be
+// null); scales: the Q8_0 scales of the six matrices (w: codes), or all null for every layer.
+// Workspace rows of layer l at lws + l * lws_stride + off_*: qkv [16][3840], o, qc, x1, x2, y
+// [16][1280], h [16][1280], f [16][5120] (byte offsets; no two overlap); y of layer l is the
+// input of layer l + 1 (the last layer writes p.y).  verify_counters: 20 per-head counters 256
+// bytes apart; ctl: 2 counters 256 bytes apart; flags: n_layers * decoder_fused_items(n_frames)
+// words; all zero before the launch and left zero by it.  part: decoder_fused_part_bytes.
+constexpr int kDecoderFusedMaxLayers = 8;
+struct DecoderFusedLayer {
+  const void* w[18];
+  const void* scales[6];
+  void* k_cache;
+  void* v_cache;
+  const void* cross_k;
+  const void* cross_v;
+};
 struct DecoderFusedParams {
   const void* x;
   void* y;
   int n_q;
   Slots slots;
-  void* k_cache;
-  void* v_cache;
   int n_kv;
   const uint32_t* mask;  // rows [n_q][ceil(n_kv / 32)] or null (every slot admitted)
-  const void* cross_k;
-  const void* cross_v;
   int n_frames;
-  const void* w[18];
-  const void* scales[6];  // Q8_0 scales of w_qkv, w_o, w_q_cross, w_o_cross, w_fc1, w_fc2 (w: codes), or all null
-  void *qkv, *o, *x1, *qc, *h, *x2, *f;
+  int n_layers;
+  DecoderFusedLayer layer[kDecoderFusedMaxLayers];
+  void* lws;
+  size_t lws_stride;
+  uint32_t off_qkv, off_o, off_x1, off_qc, off_h, off_x2, off_f, off_y;
   void* verify_counters;
   void* ctl;
   void* flags;

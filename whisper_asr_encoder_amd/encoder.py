@@ -184,6 +184,7 @@ class DecoderVerifier:
         self.cross_v = [torch.empty(shape, dtype=torch.float16, device=device) for _ in self._keep]
         nb = _lib.decoder_verify_workspace_bytes(_lib.MAX_VERIFY_QUERIES, max_kv, self.n_frames)
         self.workspace = torch.zeros(max(nb, _lib.VERIFY_COUNTER_BYTES), dtype=torch.uint8, device=device)
+        self._stack, self.stack_workspace = None, None
 
     def _dev(self, a):
         return self.torch.from_numpy(np.ascontiguousarray(a)).to(self.device)
@@ -200,3 +201,23 @@ class DecoderVerifier:
     def layer(self, x, layer: int, slots, k_cache, v_cache, n_kv, mask_rows, y, stream=None):
         _lib.edda_decoder_verify_layer(x, slots, k_cache, v_cache, n_kv, mask_rows, self.cross_k[layer],
                                        self.cross_v[layer], self.structs[layer], y, self.workspace, stream)
+
+    def stack(self, x, slots, caches, n_kv, mask_rows, y, stream=None):
+        """Every layer in order over the block x (edda_decoder_verify_stack, fp16 weights):
+        caches[l] = (k_cache, v_cache) of layer l; y receives the last layer's output."""
+        if self.q8:
+            raise ValueError("the stack entry point takes fp16 weights")
+        cache_slots = caches[0][0].shape[0]
+        if self._stack is None or self._stack[0] != [(k.data_ptr(), v.data_ptr()) for k, v in caches]:
+            arr = (_lib.DecoderStackLayer * len(self.structs))()
+            for l, w in enumerate(self.structs):
+                k, v = caches[l]
+                arr[l] = _lib.DecoderStackLayer(w, k.data_ptr(), v.data_ptr(), self.cross_k[l].data_ptr(),
+                                                self.cross_v[l].data_ptr())
+            self._stack = ([(k.data_ptr(), v.data_ptr()) for k, v in caches], arr)
+        if self.stack_workspace is None:
+            nb = _lib.decoder_verify_stack_workspace_bytes(_lib.MAX_VERIFY_QUERIES, _lib.DECODER_STACK_MAX_KV,
+                                                           self.n_frames)
+            self.stack_workspace = self.torch.zeros(nb, dtype=self.torch.uint8, device=self.device)
+        _lib.edda_decoder_verify_stack(x, slots, cache_slots, n_kv, mask_rows, self.n_frames, self._stack[1], y,
+                                       self.stack_workspace, stream)
