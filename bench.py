@@ -421,6 +421,10 @@ def decoder_bench(args, torch):
         return timer(graph.replay, args.steps), graph
 
     forms = {"layer_by_layer": layer_by_layer} if q8 else {"stack": stacked, "layer_by_layer": layer_by_layer}
+    if args.decoder_form == "stack" and not q8:
+        forms = {"stack": stacked}
+    elif args.decoder_form == "layer":
+        forms = {"layer_by_layer": layer_by_layer}
     timed = {name: graph_ms(fn) for name, fn in forms.items()}
     best = min(timed, key=lambda k: timed[k][0])
     ms = timed[best][0]
@@ -644,6 +648,8 @@ def main():
     ap.add_argument("--workload", default="window", choices=["small", "window", "chunked", "batched", "verify", "encoder", "decoder",
                                                              "decoder_q8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decoder-form", default="both", choices=["both", "stack", "layer"],
+                    help="decoder workloads: time edda_decoder_verify_stack, per-layer calls, or both")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device-to-device copy (reference dispatch for "
