@@ -181,12 +181,27 @@ __device__ __forceinline__ void verify_unit(const Args& a, int split, int head, 
     const int u = lane + kWave * r;
     return (uint32_t)(key * kKvStride + head * kHeadDim + 8 * (u & 7));
   };
+  // With rows written in the launch (Io::kFreshRows): which of the lane's keys are such rows is
+  // decided once, before the wait; keys past the cache end load nothing (zeros: their scores are
+  // masked below and their P is exactly 0), rather than the clamped last row, which may itself
+  // be one of the fresh rows.
+  bool fk[CPW][2], fv[CPW][2][2];
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const uint32_t off = k_off(c, blk);
-      if (!io.fresh(min(chunk_key0(c) + 16 * blk + r16, last_key))) {
+      if constexpr (Io::kFreshRows) {
+        const int key = chunk_key0(c) + 16 * blk + r16;
+        const bool in = key < n_kv;
+        fk[c][blk] = in && io.fresh(key);
+        if (in && !fk[c][blk]) {
+          kf[c][blk][0] = load16(a.k + off);
+          kf[c][blk][1] = load16(a.k + (off + 32));
+        } else {
+          kf[c][blk][0] = kf[c][blk][1] = z8;
+        }
+      } else {
         kf[c][blk][0] = load16(a.k + off);
         kf[c][blk][1] = load16(a.k + (off + 32));
       }
@@ -194,8 +209,18 @@ __device__ __forceinline__ void verify_unit(const Args& a, int split, int head, 
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int k0 = v_key(c, r, 0), k1 = v_key(c, r, 1);
-      if (!io.fresh(k0)) va[c][r] = load16(a.v + v_off(k0, r));
-      if (!io.fresh(k1)) vb[c][r] = load16(a.v + v_off(k1, r));
+      if constexpr (Io::kFreshRows) {
+        const int u = lane + kWave * r;
+        const int key0 = chunk_key0(c) + 2 * (u >> 3);
+        const bool in0 = key0 < n_kv, in1 = key0 + 1 < n_kv;
+        fv[c][r][0] = in0 && io.fresh(key0);
+        fv[c][r][1] = in1 && io.fresh(key0 + 1);
+        va[c][r] = in0 && !fv[c][r][0] ? load16(a.v + v_off(k0, r)) : z8;
+        vb[c][r] = in1 && !fv[c][r][1] ? load16(a.v + v_off(k1, r)) : z8;
+      } else {
+        va[c][r] = load16(a.v + v_off(k0, r));
+        vb[c][r] = load16(a.v + v_off(k1, r));
+      }
     }
   }
   io.wait();
@@ -204,18 +229,18 @@ __device__ __forceinline__ void verify_unit(const Args& a, int split, int head, 
     for (int c = 0; c < CPW; ++c) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const int key = min(chunk_key0(c) + 16 * blk + r16, last_key);
-        if (io.fresh(key)) {
+        if (fk[c][blk]) {
+          const int key = chunk_key0(c) + 16 * blk + r16;
           kf[c][blk][0] = io.fresh_k(key, head * kHeadDim + 8 * G);
           kf[c][blk][1] = io.fresh_k(key, head * kHeadDim + 8 * G + 32);
         }
       }
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        const int k0 = v_key(c, r, 0), k1 = v_key(c, r, 1);
+        const int key0 = chunk_key0(c) + 2 * ((lane + kWave * r) >> 3);
         const int col = head * kHeadDim + 8 * ((lane + kWave * r) & 7);
-        if (io.fresh(k0)) va[c][r] = io.fresh_v(k0, col);
-        if (io.fresh(k1)) vb[c][r] = io.fresh_v(k1, col);
+        if (fv[c][r][0]) va[c][r] = io.fresh_v(key0, col);
+        if (fv[c][r][1]) vb[c][r] = io.fresh_v(key0 + 1, col);
       }
     }
   }
