@@ -400,7 +400,7 @@ def decoder_bench(args, torch):
         for l in range(layers):
             dv.layer(x if l == 0 else y, l, slots, caches[l][0], caches[l][1], L, mask, y)
 
-    def stacked():  # edda_decoder_verify_stack: launches of 8 layers (fp16 weights)
+    def stacked():  # edda_decoder_verify_stack (or _q8): launches of 8 layers
         dv.stack(x, slots, caches, L, mask, y)
 
     timer = Timer(torch)
@@ -420,8 +420,8 @@ def decoder_bench(args, torch):
             graph.replay()
         return timer(graph.replay, args.steps), graph
 
-    forms = {"layer_by_layer": layer_by_layer} if q8 else {"stack": stacked, "layer_by_layer": layer_by_layer}
-    if args.decoder_form == "stack" and not q8:
+    forms = {"stack": stacked, "layer_by_layer": layer_by_layer}
+    if args.decoder_form == "stack":
         forms = {"stack": stacked}
     elif args.decoder_form == "layer":
         forms = {"layer_by_layer": layer_by_layer}
@@ -450,7 +450,8 @@ def decoder_bench(args, torch):
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp16 activations, q8_0 weights" if q8 else "fp16",
         "data": "synthetic (seeded weights, caches and block rows)",
-        "launch": f"hip graph of the pass ({'edda_decoder_verify_stack' if best == 'stack' else 'edda_decoder_verify_layer per layer'})",
+        "launch": (f"hip graph of the pass ({'edda_decoder_verify_stack' if best == 'stack' else 'edda_decoder_verify_layer'}"
+                   f"{'_q8' if q8 else ''}{'' if best == 'stack' else ' per layer'})"),
         "eager_ms_per_step": round(eager_ms, 4),
         "us_per_pass_by_form": {k: round(v[0] * 1e3, 2) for k, v in timed.items()},
         "us_per_layer": round(ms * 1e3 / layers, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 3),

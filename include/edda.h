@@ -475,6 +475,25 @@ edda_status edda_decoder_verify_layer_q8(const void* x, int32_t n_q, const int32
                                          int32_t n_frames, const edda_decoder_layer_weights_q8* weights, void* y,
                                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* One layer of a stack with Q8_0 projection weights. */
+typedef struct {
+  edda_decoder_layer_weights_q8 weights;
+  void* k_cache;
+  void* v_cache;
+  const void* cross_k;
+  const void* cross_v;
+} edda_decoder_stack_layer_q8;
+
+/*
+ * edda_decoder_verify_stack with Q8_0 projection weights (as edda_decoder_verify_layer_q8, layer
+ * by layer, bit for bit). Same workspace (edda_decoder_verify_stack_workspace_bytes) and errors;
+ * EDDA_ERR_INVALID_ARGUMENT also for a matrix without scales.
+ */
+edda_status edda_decoder_verify_stack_q8(const void* x, int32_t n_q, const int32_t* slots, int32_t cache_slots,
+                                         int32_t n_kv, const uint32_t* mask_rows, int32_t n_frames,
+                                         const edda_decoder_stack_layer_q8* layers, int32_t n_layers, void* y,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Cross-attention keys and values of the encoder output, once per utterance and layer:
  * cross_k = enc W_k (no bias), cross_v = enc W_v + b_v.

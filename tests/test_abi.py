@@ -310,6 +310,24 @@ def test_decoder_verify_stack_rejects(lib, kw, status):
     assert lib.edda_last_error()
 
 
+def test_decoder_verify_stack_q8_rejects(lib):
+    arr = (_lib.DecoderStackLayerQ8 * 2)()
+    for l in range(2):
+        w = _lib.DecoderLayerWeightsQ8()
+        for name, kind in _lib.DecoderLayerWeightsQ8._fields_:
+            setattr(w, name, _lib.Q8Matrix(A, A) if kind is _lib.Q8Matrix else A)
+        arr[l] = _lib.DecoderStackLayerQ8(w, A, A, A, A)
+    sl = ctypes.cast((ctypes.c_int32 * 16)(*range(24, 40)), ctypes.POINTER(ctypes.c_int32))
+    call = lambda: lib.edda_decoder_verify_stack_q8(A, 16, sl, 448, 40, None, 1500, arr, 2, B, B + (1 << 24), 1 << 30,
+                                                     None)
+    arr[1].weights.w_fc2 = _lib.Q8Matrix(A, None)
+    assert call() == INVALID and b"scales" in lib.edda_last_error()
+    arr[1].weights.w_fc2 = _lib.Q8Matrix(A, ODD)
+    assert call() == MISALIGNED
+    arr[1].weights.w_fc2 = _lib.Q8Matrix(None, A)
+    assert call() == INVALID
+
+
 def test_decoder_stack_workspace_bytes(lib):
     n = lib.edda_decoder_verify_stack_workspace_bytes(16, 448, 1500)
     # zeroed counters and flags, cross partials (3 splits of 512 frames), carry rows, 8 blocks of

@@ -155,3 +155,40 @@ def test_decoder_layer_q8(torch, trial, layer, kind, frames, n_kv):
     rel = np.linalg.norm(y - y16) / np.linalg.norm(y16)
     say(f"  Q8 vs fp16 weights: y relative Frobenius distance {rel:.3e} (weight quantization)")
     assert rel < 2e-2
+
+
+def test_decoder_stack_q8_matches_layer_by_layer(torch):
+    """edda_decoder_verify_stack_q8 over 9 layers (two launches) against the Q8 layer entry point
+    layer by layer: y and every cache bit for bit (the per-layer form is held to the oracle above)."""
+    from whisper_asr_encoder_amd.encoder import DecoderVerifier
+    say("Q8 decoder stack of 9 layers vs layer by layer")
+    n_layers = 9
+    weights = [I.decoder_layer_weights(l) for l in range(n_layers)]
+    cases = [I.verify_tree_case(2, l) for l in range(n_layers)]
+    n_q, nk = cases[0].q.shape[0], cases[0].n_kv
+    slots = [int(s) for s in cases[0].query_slots]
+    cap = nk + 4
+    dv = DecoderVerifier(weights, max_kv=cap, q8=True)
+    dv.set_encoder_output(dev(torch, I.encoder_workload(1, layers=1).x))
+    host = []
+    for c in cases:
+        kc = np.zeros((cap, 20, 64), dtype=np.float16)
+        vc = np.zeros((cap, 20, 64), dtype=np.float16)
+        kc[:nk], vc[:nk] = c.k, c.v
+        host.append((kc, vc))
+    mask = torch.from_numpy(_lib.pack_mask_rows(cases[0].mask).view(np.int32)).cuda()
+    x0 = I.decoder_block_input(2, n_q)
+    ca = [(dev(torch, k), dev(torch, v)) for k, v in host]
+    ya = torch.empty((n_q, 1280), dtype=torch.float16, device="cuda")
+    cur = dev(torch, x0)
+    for l in range(n_layers):
+        dv.layer(cur, l, slots, ca[l][0], ca[l][1], nk, mask, ya)
+        cur = ya
+    cb = [(dev(torch, k), dev(torch, v)) for k, v in host]
+    yb = torch.full((n_q, 1280), float("nan"), dtype=torch.float16, device="cuda")
+    dv.stack(dev(torch, x0), slots, cb, nk, mask, yb)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yb), "Q8 stack output differs from layer-by-layer"
+    for l in range(n_layers):
+        assert torch.equal(ca[l][0], cb[l][0]) and torch.equal(ca[l][1], cb[l][1]), f"layer {l} caches differ"
+    assert not dv.stack_workspace[:_lib.DECODER_STACK_ZERO_BYTES].any().item()

@@ -39,7 +39,7 @@ EXPORTS = ("edda_qkv_pack", "edda_encoder_attn", "edda_flash_attn", "edda_encode
            "edda_decoder_verify_layer", "edda_decoder_verify_workspace_bytes", "edda_cross_kv",
            "edda_verify_attn_ex", "edda_verify_workspace_bytes_ex",
            "edda_quantize_q8_0", "edda_linear_q8", "edda_decoder_verify_layer_q8",
-           "edda_decoder_verify_stack", "edda_decoder_verify_stack_workspace_bytes",
+           "edda_decoder_verify_stack", "edda_decoder_verify_stack_q8", "edda_decoder_verify_stack_workspace_bytes",
            "edda_last_error", "edda_version")
 
 D_FF = 5120
@@ -75,6 +75,12 @@ class DecoderLayerWeightsQ8(ctypes.Structure):
 class DecoderStackLayer(ctypes.Structure):
     """edda_decoder_stack_layer: a layer's weights, its caches and its cross K/V (device)."""
     _fields_ = [("weights", DecoderLayerWeights), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("cross_k", ctypes.c_void_p), ("cross_v", ctypes.c_void_p)]
+
+
+class DecoderStackLayerQ8(ctypes.Structure):
+    """edda_decoder_stack_layer_q8: as DecoderStackLayer with Q8_0 projection weights."""
+    _fields_ = [("weights", DecoderLayerWeightsQ8), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
                 ("cross_k", ctypes.c_void_p), ("cross_v", ctypes.c_void_p)]
 
 
@@ -121,6 +127,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                                  ctypes.POINTER(DecoderLayerWeightsQ8), vp, vp, sz, vp]
     lib.edda_decoder_verify_stack.argtypes = [vp, i32, ctypes.POINTER(i32), i32, i32, vp, i32,
                                               ctypes.POINTER(DecoderStackLayer), i32, vp, vp, sz, vp]
+    lib.edda_decoder_verify_stack_q8.argtypes = [vp, i32, ctypes.POINTER(i32), i32, i32, vp, i32,
+                                                 ctypes.POINTER(DecoderStackLayerQ8), i32, vp, vp, sz, vp]
     lib.edda_decoder_verify_stack_workspace_bytes.argtypes = [i32, i32, i32]
     lib.edda_decoder_verify_stack_workspace_bytes.restype = sz
     lib.edda_quantize_q8_0.argtypes = [vp, i32, i32, vp, vp, vp]
@@ -137,7 +145,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                  "edda_linear",
                  "edda_layer_norm", "edda_encoder_layer", "edda_encoder_stem", "edda_decoder_verify_layer",
                  "edda_cross_kv", "edda_verify_attn_ex", "edda_quantize_q8_0", "edda_linear_q8",
-                 "edda_decoder_verify_layer_q8", "edda_decoder_verify_stack"):
+                 "edda_decoder_verify_layer_q8", "edda_decoder_verify_stack", "edda_decoder_verify_stack_q8"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -414,8 +422,9 @@ def decoder_verify_stack_workspace_bytes(n_q: int, n_kv: int, n_frames: int) -> 
 
 def edda_decoder_verify_stack(x, slots, cache_slots, n_kv, mask_rows, n_frames, layers, y, workspace, stream=None):
     """Consecutive decoder layers over the block rows x [n_q, 1280] into y; layers: a ctypes
-    array of DecoderStackLayer (weights, caches [cache_slots, 20, 64] updated in place, cross
-    K/V [n_frames, 20, 64]); slots host ints; mask_rows as for edda_verify_attn (or None)."""
+    array of DecoderStackLayer (fp16 weights) or DecoderStackLayerQ8 (Q8_0 projections), with
+    caches [cache_slots, 20, 64] updated in place and cross K/V [n_frames, 20, 64]; slots host
+    ints; mask_rows as for edda_verify_attn (or None)."""
     lib = load()
     torch = _require(x, "x")
     n_q = x.shape[0]
@@ -425,9 +434,9 @@ def edda_decoder_verify_stack(x, slots, cache_slots, n_kv, mask_rows, n_frames, 
         _require(mask_rows, "mask_rows", (n_q, (n_kv + 31) // 32))
     arr = (ctypes.c_int32 * n_q)(*[int(v) for v in slots])
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib.edda_decoder_verify_stack(_ptr(x), n_q, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), cache_slots,
-                                         n_kv, _ptr(mask_rows), n_frames, layers, len(layers), _ptr(y),
-                                         _ptr(workspace), ws_bytes, _stream(stream)))
+    fn = lib.edda_decoder_verify_stack_q8 if layers._type_ is DecoderStackLayerQ8 else lib.edda_decoder_verify_stack
+    _check(fn(_ptr(x), n_q, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), cache_slots, n_kv, _ptr(mask_rows),
+              n_frames, layers, len(layers), _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def edda_cross_kv(enc, w_k, w_v, b_v, cross_k, cross_v, stream=None):

@@ -641,11 +641,28 @@ size_t edda_decoder_verify_stack_workspace_bytes(int32_t n_q, int32_t n_kv, int3
   return stack_ws(n_q, n_frames).total;
 }
 
-edda_status edda_decoder_verify_stack(const void* x, int32_t n_q, const int32_t* slots, int32_t cache_slots,
-                                      int32_t n_kv, const uint32_t* mask_rows, int32_t n_frames,
-                                      const edda_decoder_stack_layer* layers, int32_t n_layers, void* y,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "edda_decoder_verify_stack";
+}  // extern "C"
+
+namespace {
+// The layer's matrices in the form the single-launch kernel takes.
+DecoderMats stack_mats(const edda_decoder_layer_weights& wt) {
+  return DecoderMats{wt.ln1_gamma, wt.ln1_beta, {wt.w_qkv, nullptr}, wt.b_qkv, {wt.w_o, nullptr}, wt.b_o,
+                     wt.ln2_gamma, wt.ln2_beta, {wt.w_q_cross, nullptr}, wt.b_q_cross, {wt.w_o_cross, nullptr},
+                     wt.b_o_cross, wt.ln3_gamma, wt.ln3_beta, {wt.w_fc1, nullptr}, wt.b_fc1,
+                     {wt.w_fc2, nullptr}, wt.b_fc2};
+}
+DecoderMats stack_mats(const edda_decoder_layer_weights_q8& wt) {
+  auto M = [](const edda_q8_matrix& q) { return Mat{q.codes, q.scales}; };
+  return DecoderMats{wt.ln1_gamma, wt.ln1_beta, M(wt.w_qkv), wt.b_qkv, M(wt.w_o), wt.b_o,
+                     wt.ln2_gamma, wt.ln2_beta, M(wt.w_q_cross), wt.b_q_cross, M(wt.w_o_cross),
+                     wt.b_o_cross, wt.ln3_gamma, wt.ln3_beta, M(wt.w_fc1), wt.b_fc1, M(wt.w_fc2), wt.b_fc2};
+}
+
+template <typename Layer>
+edda_status decoder_stack(const char* fn, const void* x, int32_t n_q, const int32_t* slots, int32_t cache_slots,
+                          int32_t n_kv, const uint32_t* mask_rows, int32_t n_frames, const Layer* layers,
+                          int32_t n_layers, void* y, void* workspace, size_t workspace_bytes, void* stream,
+                          bool q8) {
   if (!x || !slots || !layers || !y)
     return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: x, slots, layers and y must be non-null", fn);
   if (n_layers < 1) return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: n_layers = %d must be >= 1", fn, n_layers);
@@ -671,19 +688,24 @@ edda_status edda_decoder_verify_stack(const void* x, int32_t n_q, const int32_t*
     return fail(EDDA_ERR_MISALIGNED, "%s: x and y must be 16-byte, the workspace 256-byte aligned", fn);
   if (mask_rows && !aligned(mask_rows, 4)) return fail(EDDA_ERR_MISALIGNED, "%s: mask_rows must be 4-byte aligned", fn);
   for (int32_t l = 0; l < n_layers; ++l) {
-    const edda_decoder_stack_layer& L = layers[l];
-    const edda_decoder_layer_weights& w = L.weights;
-    const void* required[] = {w.ln1_gamma, w.ln1_beta, w.w_qkv,     w.w_o,       w.ln2_gamma, w.ln2_beta,
-                              w.w_q_cross, w.w_o_cross, w.ln3_gamma, w.ln3_beta, w.w_fc1,     w.w_fc2,
+    const Layer& L = layers[l];
+    const DecoderMats m = stack_mats(L.weights);
+    const void* required[] = {m.ln1_gamma, m.ln1_beta, m.qkv.w,     m.o.w,       m.ln2_gamma, m.ln2_beta,
+                              m.q_cross.w, m.o_cross.w, m.ln3_gamma, m.ln3_beta, m.fc1.w,     m.fc2.w,
                               L.k_cache,   L.v_cache,   L.cross_k,   L.cross_v};
     for (const void* q : required)
       if (!q)
         return fail(EDDA_ERR_INVALID_ARGUMENT,
                     "%s: layer %d: every LayerNorm, weight-matrix, cache and cross K/V pointer is required", fn, l);
-    const void* all[] = {w.ln1_gamma, w.ln1_beta, w.w_qkv,     w.b_qkv,     w.w_o,       w.b_o,       w.ln2_gamma,
-                         w.ln2_beta,  w.w_q_cross, w.b_q_cross, w.w_o_cross, w.b_o_cross, w.ln3_gamma, w.ln3_beta,
-                         w.w_fc1,     w.b_fc1,     w.w_fc2,     w.b_fc2,     L.k_cache,   L.v_cache,   L.cross_k,
-                         L.cross_v};
+    const Mat* mats[] = {&m.qkv, &m.o, &m.q_cross, &m.o_cross, &m.fc1, &m.fc2};
+    for (const Mat* mt : mats)
+      if (q8 && !mt->scales)
+        return fail(EDDA_ERR_INVALID_ARGUMENT, "%s: layer %d: every Q8_0 matrix needs its scales", fn, l);
+    const void* all[] = {m.ln1_gamma, m.ln1_beta, m.qkv.w,     m.b_qkv,     m.o.w,       m.b_o,       m.ln2_gamma,
+                         m.ln2_beta,  m.q_cross.w, m.b_q_cross, m.o_cross.w, m.b_o_cross, m.ln3_gamma, m.ln3_beta,
+                         m.fc1.w,     m.b_fc1,     m.fc2.w,     m.b_fc2,     L.k_cache,   L.v_cache,   L.cross_k,
+                         L.cross_v,   m.qkv.scales, m.o.scales, m.q_cross.scales, m.o_cross.scales, m.fc1.scales,
+                         m.fc2.scales};
     for (const void* q : all)
       if (q && !aligned(q, 16)) return fail(EDDA_ERR_MISALIGNED, "%s: layer %d: pointers must be 16-byte aligned", fn, l);
   }
@@ -704,13 +726,8 @@ edda_status edda_decoder_verify_stack(const void* x, int32_t n_q, const int32_t*
     p.y = l0 + n == n_layers ? y : ws + W.carry;
     p.n_q = n_q, p.slots = sl, p.n_kv = n_kv, p.mask = mask_rows, p.n_frames = n_frames, p.n_layers = n;
     for (int i = 0; i < n; ++i) {
-      const edda_decoder_stack_layer& L = layers[l0 + i];
-      const edda_decoder_layer_weights& wt = L.weights;
-      const DecoderMats m{wt.ln1_gamma, wt.ln1_beta, {wt.w_qkv, nullptr}, wt.b_qkv, {wt.w_o, nullptr}, wt.b_o,
-                          wt.ln2_gamma, wt.ln2_beta, {wt.w_q_cross, nullptr}, wt.b_q_cross, {wt.w_o_cross, nullptr},
-                          wt.b_o_cross, wt.ln3_gamma, wt.ln3_beta, {wt.w_fc1, nullptr}, wt.b_fc1,
-                          {wt.w_fc2, nullptr}, wt.b_fc2};
-      fused_layer_ptrs(m, false, L.k_cache, L.v_cache, L.cross_k, L.cross_v, &p.layer[i]);
+      const Layer& L = layers[l0 + i];
+      fused_layer_ptrs(stack_mats(L.weights), q8, L.k_cache, L.v_cache, L.cross_k, L.cross_v, &p.layer[i]);
     }
     p.lws = ws + W.blocks, p.lws_stride = W.block;
     p.off_qkv = (uint32_t)W.qkv, p.off_o = (uint32_t)W.o, p.off_x1 = (uint32_t)W.x1, p.off_qc = (uint32_t)W.qc;
@@ -725,6 +742,26 @@ edda_status edda_decoder_verify_stack(const void* x, int32_t n_q, const int32_t*
     }
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+edda_status edda_decoder_verify_stack(const void* x, int32_t n_q, const int32_t* slots, int32_t cache_slots,
+                                      int32_t n_kv, const uint32_t* mask_rows, int32_t n_frames,
+                                      const edda_decoder_stack_layer* layers, int32_t n_layers, void* y,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return decoder_stack("edda_decoder_verify_stack", x, n_q, slots, cache_slots, n_kv, mask_rows, n_frames, layers,
+                       n_layers, y, workspace, workspace_bytes, stream, false);
+}
+
+edda_status edda_decoder_verify_stack_q8(const void* x, int32_t n_q, const int32_t* slots, int32_t cache_slots,
+                                         int32_t n_kv, const uint32_t* mask_rows, int32_t n_frames,
+                                         const edda_decoder_stack_layer_q8* layers, int32_t n_layers, void* y,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  return decoder_stack("edda_decoder_verify_stack_q8", x, n_q, slots, cache_slots, n_kv, mask_rows, n_frames, layers,
+                       n_layers, y, workspace, workspace_bytes, stream, true);
 }
 
 edda_status edda_quantize_q8_0(const void* w, int32_t rows, int32_t cols, void* codes, void* scales, void* stream) {

@@ -203,17 +203,15 @@ class DecoderVerifier:
                                        self.cross_v[layer], self.structs[layer], y, self.workspace, stream)
 
     def stack(self, x, slots, caches, n_kv, mask_rows, y, stream=None):
-        """Every layer in order over the block x (edda_decoder_verify_stack, fp16 weights):
-        caches[l] = (k_cache, v_cache) of layer l; y receives the last layer's output."""
-        if self.q8:
-            raise ValueError("the stack entry point takes fp16 weights")
+        """Every layer in order over the block x (edda_decoder_verify_stack, or _q8 for Q8_0
+        weights): caches[l] = (k_cache, v_cache) of layer l; y receives the last layer's output."""
         cache_slots = caches[0][0].shape[0]
         if self._stack is None or self._stack[0] != [(k.data_ptr(), v.data_ptr()) for k, v in caches]:
-            arr = (_lib.DecoderStackLayer * len(self.structs))()
+            kind = _lib.DecoderStackLayerQ8 if self.q8 else _lib.DecoderStackLayer
+            arr = (kind * len(self.structs))()
             for l, w in enumerate(self.structs):
                 k, v = caches[l]
-                arr[l] = _lib.DecoderStackLayer(w, k.data_ptr(), v.data_ptr(), self.cross_k[l].data_ptr(),
-                                                self.cross_v[l].data_ptr())
+                arr[l] = kind(w, k.data_ptr(), v.data_ptr(), self.cross_k[l].data_ptr(), self.cross_v[l].data_ptr())
             self._stack = ([(k.data_ptr(), v.data_ptr()) for k, v in caches], arr)
         if self.stack_workspace is None:
             nb = _lib.decoder_verify_stack_workspace_bytes(_lib.MAX_VERIFY_QUERIES, _lib.DECODER_STACK_MAX_KV,
