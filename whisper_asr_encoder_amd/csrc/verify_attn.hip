@@ -23,7 +23,10 @@ using namespace vcore;
 
 constexpr int kVWaves = 4;
 constexpr int kVThreads = kVWaves * kWave;
-constexpr int kSplitKeys = kVWaves * kWaveKeys;
+constexpr int kChunk4 = kVWaves * kWaveKeys;  // keys of 4 waves x one 32-key chunk
+// Caches longer than kOneWorkgroupKeys: splits of kSplitWaves waves x kSplitCpw chunks.
+constexpr int kSplitWaves = 4, kSplitCpw = 1;
+constexpr int kSplitKeys = kSplitWaves * kSplitCpw * kWaveKeys;
 // Per-head arrival counters at the workspace start, one per 256-byte line.
 constexpr int kMaxHeads = 64;
 constexpr size_t kCounterBytes = (size_t)kMaxHeads * kCounterStride * sizeof(uint32_t);
@@ -38,7 +41,7 @@ __global__ __launch_bounds__(NW * kWave) void verify_kernel(Args a) {
   verify_unit<kMode, CPW, NW>(a, blockIdx.x, blockIdx.y, gridDim.x, sm, PlainIo{}, (int)threadIdx.x);
 }
 
-constexpr int kOneWorkgroupKeys = 4 * kSplitKeys;  // up to 512 keys: one workgroup per head
+constexpr int kOneWorkgroupKeys = 4 * kChunk4;  // up to 512 keys: one workgroup per head
 
 __global__ void zero_words_kernel(uint32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -86,12 +89,16 @@ hipError_t launch_verify(const void* q, int q_stride, int n_q, const void* k, co
   // keys 4 waves of 3 chunks beat 8 of 2 by 7 %, at 448 keys 8 of 2 beat 4 of 4 by 12 %).
   auto by_chunks = [&](auto mode_c) {
     constexpr int M = decltype(mode_c)::value;
-    if (n_splits == 1 && n_kv > 3 * kSplitKeys) {
+    if (n_splits > 1) {
+      threads = kSplitWaves * kWave;
+      return go(verify_kernel<M, kSplitCpw, kSplitWaves>);
+    }
+    if (n_kv > 3 * kChunk4) {
       threads = 8 * kWave;
       return go(verify_kernel<M, 2, 8>);
     }
-    if (n_splits == 1 && n_kv > 2 * kSplitKeys) return go(verify_kernel<M, 3, kVWaves>);
-    if (n_splits == 1 && n_kv > kSplitKeys) return go(verify_kernel<M, 2, kVWaves>);
+    if (n_kv > 2 * kChunk4) return go(verify_kernel<M, 3, kVWaves>);
+    if (n_kv > kChunk4) return go(verify_kernel<M, 2, kVWaves>);
     return go(verify_kernel<M, 1, kVWaves>);
   };
   if (mask_mode == kMaskRows) return by_chunks(std::integral_constant<int, kMaskRows>());

@@ -51,12 +51,18 @@ __device__ __forceinline__ f32x2 load_coherent(const float* p) {
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
-// Four floats (16-byte aligned) read with the device-coherent cache policy (sc1) through a
-// buffer load: at a float index from a wave-uniform base.
+// Four floats (16-byte aligned) read / written with the device-coherent cache policy (sc1)
+// through a buffer access: at a float index from a wave-uniform base.  One 16-byte store per
+// lane keeps a wave's 1 KB of partials in whole 64-byte lines (two 8-byte stores would each
+// touch every line with half of its bytes, doubling the write requests).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const float* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
 __device__ __forceinline__ f32x4 load_coherent4(const float* base, uint32_t idx) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, 0x7fffffff, 0x00020000);
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 4 * idx, 0, 16));
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(coherent_rsrc(base), 4 * idx, 0, 16));
+}
+__device__ __forceinline__ void store_coherent4(float* base, uint32_t idx, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), coherent_rsrc(base), 4 * idx, 0, 16);
 }
 
 __device__ __forceinline__ float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
@@ -144,6 +150,7 @@ __device__ __forceinline__ void verify_unit(const Args& a, int split, int head, 
                                             const Io& io, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, G = lane >> 4;
+  static_assert(NW * kWave >= kMaxQ * (kHeadDim / 4), "the merge gives each (query, 4 dims) a thread");
   const int wg_key0 = split * NW * kWaveKeys * CPW;
   auto chunk_key0 = [&](int c) { return wg_key0 + (c * NW + wave) * kWaveKeys; };  // multiple of 32
   const int kKvStride = a.n_heads * kHeadDim;
@@ -363,8 +370,7 @@ __device__ __forceinline__ void verify_unit(const Args& a, int split, int head, 
   const int slot0 = mq * a.n_heads + head, slot_step = n_q * a.n_heads;
   if (row_ok) {
     const int slot = split * slot_step + slot0;
-    store_coherent(a.part_o + (uint32_t)(slot * kHeadDim + d0), acc[0], acc[1]);
-    store_coherent(a.part_o + (uint32_t)(slot * kHeadDim + d0 + 2), acc[2], acc[3]);
+    store_coherent4(a.part_o, (uint32_t)(slot * kHeadDim + d0), (f32x4){acc[0], acc[1], acc[2], acc[3]});
     if (d0 == 0) store_coherent(a.part_ml + (uint32_t)(slot * 2), M, L);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
