@@ -53,6 +53,7 @@ constexpr int kComputeThreads = kComputeWaves * kWave;
 constexpr int kGemmThreads = (kComputeWaves + kProducerWaves) * kWave;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 constexpr int kCus = 256;
+constexpr int kSc1 = 16;  // buffer-instruction cache policy bit: device-coherent (sc1)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -365,13 +366,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_bias_kernel(const f16* __re
     }
   }
   __syncthreads();
+  // Row stores with the device-coherent policy (sc1): the lines are written through to
+  // memory as the tile finishes, while other tiles still compute, instead of staying dirty in
+  // the XCD's L2 until the write-back at the end of the kernel, which nothing overlaps.
+  // Offsets are taken from the tile's origin (wave-uniform), so they stay small.
   constexpr int kChunksPerRow = BN / 8;
   constexpr int kChunks = BM * kChunksPerRow;
+  const __amdgpu_buffer_rsrc_t c_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(C + (size_t)m0 * N + n0, (short)0, 0x7fffffff, 0x00020000);
 #pragma unroll 4
   for (int c = tid; c < kChunks; c += kComputeThreads) {
     const int ml = c / kChunksPerRow, cc = c % kChunksPerRow;
-    const int m = m0 + ml;
-    if (m < M) store16(C + (size_t)m * N + n0 + cc * 8, load16(cs + ml * kCld + cc * 8));
+    if (m0 + ml < M)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, load16(cs + ml * kCld + cc * 8)), c_rsrc,
+                                             2 * (ml * N + cc * 8), 0, kSc1);
   }
 }
 
