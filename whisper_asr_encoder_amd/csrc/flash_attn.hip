@@ -61,6 +61,8 @@ constexpr int kStageB = kQuarters * 2 * kTileB;  // K and V tiles of every quart
 constexpr int kXcds = 8;
 constexpr int kMaxBatchPerLaunch = 256;
 constexpr float kRedoSum = 16384.0f;    // per-tile sum of P that triggers a re-reference
+constexpr int kOutLd = kHeadDim + 8;    // LDS row stride (halves) of the finished output block
+constexpr int kSc1 = 16;                // buffer-instruction cache policy bit: device-coherent (sc1)
 constexpr float kQScale = 0.18033688011112042f;  // log2(e) / sqrt(64)
 
 struct ValidLens {
@@ -516,10 +518,14 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
   }
   xml[(qg * 4 + quarter) * kWave + lane] = (f32x4){mref[0], l_run[0], mref[1], l_run[1]};
   __syncthreads();
-  if (!wave_rows) return;
+  // The finished fp16 block goes to LDS first (rows of kOutLd halves after the merge
+  // buffers), so that the workgroup writes whole 128-byte rows below.
+  f16* const ost = reinterpret_cast<f16*>(xml + kQGroups * 4 * kWave);
+  static_assert((kQGroups * 4 * 3 * 4 + kQGroups * 4) * kWave * 16 + kBMq * kOutLd * 2 <= kStages * kStageB,
+                "merge buffers and the output block must fit in the ring");
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) {
-    if (blk != quarter) continue;
+    if (blk != quarter || !wave_rows) continue;
     const int qb = blk >> 1, db = blk & 1;
     f32x4 ml[4];
     float M = mref[qb];
@@ -551,17 +557,27 @@ __global__ __launch_bounds__(kThreads) void flash_attn_kernel(
         }
       }
     }
-    const int q = wq0 + 32 * qb + l32;
-    if (q < seg_end) {
-      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-      f16* orow = O + (win_row0 + q) * kDModel + head * kHeadDim;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    f16* orow = ost + (qg * kQW + 32 * qb + l32) * kOutLd;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f16x2 lo = pack_rne(o[4 * i + 0] * inv, o[4 * i + 1] * inv);
-        const f16x2 hi = pack_rne(o[4 * i + 2] * inv, o[4 * i + 3] * inv);
-        *reinterpret_cast<f16x4*>(orow + 32 * db + 8 * i + 4 * g) = (f16x4){lo[0], lo[1], hi[0], hi[1]};
-      }
+    for (int i = 0; i < 4; ++i) {
+      const f16x2 lo = pack_rne(o[4 * i + 0] * inv, o[4 * i + 1] * inv);
+      const f16x2 hi = pack_rne(o[4 * i + 2] * inv, o[4 * i + 3] * inv);
+      *reinterpret_cast<f16x4*>(orow + 32 * db + 8 * i + 4 * g) = (f16x4){lo[0], lo[1], hi[0], hi[1]};
     }
+  }
+  __syncthreads();
+  // Rows q_begin .. of this head's 64 columns: 8 lanes per 128-byte row, written through to
+  // memory (sc1) as the GEMM's output rows are.  Offsets from the block's origin.
+  const __amdgpu_buffer_rsrc_t o_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      O + (win_row0 + q_begin) * kDModel + head * kHeadDim, (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+  for (int c = tid; c < kBMq * 8; c += kThreads) {
+    const int r = c >> 3, cc = c & 7;
+    if (q_begin + r < seg_end)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4, *reinterpret_cast<const f16x8*>(ost + r * kOutLd + 8 * cc)), o_rsrc,
+          2 * (r * kDModel + 8 * cc), 0, kSc1);
   }
 }
 
