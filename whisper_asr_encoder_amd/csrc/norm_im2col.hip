@@ -28,9 +28,13 @@ __global__ __launch_bounds__(kLnRowsPerBlock * kWave) void layer_norm_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int row = blockIdx.x * kLnRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
-  f16* yr = y + (size_t)row * kFeatures;
-  layer_norm_row<kGroups>(x + (size_t)row * kFeatures, gamma, beta, lane,
-                          [&](int f, f16x4 v) { *reinterpret_cast<f16x4*>(yr + f) = v; });
+  // Output rows written through to memory (sc1), as the GEMM's: no dirty lines left for the
+  // end-of-kernel L2 write-back.  The row's base is wave-uniform.
+  const __amdgpu_buffer_rsrc_t yr =
+      __builtin_amdgcn_make_buffer_rsrc(y + (size_t)row * kFeatures, (short)0, 0x7fffffff, 0x00020000);
+  layer_norm_row<kGroups>(x + (size_t)row * kFeatures, gamma, beta, lane, [&](int f, f16x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), yr, 2 * f, 0, 16);
+  });
 }
 
 template <int kGroups>
