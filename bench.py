@@ -53,20 +53,38 @@ def source_digest(names):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key, digest):
-    """HBM bytes per launch from committed rocprofv3 PMC summaries, or None when the
-    kernel source changed since the counters were taken."""
+def profile_entry(kernel_key, digest):
+    """The committed rocprofv3 summary of a kernel (profiles/traffic.json: HBM bytes per launch
+    from the PMC runs, the kernel trace's mean duration), or None when the kernel source
+    changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        data = json.load(open(path))
-        ent = data.get(kernel_key)
+        ent = json.load(open(path)).get(kernel_key)
         if ent and ent.get("source_digest") == digest:
-            return ent.get("bytes_per_launch")
+            return ent
     except (OSError, ValueError):
         return None
     return None
+
+
+def measured_traffic(kernel_key, digest):
+    """HBM bytes per launch from the committed counters, or None (see profile_entry)."""
+    ent = profile_entry(kernel_key, digest)
+    return ent.get("bytes_per_launch") if ent else None
+
+
+def profile_roofline(kernel_key, digest, work, peak, unit_scale):
+    """The roofline fraction from the committed profile's timing source (rocprofv3 kernel-trace
+    mean duration, another run and possibly another box), beside the live HIP-event figure."""
+    ent = profile_entry(kernel_key, digest)
+    if not ent or not ent.get("trace_mean_us"):
+        return None
+    achieved = work / (ent["trace_mean_us"] * 1e-6) / unit_scale
+    return {"source": f"profiles/ rocprofv3 kernel-trace mean duration of {kernel_key}",
+            "us_per_launch": ent["trace_mean_us"], "achieved": round(achieved, 2),
+            "frac": round(achieved / peak, 4)}
 
 
 class Timer:
@@ -185,7 +203,9 @@ def encoder_bench(args, torch, cfg):
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
                 "flops_per_launch": dom_flops, "ms_per_launch": round(kernels[dom]["ms"], 5),
-                "traffic": measured_traffic(dom, source_digest(dom_src))}
+                "timing": "HIP events around back-to-back launches of the kernel, this run",
+                "traffic": measured_traffic(dom, source_digest(dom_src)),
+                "profile": profile_roofline(dom, source_digest(dom_src), dom_flops, PEAK_FP16_TFLOPS, 1e12)}
 
     names = {0: "one 4 s chunk (200 frames), 1 attention sublayer",
              1: "one 30 s Whisper-large-v3 window (1500 frames), 32 attention sublayers",
@@ -335,7 +355,9 @@ def full_encoder_bench(args, torch):
     achieved = flops[dom] / (t[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "flops_per_launch": flops[dom],
-                "ms_per_launch": round(t[dom], 5), "traffic": measured_traffic(dom, source_digest(src))}
+                "ms_per_launch": round(t[dom], 5), "timing": "HIP events around back-to-back launches, this run",
+                "traffic": measured_traffic(dom, source_digest(src)),
+                "profile": profile_roofline(dom, source_digest(src), flops[dom], PEAK_FP16_TFLOPS, 1e12)}
     result = {
         "metric": "whole-encoder ms per 30 s window (stem + 32 layers + final LayerNorm) on 1 MI355X",
         "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -586,9 +608,18 @@ def verify_bench(args, torch):
         tot["flops"] += f
         del g, gb, sets, beams
     gbs = tot["bytes"] / (tot["us"] * 1e-6) / 1e9
-    dig = source_digest(["verify_attn.hip"])
+    dig = source_digest(["verify_attn.hip", "verify_core.hpp"])
     t_causal, t_cross = measured_traffic("verify_causal", dig), measured_traffic("verify_cross", dig)
     traffic = round((t_causal + t_cross) / 2) if t_causal and t_cross else None
+    p_causal, p_cross = profile_entry("verify_causal", dig), profile_entry("verify_cross", dig)
+    bytes_per_launch = round(tot["bytes"] / (trials * 2 * layers))
+    profile = None
+    if p_causal and p_cross and p_causal.get("trace_mean_us") and p_cross.get("trace_mean_us"):
+        # As many causal as cross launches per pass: the mean of the two traced means.
+        us = (p_causal["trace_mean_us"] + p_cross["trace_mean_us"]) / 2
+        ach = bytes_per_launch / (us * 1e-6) / 1e9
+        profile = {"source": "profiles/ rocprofv3 kernel-trace mean durations of verify_causal and verify_cross",
+                   "us_per_launch": round(us, 3), "achieved": round(ach, 2), "frac": round(ach / PEAK_HBM_GBS, 4)}
     res = {
         "metric": "verification attention (8 drawn cache lengths x 32 layers x causal self + cross attention) "
                   "on 1 MI355X, HBM GB/s of algorithmic bytes",
@@ -610,7 +641,8 @@ def verify_bench(args, torch):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "bytes_per_launch": round(tot["bytes"] / (trials * 2 * layers)), "traffic": traffic},
+                     "bytes_per_launch": bytes_per_launch, "timing": "HIP events around each trial's graph replay, this run",
+                     "traffic": traffic, "profile": profile},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_verify(cross_cases, args.cpu_seconds)

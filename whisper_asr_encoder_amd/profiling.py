@@ -13,16 +13,17 @@ passes (FETCH_SIZE, then WRITE_SIZE) write, and produces
   trace's mean duration, and rocprof's own MfmaUtil formula; the share of L2 read / write
   requests that go to DRAM (TCC_EA0_RDREQ_DRAM / TCC_EA0_RDREQ and the write pair) and the
   DRAM bytes they imply,
-* beside the trace's mean, the per-launch time bench.py measured with HIP events in the
-  same traced run (--bench-json).
+* beside the trace's mean, the per-launch time bench.py measured with HIP events on the same
+  box (--bench-json: the JSON line of an untraced run, since under the tracer the eager
+  launches become host-bound).
 
     python -m whisper_asr_encoder_amd.profiling TRACE_DIR FETCH_DIR WRITE_DIR OUT_DIR \
         --workload window|verify --command "<the rocprofv3 command lines>"
 
 writes OUT_DIR/<kernel>_<workload>.md for each kernel of the workload and updates
 OUT_DIR/traffic.json, keyed by the names bench.py reports (qkv_gemm, flash_attn, out_gemm;
-verify_causal, verify_cross), each with the digest of the kernel sources the counters were
-taken on.
+verify_causal, verify_cross), each with the trace's mean duration and the digest of the kernel
+sources the counters were taken on.
 """
 from __future__ import annotations
 
@@ -225,7 +226,7 @@ def summarize(trace_dir, fetch_dir, write_dir, out_dir, command, workload="windo
         wb = statistics.median(wv) * 1024.0 * w_scale
         digest = source_digest(srcs)
         traffic[key] = {"bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
-                        "source_digest": digest}
+                        "trace_mean_us": round(s["avg_ns"] / 1e3, 3), "source_digest": digest}
         names = [k for k in stats if _has(k, frag)]
         with open(os.path.join(out_dir, f"{key}_{workload}.md"), "w") as f:
             f.write(f"# {key}: {title}\n\n")
@@ -253,7 +254,7 @@ def summarize(trace_dir, fetch_dir, write_dir, out_dir, command, workload="windo
                 f.write(f"| {label} | {value} |\n")
             k = (bench or {}).get("kernels", {}).get(key) or {}
             if k.get("ms"):
-                f.write(f"| the same run's bench.py, HIP events around back-to-back launches | "
+                f.write(f"| bench.py on the same box (--bench-json), HIP events around back-to-back launches | "
                         f"{k['ms'] * 1e3:.2f} us per launch ({100 * (s['avg_ns'] / 1e3 / (k['ms'] * 1e3) - 1):+.1f} % "
                         f"trace vs events) |\n")
     with open(tpath, "w") as f:
@@ -293,7 +294,8 @@ def main():
     ap.add_argument("--workload", default="window", choices=sorted(WORKLOADS))
     ap.add_argument("--extra-pmc", action="append", default=[],
                     help="directory of a further rocprofv3 --pmc run (repeatable)")
-    ap.add_argument("--bench-json", default=None, help="stdout of the traced bench.py run (its JSON line)")
+    ap.add_argument("--bench-json", default=None,
+                    help="stdout of an untraced bench.py run of the same workload on the same box (its JSON line)")
     a = ap.parse_args()
     fetch = None if a.fetch_dir == "-" else a.fetch_dir
     write = None if a.write_dir == "-" else a.write_dir
