@@ -219,6 +219,44 @@ def test_encoder_layer_in_place_matches(torch):
     assert torch.equal(xi, y)
 
 
+def test_encoder_layers_graph_replay(torch):
+    """Two encoder layers (LayerNorms, QKV / output / MLP GEMMs, flash attention, all with
+    write-through row stores) captured in a HIP graph: every replay equals the eager result bit
+    for bit, with eager work between replays."""
+    say("encoder layers graph replay: 2 layers, one 30 s window")
+    layers = [I.full_layer_weights(1, l) for l in range(2)]
+    enc = make_encoder(torch, layers, 1, 1500, 0, None)
+    x = dev(torch, I.encoder_workload(1, layers=1).x)
+    h = torch.empty_like(x)
+    y = torch.empty_like(x)
+
+    def step():
+        enc.layer(x, 0, h)
+        enc.layer(h, 1, y)
+
+    step()
+    torch.cuda.synchronize()
+    eager = y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        h.fill_(float("nan"))
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), f"replay {rep} differs from eager"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), f"eager step after replay {rep} differs"
+
+
 def test_full_encoder_small(torch):
     """Stem -> 2 layers -> final LayerNorm; each stage is compared with the oracle applied to
     the GPU's own input to that stage, and the whole chain end to end."""
